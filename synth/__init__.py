@@ -1,0 +1,282 @@
+"""Seeded synthetic inputs for the paged KV-cache write + PagedAttention decode path.
+
+This module is shared by the oracle side and the HIP side and holds none of the
+method's arithmetic: it draws context lengths, block placements (the order of
+the free list), and the query / key / value values, and it describes, as a
+script of block-manager operations, how each workload's cache is built.  Each
+side executes that script with its own block manager, its own cache write and
+its own attention.
+
+Randomness: ``numpy.random.default_rng(SeedSequence([cfg, stream, sub]))`` with
+one stream per kind of draw (0 context lengths, 1 placement, 2 q, 3 history K,
+4 history V, 5 step-token K/V, 6 tails, 7 fork offsets) and ``sub`` naming the
+sequence (or prompt group, or block size for placements), so that a sequence's
+values do not depend on how many other sequences are drawn.  Values are drawn as
+float32 N(0, 1) and rounded to the storage type with round-to-nearest-even.
+
+The workloads follow the shapes that the pages use: the LLaMA-13B layer
+(40 heads x head_dim 128 = d_model 5120, brentwoodlivery "5.3.18 LLM serving"
+worked example; polomodov.tech "vLLM and PagedAttention" slide 5), a batch of 30
+requests (slide 17), the 4096-token worked-example length, parallel sampling
+with a shared prompt (comfyai.app "6.4 PagedAttention" 6.4.3; slide 13), and
+block sizes around the 16-32 sweet spot (slide 19).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+try:  # optional: fast IEEE casts on the CPU
+    import torch as _torch
+except Exception:  # pragma: no cover
+    _torch = None
+
+__all__ = [
+    "DTYPES", "Workload", "make_workload", "to_storage", "CONFIG_NAMES",
+    "SWEEP_BLOCK_SIZES",
+]
+
+# storage dtype name -> (numpy storage dtype, bytes per element)
+DTYPES = {"f32": (np.float32, 4), "f16": (np.float16, 2), "bf16": (np.uint16, 2)}
+
+CONFIG_NAMES = {
+    1: "tiny-fp32",
+    2: "llama13b-layer-batch30",
+    3: "long-context-8x4096",
+    4: "shared-prefix-8x8",
+    5: "high-batch-bs-sweep",
+}
+SWEEP_BLOCK_SIZES = (8, 16, 32, 64, 128)
+
+_STREAM_CTX, _STREAM_PLACE, _STREAM_Q, _STREAM_K, _STREAM_V = 0, 1, 2, 3, 4
+_STREAM_STEP, _STREAM_TAIL, _STREAM_FORK = 5, 6, 7
+
+
+def _rng(cfg: int, stream: int, sub: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([cfg, stream, sub]))
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 draws to the storage type (round to nearest, ties to even).
+
+    bf16 is returned as its raw uint16 bit pattern.  torch's CPU casts are used
+    when available (they are IEEE round-to-nearest-even, like NumPy's, and
+    much faster); the NumPy path gives the same bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if _torch is not None and x.size > 4096:
+        t = _torch.from_numpy(x)
+        if dtype == "f16":
+            return t.to(_torch.float16).numpy()
+        if dtype == "bf16":
+            return t.to(_torch.bfloat16).view(_torch.int16).numpy().view(np.uint16)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        bits = x.view(np.uint32).astype(np.uint64)
+        nan = np.isnan(x)
+        rounded = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint16)
+        rounded[nan] = 0x7FC0
+        return rounded
+    raise ValueError(dtype)
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    return to_storage(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
+def _draw_many(cfg: int, stream: int, jobs, dtype: str):
+    """Draw one array per (sub, shape) job, each from its own seed stream
+    (cfg, stream, sub); threads only change the speed, never the values."""
+    def one(job):
+        sub, shape = job
+        return _normal(_rng(cfg, stream, sub), shape, dtype)
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        return list(ex.map(one, jobs))
+
+
+@dataclass
+class Workload:
+    """One seeded workload: shapes, pool, free-list order, values and the op script.
+
+    ``ops`` is executed in order by each side:
+      ("add", seq, n)         new sequence whose first n tokens are written (prefill)
+      ("fork", parent, child) child shares all of parent's blocks
+      ("extend", seq, n)      append n tokens to seq, one at a time
+      ("step", [seqs])        append one token to each listed seq, then decode them
+    The values of token t of sequence s are ``kv(s, t, t+1)``; the step token of
+    each sequence is its last logical token.
+    """
+    cfg: int
+    name: str
+    H: int
+    D: int
+    dtype: str
+    bs: int
+    NB: int
+    scale: float
+    free_order: np.ndarray          # int32, the free list (front is popped first)
+    poison_block: int               # a block id never handed out; tests fill it with NaN
+    ctx: np.ndarray                 # int64 [S] context length after the step (incl. step token)
+    q: np.ndarray                   # [S, H, D] storage dtype
+    ops: list
+    max_blocks_per_seq: int
+    partition_tokens: int = 0       # 0 = let the launcher choose
+    _segments: dict = field(default_factory=dict, repr=False)
+    notes: str = ""
+
+    @property
+    def S(self) -> int:
+        return int(self.ctx.shape[0])
+
+    @property
+    def elem_bytes(self) -> int:
+        return DTYPES[self.dtype][1]
+
+    def kv(self, seq: int, t0: int, t1: int):
+        """Logical K and V rows [t0, t1) of sequence ``seq``: arrays [t1-t0, H, D]."""
+        parts_k, parts_v = [], []
+        for (s0, s1, k, v) in self._segments[seq]:
+            a, b = max(t0, s0), min(t1, s1)
+            if a < b:
+                parts_k.append(k[a - s0:b - s0])
+                parts_v.append(v[a - s0:b - s0])
+        shape = (0, self.H, self.D)
+        empty = np.empty(shape, dtype=DTYPES[self.dtype][0])
+        k = np.concatenate(parts_k) if parts_k else empty
+        v = np.concatenate(parts_v) if parts_v else empty
+        assert k.shape[0] == t1 - t0, (seq, t0, t1, k.shape)
+        return k, v
+
+    def kv_bytes_effective(self) -> int:
+        """K+V bytes a decode over all sequences reads (shared blocks once per sequence)."""
+        return int(self.ctx.sum()) * self.H * self.D * 2 * self.elem_bytes
+
+
+def _placement(cfg: int, NB: int, sub: int = 0):
+    perm = _rng(cfg, _STREAM_PLACE, sub).permutation(NB).astype(np.int32)
+    return int(perm[-1]), perm[:-1].copy()
+
+
+def _simple(cfg, name, H, D, dtype, bs, NB, ctx, scale, part_tokens=0, seed_sub=0):
+    """Independent sequences: prefill of ctx-1 tokens then one decode step."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    S = ctx.shape[0]
+    poison, free_order = _placement(cfg, NB, seed_sub)
+    rs = _rng(cfg, _STREAM_STEP)
+    step_k = _normal(rs, (S, H, D), dtype)
+    step_v = _normal(rs, (S, H, D), dtype)
+    jobs = [(s, (int(ctx[s]) - 1, H, D)) for s in range(S)]
+    hks = _draw_many(cfg, _STREAM_K, jobs, dtype)
+    hvs = _draw_many(cfg, _STREAM_V, jobs, dtype)
+    segs = {}
+    for s in range(S):
+        n = int(ctx[s]) - 1
+        segs[s] = [(0, n, hks[s], hvs[s]), (n, n + 1, step_k[s:s + 1], step_v[s:s + 1])]
+    q = _normal(_rng(cfg, _STREAM_Q), (S, H, D), dtype)
+    ops = [("add", s, int(ctx[s]) - 1) for s in range(S)]
+    ops.append(("step", list(range(S))))
+    maxb = int(math.ceil(int(ctx.max()) / bs))
+    return Workload(cfg=cfg, name=name, H=H, D=D, dtype=dtype, bs=bs, NB=NB,
+                    scale=scale, free_order=free_order, poison_block=poison,
+                    ctx=ctx, q=q, ops=ops, max_blocks_per_seq=maxb,
+                    partition_tokens=part_tokens, _segments=segs)
+
+
+def _config4(cow: bool, bs: int = 16) -> Workload:
+    """8 groups x 8 samples sharing one 1024-token prompt, private tails U[1,256].
+
+    cow=False: the samples fork right after the prompt, which ends on a block
+    boundary, so every tail starts in a fresh private block.
+    cow=True: each group first generates r_g in [1,15] common tokens, then forks;
+    the shared last block is partly filled, so the first divergent append of all
+    but the last sample of a group copies it on write."""
+    cfg, H, D, dtype, G, per = 4, 40, 128, "bf16", 8, 8
+    prompt = 1024
+    NB = 4096
+    poison, free_order = _placement(cfg, NB)
+    rt = _rng(cfg, _STREAM_TAIL)
+    tails = rt.integers(1, 257, size=G * per).astype(np.int64)
+    r = _rng(cfg, _STREAM_FORK).integers(1, 16, size=G).astype(np.int64)
+    rs = _rng(cfg, _STREAM_STEP)
+    step_k = _normal(rs, (G * per, H, D), dtype)
+    step_v = _normal(rs, (G * per, H, D), dtype)
+    segs, ops, ctx = {}, [], np.zeros(G * per, dtype=np.int64)
+    shared_len = [prompt + (int(r[g]) if cow else 0) for g in range(G)]
+    # T = tokens after the shared part, including the step token
+    T = [int(tails[j]) if not cow else
+         max(int(tails[j]), int(r[j // per]) + 1) - int(r[j // per]) for j in range(G * per)]
+    jobs = [(g, (shared_len[g], H, D)) for g in range(G)] + \
+           [(1000 + j, (T[j] - 1, H, D)) for j in range(G * per)]
+    ks = _draw_many(cfg, _STREAM_K, jobs, dtype)
+    vs = _draw_many(cfg, _STREAM_V, jobs, dtype)
+    for g in range(G):
+        shared = shared_len[g]
+        pk, pv = ks[g], vs[g]
+        members = [g * per + i for i in range(per)]
+        for j in members:
+            hk, hv = ks[G + j], vs[G + j]
+            segs[j] = [(0, shared, pk, pv),
+                       (shared, shared + T[j] - 1, hk, hv),
+                       (shared + T[j] - 1, shared + T[j], step_k[j:j + 1], step_v[j:j + 1])]
+            ctx[j] = shared + T[j]
+        ops.append(("add", members[0], shared))
+        for j in members[1:]:
+            ops.append(("fork", members[0], j))
+    for j in range(G * per):
+        shared = segs[j][0][1]
+        n = int(ctx[j]) - shared - 1
+        if n > 0:
+            ops.append(("extend", j, n))
+    ops.append(("step", list(range(G * per))))
+    q = _normal(_rng(cfg, _STREAM_Q), (G * per, H, D), dtype)
+    maxb = int(math.ceil(int(ctx.max()) / bs))
+    name = CONFIG_NAMES[4] + ("-cow" if cow else "")
+    return Workload(cfg=4, name=name, H=H, D=D, dtype=dtype, bs=bs, NB=NB,
+                    scale=1.0 / math.sqrt(D), free_order=free_order,
+                    poison_block=poison, ctx=ctx, q=q, ops=ops,
+                    max_blocks_per_seq=maxb, _segments=segs,
+                    notes=("fork after prompt+r_g common tokens" if cow else
+                           "fork at the prompt's block boundary"))
+
+
+def config5_ctx() -> np.ndarray:
+    z = _rng(5, _STREAM_CTX).standard_normal(256)
+    return np.clip(np.round(512.0 * np.exp(0.8 * z)), 1, 4096).astype(np.int64)
+
+
+def make_workload(cfg: int, bs: int | None = None, cow: bool = False,
+                  S: int | None = None) -> Workload:
+    """Build workload ``cfg`` (1..5).
+
+    ``bs`` selects the block size of the config-5 sweep; ``cow`` selects the
+    copy-on-write variant of config 4; ``S`` (config 5 only) keeps the first S
+    sequences, for smaller CPU-side cases."""
+    if cfg == 1:
+        return _simple(1, CONFIG_NAMES[1], 4, 64, "f32", 16, 64, [1, 17, 33, 100],
+                       1.0 / 8.0)
+    if cfg == 2:
+        ctx = _rng(2, _STREAM_CTX).integers(256, 2049, size=30)
+        return _simple(2, CONFIG_NAMES[2], 40, 128, "f16", 16, 4096, ctx,
+                       1.0 / math.sqrt(128))
+    if cfg == 3:
+        return _simple(3, CONFIG_NAMES[3], 40, 128, "f16", 16, 4096, [4096] * 8,
+                       1.0 / math.sqrt(128), part_tokens=512)
+    if cfg == 4:
+        return _config4(cow)
+    if cfg == 5:
+        bs = 16 if bs is None else int(bs)
+        ctx = config5_ctx()
+        if S is not None:
+            ctx = ctx[:S]
+        demand = int(sum(math.ceil(int(c) / bs) for c in ctx))
+        NB = int(math.ceil(1.1 * demand))
+        wl = _simple(5, CONFIG_NAMES[5] + f"-bs{bs}", 40, 128, "f16", bs, NB, ctx,
+                     1.0 / math.sqrt(128), seed_sub=bs)
+        return wl
+    raise ValueError(f"unknown config {cfg}")
