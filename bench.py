@@ -1,0 +1,247 @@
+"""Benchmark: one decode engine step of the LLaMA-13B layer at batch 30 on one MI355X.
+
+A step is one pass of the whole hot path for every sequence of the batch:
+host slot assignment (C++ block manager), block tables shipped to the GPU,
+copy-on-write copies, the slot-mapped cache write of the new tokens' K/V, and
+PagedAttention decode (partition kernel + log-sum-exp reduce).  Inputs are
+synthetic (seeded N(0,1) values, seeded context lengths and block placement)
+and already resident in HBM when timing starts; each step appends one token
+per sequence, so contexts grow by one per step.
+
+Prints ONE JSON line.  Extra diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "pa_decode effective KV GB/s and % of MI355X HBM peak; decode seq-steps/s"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(ctx, H, D, elem, bs):
+    """Algorithmic bytes of one decode over contexts ``ctx``: K and V of every
+    context token (shared blocks counted once per sequence), q, out, the table
+    entries read and the context lengths."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    S = ctx.size
+    kv = int(ctx.sum()) * H * D * 2 * elem
+    return kv + 2 * S * H * D * elem + int((-(-ctx // bs)).sum()) * 4 + 4 * S, kv
+
+
+def partition_kernel_bytes(ctx, H, D, elem, bs):
+    """Bytes the partition kernel must read: K/V, q, table entries, context lengths."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    S = ctx.size
+    return int(ctx.sum()) * H * D * 2 * elem + S * H * D * elem + \
+        int((-(-ctx // bs)).sum()) * 4 + 4 * S
+
+
+def step_bytes(ctx, H, D, elem, bs, ncow):
+    """Whole step: decode + cache write (read k, v; write both rows) + slots + CoW copies."""
+    S = len(ctx)
+    dec, _ = decode_bytes(ctx, H, D, elem, bs)
+    return dec + 4 * S * H * D * elem + 8 * S + ncow * 2 * 2 * H * bs * D * elem
+
+
+def build_state(wl, dtype):
+    """Run the workload's cache-building ops (prefill, forks, extends) on the GPU.
+    Returns the engine and the step's sequence list."""
+    import torch
+    from paged_kv_cache_write_amd.engine import PagedKVEngine
+    from synth import to_torch as to_dev
+    step_seqs = None
+    for op in wl.ops:
+        if op[0] == "step":
+            step_seqs = np.array(op[1], dtype=np.int64)
+    eng = PagedKVEngine(wl.NB, wl.H, wl.D, wl.bs, dtype, wl.max_blocks_per_seq + 64,
+                        len(step_seqs), free_order=wl.free_order, pad_block=wl.poison_block,
+                        fill=0.0)
+    for op in wl.ops:
+        if op[0] == "add":
+            k, v = wl.kv(op[1], 0, op[2])
+            eng.add_sequence(op[1], to_dev(k, wl.dtype), to_dev(v, wl.dtype))
+        elif op[0] == "fork":
+            eng.fork(op[1], op[2])
+        elif op[0] == "extend":
+            t = eng.bm.seq_len(op[1])
+            k, v = wl.kv(op[1], t, t + op[2])
+            eng.extend([op[1]] * op[2], to_dev(k, wl.dtype), to_dev(v, wl.dtype))
+    torch.cuda.synchronize()
+    return eng, step_seqs
+
+
+def cpu_baseline(wl, max_seconds=20.0):
+    """The oracle (float64 NumPy, one thread) on one step of the same workload:
+    the step's cache write plus decode of every sequence.  Repeated until about
+    ``max_seconds`` of work or 3 repetitions."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    r = oracle.run_workload(wl, decode=False)
+    kc, vc = r["k_cache"], r["v_cache"]
+    new_k = np.stack([wl.kv(int(s), int(c) - 1, int(c))[0][0] for s, c in enumerate(r["ctx"])])
+    new_v = np.stack([wl.kv(int(s), int(c) - 1, int(c))[1][0] for s, c in enumerate(r["ctx"])])
+    reps, t_total = 0, 0.0
+    with threadpool_limits(limits=1):
+        while reps < 3 and t_total < max_seconds:
+            t0 = time.perf_counter()
+            oracle.oracle_cache_write(new_k, new_v, r["step_slots"], kc, vc)
+            oracle.oracle_decode(wl.q, kc, vc, r["tables"], r["ctx"], wl.scale, wl.dtype)
+            t_total += time.perf_counter() - t0
+            reps += 1
+    per = t_total / reps
+    b = step_bytes(r["ctx"], wl.H, wl.D, wl.elem_bytes, wl.bs, 0)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full step of {wl.name} (cache write of {wl.S} tokens + decode of "
+                      f"{wl.S} seqs x {wl.H} heads, sum(ctx)={int(r['ctx'].sum())}), "
+                      f"{reps} rep(s), {per:.2f} s each, float64 NumPy, 1 thread, {model}",
+            "seconds_per_step": round(per, 3)}
+
+
+def load_traffic(kernel_tag):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    import hashlib
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec.get("sources", []):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--bs", type=int, default=None, help="block size (config 5)")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "cross-GPU component to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import paged_kv_cache_write_amd as pk
+    pk.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_setup = time.perf_counter()
+    wl = synth.make_workload(args.config, bs=args.bs)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.dtype]
+    eng, seqs = build_state(wl, tdt)
+    from synth import to_torch as to_dev
+    S = seqs.size
+    q = to_dev(wl.q, wl.dtype)
+    k_new = torch.randn(S, wl.H, wl.D, device=dev).to(tdt)
+    v_new = torch.randn(S, wl.H, wl.D, device=dev).to(tdt)
+    out = torch.empty_like(q)
+    eprint(f"setup {time.perf_counter() - t_setup:.1f} s: {wl.name}, S={S}, "
+           f"sum(ctx)={int(wl.ctx.sum())}")
+
+    pt = args.partition_tokens or wl.partition_tokens
+    for _ in range(args.warmup):
+        eng.step(seqs, q, k_new, v_new, wl.scale, out=out, partition_tokens=pt)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    ctxs, ncows = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        eng.step(seqs, q, k_new, v_new, wl.scale, out=out, partition_tokens=pt, timing=evs[i])
+        ctxs.append(eng.last_step["ctx"])
+        ncows.append(eng.last_step["num_cow"])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    elem = wl.elem_bytes
+    total_step_bytes = sum(step_bytes(c, wl.H, wl.D, elem, wl.bs, n) for c, n in zip(ctxs, ncows))
+    dec_bytes = [decode_bytes(c, wl.H, wl.D, elem, wl.bs)[0] for c in ctxs]
+    part_bytes = [partition_kernel_bytes(c, wl.H, wl.D, elem, wl.bs) for c in ctxs]
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    kern_s = float(kern_ms.mean()) / 1e3
+    achieved = float(np.mean(part_bytes)) / kern_s / 1e9
+    value = total_step_bytes / elapsed / 1e9
+    pt_used, nparts, _ = pk.decode_plan(S, wl.H, wl.D, wl.bs, int(ctxs[-1].max()),
+                                        pk.DTYPE_CODES()[tdt], pt)
+    traffic = load_traffic("decode_partition_" + wl.name)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage_dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "seqs": int(S), "heads": wl.H, "head_dim": wl.D,
+                   "block_size": wl.bs, "num_blocks": wl.NB,
+                   "ctx_sum_first_step": int(ctxs[0].sum()),
+                   "ctx_sum_last_step": int(ctxs[-1].sum()),
+                   "partition_tokens": pt_used, "partitions_max": nparts},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(S * args.steps / elapsed, 1),
+        "decode_seq_steps_per_s": round(S / kern_s, 1),
+        "decode_partition_kernel_us": round(kern_s * 1e6, 2),
+        "decode_partition_kernel_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+                                               round(float(np.percentile(kern_ms, 90)) * 1e3, 2)],
+        "decode_bytes_per_step": int(np.mean(dec_bytes)),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_partition_kernel",
+                     "algorithmic_bytes_per_launch": int(np.mean(part_bytes))},
+    }
+    if not args.no_cpu_baseline:
+        t = time.perf_counter()
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        eprint(f"cpu baseline {time.perf_counter() - t:.1f} s")
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

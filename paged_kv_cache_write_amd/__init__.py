@@ -1,0 +1,352 @@
+"""Python binding of libpa.so: the MI355X paged KV-cache write and PagedAttention decode.
+
+Argument marshalling only: each function checks torch tensors (device, dtype,
+shape, contiguity), passes their data pointers and the current HIP stream to
+the C ABI declared in include/pa.h, and raises on a non-zero status.  Every
+step of the computation runs in the library's HIP kernels or its C++ block
+manager.  If libpa.so is missing, loading fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "lib", "PAError", "cache_write", "copy_blocks", "decode", "decode_partitions",
+    "decode_reduce", "decode_plan", "decode_workspace_size", "BlockManager",
+    "DTYPE_CODES", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+_LIB = None
+
+PA_OK = 0
+PA_ERR_NO_BLOCKS = -4
+_c = ctypes
+_vp, _i32, _i64, _f32, _sz = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_float, _c.c_size_t
+_pi32, _pi64 = _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int64)
+
+_DECODE_ARGS = [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _i32,
+                _vp, _vp, _sz, _i32, _vp]
+
+_SIGNATURES = {
+    "pa_status_string": (_c.c_char_p, [_c.c_int]),
+    "pa_version": (_c.c_int, []),
+    "pa_cache_write": (_c.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),
+    "pa_copy_blocks": (_c.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]),
+    "pa_decode": (_c.c_int, _DECODE_ARGS),
+    "pa_decode_partitions": (_c.c_int, _DECODE_ARGS),
+    "pa_decode_reduce": (_c.c_int, _DECODE_ARGS),
+    "pa_decode_plan": (_c.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
+                                  _c.POINTER(_sz)]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_bm_create": (_c.c_int, [_i64, _i32, _vp, _i64, _c.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_add_seq": (_c.c_int, [_vp, _i64, _i64]),
+    "pa_bm_fork": (_c.c_int, [_vp, _i64, _i64]),
+    "pa_bm_append_slot": (_c.c_int, [_vp, _i64, _pi64, _pi32, _pi32]),
+    "pa_bm_append_slots": (_c.c_int, [_vp, _vp, _i32, _vp, _vp, _pi32, _pi32]),
+    "pa_bm_step": (_c.c_int, [_vp, _vp, _i32, _vp, _vp, _pi32, _vp, _i32, _i32, _vp]),
+    "pa_bm_free_seq": (_c.c_int, [_vp, _i64]),
+    "pa_bm_slots": (_c.c_int, [_vp, _i64, _i64, _i64, _vp]),
+    "pa_bm_block_table": (_c.c_int, [_vp, _i64, _vp, _i32, _pi32]),
+    "pa_bm_block_tables": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp]),
+    "pa_bm_seq_len": (_i64, [_vp, _i64]),
+    "pa_bm_refcount": (_i32, [_vp, _i32]),
+    "pa_bm_num_free": (_i64, [_vp]),
+    "pa_bm_num_seqs": (_i64, [_vp]),
+    "pa_bm_free_list": (_i64, [_vp, _vp, _i64]),
+}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().pa_status_string(status).decode()
+        super().__init__(f"{where}: {msg} ({status})")
+
+
+def lib():
+    """Load libpa.so (after torch, so that both use torch's HIP runtime)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_write_amd.build`")
+        import torch  # noqa: F401  (loads torch's libamdhip64 first)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def _check(status: int, where: str):
+    if status != PA_OK:
+        raise PAError(status, where)
+
+
+# ----------------------------------------------------------------- device
+def _torch():
+    import torch
+    return torch
+
+
+def DTYPE_CODES():
+    torch = _torch()
+    return {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+def _dt(t) -> int:
+    code = DTYPE_CODES().get(t.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return code
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    """k_cache[s//bs, :, s%bs, :] = k[n] (and v) for every slot s = slot_mapping[n] >= 0."""
+    torch = _torch()
+    N, H, D = k.shape
+    NB, Hc, bs, Dc = k_cache.shape
+    if (Hc, Dc) != (H, D) or v.shape != k.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if slot_mapping.shape != (N,):
+        raise ValueError("slot_mapping must be [N]")
+    for t in (v, k_cache, v_cache):
+        if t.dtype != k.dtype:
+            raise TypeError("k, v and the caches must share a dtype")
+    rc = lib().pa_cache_write(
+        _dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int64), N,
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), NB, H, D, bs, _dt(k),
+        _stream(stream, k.device))
+    _check(rc, "pa_cache_write")
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """k_cache[dst] = k_cache[src] (and v) for each (src, dst) row of block_pairs [n, 2]."""
+    torch = _torch()
+    NB, H, bs, D = k_cache.shape
+    n = int(block_pairs.shape[0])
+    if n and tuple(block_pairs.shape) != (n, 2):
+        raise ValueError("block_pairs must be [n, 2]")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("cache mismatch")
+    if n == 0:
+        return
+    rc = lib().pa_copy_blocks(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_pairs, "block_pairs", torch.int32), n, NB, H, D, bs, _dt(k_cache),
+        _stream(stream, k_cache.device))
+    _check(rc, "pa_copy_blocks")
+
+
+def decode_plan(num_seqs, num_heads, head_dim, block_size, max_context_len, dtype_code,
+                partition_tokens=0):
+    """(tokens per partition, partitions of the longest context, workspace bytes)."""
+    pt, nparts, ws = _c.c_int32(), _c.c_int32(), _c.c_size_t()
+    rc = lib().pa_decode_plan(num_seqs, num_heads, head_dim, block_size, max_context_len,
+                              dtype_code, partition_tokens, _c.byref(pt), _c.byref(nparts),
+                              _c.byref(ws))
+    _check(rc, "pa_decode_plan")
+    return pt.value, nparts.value, ws.value
+
+
+def decode_workspace_size(num_seqs, num_heads, head_dim, block_size, max_context_len,
+                          dtype_code, partition_tokens=0):
+    return decode_plan(num_seqs, num_heads, head_dim, block_size, max_context_len, dtype_code,
+                       partition_tokens)[2]
+
+
+def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 max_context_len, out, workspace, partition_tokens, stream):
+    torch = _torch()
+    S, H, D = q.shape
+    NB, Hc, bs, Dc = k_cache.shape
+    if (Hc, Dc) != (H, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, max_blocks]")
+    if context_lens.shape != (S,):
+        raise ValueError("context_lens must be [S]")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    for t in (k_cache, v_cache):
+        if t.dtype != q.dtype:
+            raise TypeError("q and the caches must share a dtype")
+    dt = _dt(q)
+    ws_need = decode_workspace_size(S, H, D, bs, int(max_context_len), dt, partition_tokens)
+    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = getattr(lib(), fn_name)(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), S, H, D, bs, NB, float(scale),
+        int(max_context_len), dt, _dev(out, "out"), ws_ptr, ws_bytes, int(partition_tokens),
+        _stream(stream, q.device))
+    _check(rc, fn_name)
+    return out
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=None,
+           workspace=None, partition_tokens=0, stream=None):
+    """PagedAttention decode of one query token per sequence; returns out [S, H, D]."""
+    return _decode_call("pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale,
+                        max_context_len, out, workspace, partition_tokens, stream)
+
+
+def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                      out, workspace=None, partition_tokens=0, stream=None):
+    """First launch of decode (per-partition attention); see pa_decode_partitions."""
+    return _decode_call("pa_decode_partitions", q, k_cache, v_cache, block_tables, context_lens,
+                        scale, max_context_len, out, workspace, partition_tokens, stream)
+
+
+def decode_reduce(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                  out, workspace=None, partition_tokens=0, stream=None):
+    """Second launch of decode (log-sum-exp merge of partitions); see pa_decode_reduce."""
+    return _decode_call("pa_decode_reduce", q, k_cache, v_cache, block_tables, context_lens,
+                        scale, max_context_len, out, workspace, partition_tokens, stream)
+
+
+# ---------------------------------------------------------- block manager
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_vp) if a.size else None
+
+
+class BlockManager:
+    """Host block manager (C++): FIFO free list, refcounts, block tables, copy-on-write."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        h = _vp()
+        if free_order is None:
+            rc = lib().pa_bm_create(num_blocks, block_size, None, 0, _c.byref(h))
+        else:
+            fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            rc = lib().pa_bm_create(num_blocks, block_size, _ptr(fo), fo.size, _c.byref(h))
+        _check(rc, "pa_bm_create")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _LIB is not None:
+            _LIB.pa_bm_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq: int, num_tokens: int):
+        _check(lib().pa_bm_add_seq(self._h, seq, num_tokens), "pa_bm_add_seq")
+
+    def fork(self, parent: int, child: int):
+        _check(lib().pa_bm_fork(self._h, parent, child), "pa_bm_fork")
+
+    def append_slot(self, seq: int):
+        """Returns (slot, cow) with cow None or (src, dst)."""
+        slot, src, dst = _c.c_int64(), _c.c_int32(), _c.c_int32()
+        rc = lib().pa_bm_append_slot(self._h, seq, _c.byref(slot), _c.byref(src), _c.byref(dst))
+        if rc < 0:
+            _check(rc, "pa_bm_append_slot")
+        return slot.value, ((src.value, dst.value) if rc == 1 else None)
+
+    def append_slots(self, seqs):
+        """Append one token to each listed sequence in order: (slots int64 [n], cow int32 [k, 2])."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = seqs.size
+        slots = np.empty(n, dtype=np.int64)
+        cows = np.empty(2 * max(n, 1), dtype=np.int32)
+        ncow, done = _c.c_int32(), _c.c_int32()
+        rc = lib().pa_bm_append_slots(self._h, _ptr(seqs), n, _ptr(slots), _ptr(cows),
+                                      _c.byref(ncow), _c.byref(done))
+        _check(rc, "pa_bm_append_slots")
+        return slots, cows[:2 * ncow.value].reshape(-1, 2).copy()
+
+    def step_into(self, seqs: np.ndarray, slots: np.ndarray, cows: np.ndarray,
+                  tables: np.ndarray, pad: int, context_lens: np.ndarray) -> int:
+        """pa_bm_step into caller arrays (views of pinned memory); returns the CoW count."""
+        ncow = _c.c_int32()
+        rc = lib().pa_bm_step(self._h, _ptr(seqs), seqs.size, _ptr(slots), _ptr(cows),
+                              _c.byref(ncow), _ptr(tables), tables.shape[1], pad,
+                              _ptr(context_lens))
+        _check(rc, "pa_bm_step")
+        return ncow.value
+
+    def free_seq(self, seq: int):
+        _check(lib().pa_bm_free_seq(self._h, seq), "pa_bm_free_seq")
+
+    def slots(self, seq: int, start: int, n: int) -> np.ndarray:
+        out = np.empty(n, dtype=np.int64)
+        _check(lib().pa_bm_slots(self._h, seq, start, n, _ptr(out)), "pa_bm_slots")
+        return out
+
+    def block_table(self, seq: int) -> list:
+        n = _c.c_int32()
+        rc = lib().pa_bm_block_table(self._h, seq, None, 0, _c.byref(n))
+        if rc not in (PA_OK, -8):
+            _check(rc, "pa_bm_block_table")
+        out = np.empty(n.value, dtype=np.int32)
+        _check(lib().pa_bm_block_table(self._h, seq, _ptr(out), n.value, _c.byref(n)),
+               "pa_bm_block_table")
+        return out.tolist()
+
+    def block_tables(self, seqs, max_blocks: int, pad: int):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        tables = np.empty((seqs.size, max_blocks), dtype=np.int32)
+        ctx = np.empty(seqs.size, dtype=np.int32)
+        _check(lib().pa_bm_block_tables(self._h, _ptr(seqs), seqs.size, _ptr(tables), max_blocks,
+                                        pad, _ptr(ctx)), "pa_bm_block_tables")
+        return tables, ctx
+
+    def seq_len(self, seq: int) -> int:
+        n = lib().pa_bm_seq_len(self._h, seq)
+        if n < 0:
+            _check(int(n), "pa_bm_seq_len")
+        return int(n)
+
+    def refcount(self, block: int) -> int:
+        r = lib().pa_bm_refcount(self._h, block)
+        if r < 0:
+            _check(int(r), "pa_bm_refcount")
+        return int(r)
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_bm_num_free(self._h))
+
+    @property
+    def num_seqs(self) -> int:
+        return int(lib().pa_bm_num_seqs(self._h))
+
+    def free_list(self) -> list:
+        n = int(lib().pa_bm_free_list(self._h, None, 0))
+        out = np.empty(n, dtype=np.int32)
+        lib().pa_bm_free_list(self._h, _ptr(out), n)
+        return out.tolist()
+
+    def refcounts(self) -> list:
+        return [self.refcount(b) for b in range(self.num_blocks)]

@@ -1,0 +1,269 @@
+// Host block manager: shared pool, FIFO free list, per-block reference counts,
+// per-sequence block tables and copy-on-write planning.  No device memory.
+//
+// Method (comfyai.app "6.4 PagedAttention" 6.4.1-6.4.3; polomodov.tech
+// "vLLM and PagedAttention" slides 10-14):
+//   * logical block j of a sequence maps to a physical block of one shared
+//     pool; a free block goes to whichever sequence needs it next;
+//   * a block is taken only when the previous one is full;
+//   * forked sequences share blocks; a block's reference count is the number
+//     of table entries that name it;
+//   * writing into a shared last block first copies it: the writer gets a new
+//     block (count 1), the old block's count drops by one.
+#include <cstdint>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pa.h"
+
+struct SeqState {
+  std::vector<int32_t> table;
+  int64_t len = 0;
+};
+
+struct pa_bm {
+  int64_t num_blocks = 0;
+  int32_t bs = 0;
+  std::deque<int32_t> free_list;
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, SeqState> seqs;
+};
+
+namespace {
+
+bool pop_free(pa_bm* bm, int32_t* out) {
+  if (bm->free_list.empty()) return false;
+  *out = bm->free_list.front();
+  bm->free_list.pop_front();
+  bm->ref[*out] = 1;
+  return true;
+}
+
+int append_one(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
+               int32_t* cow_dst) {
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  SeqState& st = it->second;
+  const int64_t t = st.len;
+  int copied = 0;
+  if (t % bm->bs == 0) {
+    int32_t b;
+    if (!pop_free(bm, &b)) return PA_ERR_NO_BLOCKS;
+    st.table.push_back(b);
+  } else {
+    int32_t last = st.table.back();
+    if (bm->ref[last] > 1) {
+      int32_t b;
+      if (!pop_free(bm, &b)) return PA_ERR_NO_BLOCKS;
+      bm->ref[last] -= 1;
+      st.table.back() = b;
+      if (cow_src) *cow_src = last;
+      if (cow_dst) *cow_dst = b;
+      copied = 1;
+    }
+  }
+  if (slot) *slot = int64_t(st.table[t / bm->bs]) * bm->bs + t % bm->bs;
+  st.len = t + 1;
+  return copied;
+}
+
+void export_row(const SeqState& st, int32_t* row, int32_t width, int32_t pad) {
+  const int32_t n = int32_t(st.table.size());
+  for (int32_t j = 0; j < width; ++j) row[j] = j < n ? st.table[j] : pad;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_bm_create(int64_t num_blocks, int32_t block_size,
+                 const int32_t* free_order, int64_t num_free, pa_bm** out) {
+  if (!out || num_blocks <= 0 || num_blocks > INT32_MAX || block_size <= 0)
+    return PA_ERR_INVALID;
+  *out = nullptr;
+  pa_bm* bm = new (std::nothrow) pa_bm;
+  if (!bm) return PA_ERR_INVALID;
+  bm->num_blocks = num_blocks;
+  bm->bs = block_size;
+  bm->ref.assign(size_t(num_blocks), 0);
+  if (free_order) {
+    if (num_free < 0 || num_free > num_blocks) {
+      delete bm;
+      return PA_ERR_INVALID;
+    }
+    std::vector<char> seen(size_t(num_blocks), 0);
+    for (int64_t i = 0; i < num_free; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        return PA_ERR_INVALID;
+      }
+      seen[b] = 1;
+      bm->free_list.push_back(b);
+    }
+  } else {
+    for (int64_t b = 0; b < num_blocks; ++b) bm->free_list.push_back(int32_t(b));
+  }
+  *out = bm;
+  return PA_OK;
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+int pa_bm_add_seq(pa_bm* bm, int64_t seq, int64_t num_tokens) {
+  if (!bm || num_tokens < 0) return PA_ERR_INVALID;
+  if (bm->seqs.count(seq)) return PA_ERR_EXISTS;
+  const int64_t need = (num_tokens + bm->bs - 1) / bm->bs;
+  if (need > int64_t(bm->free_list.size())) return PA_ERR_NO_BLOCKS;
+  SeqState st;
+  st.table.reserve(size_t(need));
+  for (int64_t j = 0; j < need; ++j) {
+    int32_t b;
+    pop_free(bm, &b);
+    st.table.push_back(b);
+  }
+  st.len = num_tokens;
+  bm->seqs.emplace(seq, std::move(st));
+  return PA_OK;
+}
+
+int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
+  if (!bm) return PA_ERR_INVALID;
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  if (bm->seqs.count(child)) return PA_ERR_EXISTS;
+  SeqState st = it->second;
+  for (int32_t b : st.table) bm->ref[b] += 1;
+  bm->seqs.emplace(child, std::move(st));
+  return PA_OK;
+}
+
+int pa_bm_append_slot(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
+                      int32_t* cow_dst) {
+  if (!bm) return PA_ERR_INVALID;
+  return append_one(bm, seq, slot, cow_src, cow_dst);
+}
+
+int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n,
+                       int64_t* slots, int32_t* cow_pairs, int32_t* num_cow,
+                       int32_t* num_done) {
+  if (num_done) *num_done = 0;
+  if (num_cow) *num_cow = 0;
+  if (!bm || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)))
+    return PA_ERR_INVALID;
+  int32_t ncow = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t src = -1, dst = -1;
+    int rc = append_one(bm, seqs[i], &slots[i], &src, &dst);
+    if (rc < 0) {
+      if (num_cow) *num_cow = ncow;
+      return rc;
+    }
+    if (rc == 1) {
+      cow_pairs[2 * ncow] = src;
+      cow_pairs[2 * ncow + 1] = dst;
+      ++ncow;
+    }
+    if (num_done) *num_done = i + 1;
+  }
+  if (num_cow) *num_cow = ncow;
+  return PA_OK;
+}
+
+int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int32_t n,
+                       int32_t* tables, int32_t max_blocks, int32_t pad,
+                       int32_t* context_lens) {
+  if (!bm || n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !tables)))
+    return PA_ERR_INVALID;
+  int rc = PA_OK;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+    const SeqState& st = it->second;
+    if (int64_t(st.table.size()) > max_blocks) rc = PA_ERR_CAPACITY;
+    export_row(st, tables + int64_t(i) * max_blocks, max_blocks, pad);
+    if (context_lens) context_lens[i] = int32_t(st.len);
+  }
+  return rc;
+}
+
+int pa_bm_step(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots,
+               int32_t* cow_pairs, int32_t* num_cow, int32_t* tables,
+               int32_t max_blocks, int32_t pad, int32_t* context_lens) {
+  int32_t done = 0;
+  int rc = pa_bm_append_slots(bm, seqs, n, slots, cow_pairs, num_cow, &done);
+  if (rc != PA_OK) return rc;
+  return pa_bm_block_tables(bm, seqs, n, tables, max_blocks, pad, context_lens);
+}
+
+int pa_bm_free_seq(pa_bm* bm, int64_t seq) {
+  if (!bm) return PA_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  for (int32_t b : it->second.table) {
+    bm->ref[b] -= 1;
+    if (bm->ref[b] == 0) bm->free_list.push_back(b);
+  }
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+int pa_bm_slots(const pa_bm* bm, int64_t seq, int64_t start, int64_t n,
+                int64_t* out) {
+  if (!bm || start < 0 || n < 0 || (n > 0 && !out)) return PA_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  const SeqState& st = it->second;
+  if (start + n > st.len) return PA_ERR_INVALID;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t t = start + i;
+    out[i] = int64_t(st.table[t / bm->bs]) * bm->bs + t % bm->bs;
+  }
+  return PA_OK;
+}
+
+int pa_bm_block_table(const pa_bm* bm, int64_t seq, int32_t* out, int32_t cap,
+                      int32_t* n) {
+  if (!bm || cap < 0 || (cap > 0 && !out)) return PA_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
+  const auto& tab = it->second.table;
+  if (n) *n = int32_t(tab.size());
+  if (int64_t(tab.size()) > cap) return PA_ERR_CAPACITY;
+  if (!tab.empty()) std::memcpy(out, tab.data(), tab.size() * sizeof(int32_t));
+  return PA_OK;
+}
+
+int64_t pa_bm_seq_len(const pa_bm* bm, int64_t seq) {
+  if (!bm) return PA_ERR_INVALID;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? int64_t(PA_ERR_NOT_FOUND) : it->second.len;
+}
+
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return PA_ERR_INVALID;
+  return bm->ref[block];
+}
+
+int64_t pa_bm_num_free(const pa_bm* bm) {
+  return bm ? int64_t(bm->free_list.size()) : int64_t(PA_ERR_INVALID);
+}
+
+int64_t pa_bm_num_seqs(const pa_bm* bm) {
+  return bm ? int64_t(bm->seqs.size()) : int64_t(PA_ERR_INVALID);
+}
+
+int64_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int64_t cap) {
+  if (!bm || cap < 0 || (cap > 0 && !out)) return PA_ERR_INVALID;
+  int64_t i = 0;
+  for (int32_t b : bm->free_list) {
+    if (i < cap) out[i] = b;
+    ++i;
+  }
+  return i;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Slot-mapped KV-cache write and whole-block copy (copy-on-write) for gfx950.
+//
+// Cache write (polomodov.tech "vLLM and PagedAttention" slide 11: a new
+// token's K/V go into the free slot of the sequence's last block): token n
+// with slot s >= 0 is stored at [s / bs, h, s % bs, :] of both caches.
+// Block copy (comfyai.app "6.4 PagedAttention" 6.4.3; slide 13: only the last
+// block is copied when shared samples diverge): dst block = src block.
+//
+// Both are pure 16-byte moves: each lane carries one 16-byte slice of a
+// token row (D elements), so a wave moves 1 KiB of contiguous source per
+// instruction and writes whole 16-byte slices of contiguous destination rows.
+#include "launch_common.hpp"
+#include "pa_device.hpp"
+
+namespace pa {
+
+constexpr int kCwThreads = 256;
+
+// One lane per 16-byte slice of (token, head) row; rows_per_token = H.
+__global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
+    const char* __restrict__ k, const char* __restrict__ v, const int64_t* __restrict__ slots,
+    char* __restrict__ k_cache, char* __restrict__ v_cache, int64_t total_vecs, int H,
+    int vecs_per_row, int row_bytes, int log2_bs) {
+  const int64_t g = int64_t(blockIdx.x) * kCwThreads + threadIdx.x;
+  if (g >= total_vecs) return;
+  const int64_t row = g / vecs_per_row;  // n * H + h
+  const int col = int(g - row * vecs_per_row);
+  const int64_t n = row / H;
+  const int h = int(row - n * H);
+  const int64_t slot = slots[n];
+  if (slot < 0) return;
+  const int64_t blk = slot >> log2_bs;
+  const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
+  const int64_t dst = ((((blk * H + h) << log2_bs) + off) * row_bytes) + int64_t(col) * 16;
+  const int64_t src = g * 16;
+  *reinterpret_cast<u32x4*>(k_cache + dst) = *reinterpret_cast<const u32x4*>(k + src);
+  *reinterpret_cast<u32x4*>(v_cache + dst) = *reinterpret_cast<const u32x4*>(v + src);
+}
+
+// blockIdx.y = pair; blocks of blockIdx.x stride over the tile's 16-byte vectors.
+__global__ __launch_bounds__(kCwThreads) void copy_blocks_kernel(
+    char* __restrict__ k_cache, char* __restrict__ v_cache, const int32_t* __restrict__ pairs,
+    int64_t tile_vecs) {
+  const int pair = blockIdx.y;
+  const int64_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache) + src * tile_vecs;
+  const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache) + src * tile_vecs;
+  u32x4* kd = reinterpret_cast<u32x4*>(k_cache) + dst * tile_vecs;
+  u32x4* vd = reinterpret_cast<u32x4*>(v_cache) + dst * tile_vecs;
+  for (int64_t i = int64_t(blockIdx.x) * kCwThreads + threadIdx.x; i < tile_vecs;
+       i += int64_t(gridDim.x) * kCwThreads) {
+    const u32x4 a = ks[i];
+    const u32x4 b = vs[i];
+    kd[i] = a;
+    vd[i] = b;
+  }
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                   void* k_cache, void* v_cache, int64_t num_blocks, int32_t num_heads,
+                   int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+  int rc = pa::check_shape(head_dim, block_size, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_tokens < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID;
+  if (!pa::aligned16(k) || !pa::aligned16(v) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache))
+    return PA_ERR_INVALID;
+  const int row_bytes = head_dim * pa::elem_bytes(dtype);
+  const int vecs_per_row = row_bytes / 16;
+  const int64_t total = num_tokens * num_heads * vecs_per_row;
+  const int64_t nblocks = (total + pa::kCwThreads - 1) / pa::kCwThreads;
+  if (nblocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(pa::cache_write_kernel, dim3(unsigned(nblocks)), dim3(pa::kCwThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const char*>(k),
+                     static_cast<const char*>(v), slot_mapping, static_cast<char*>(k_cache),
+                     static_cast<char*>(v_cache), total, num_heads, vecs_per_row, row_bytes,
+                     pa::log2_exact(block_size));
+  return pa::launch_status();
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
+                   int64_t num_blocks, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                   int32_t dtype, void* stream) {
+  int rc = pa::check_shape(head_dim, block_size, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_pairs < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > 65535) return PA_ERR_UNSUPPORTED;
+  if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID;
+  if (!pa::aligned16(k_cache) || !pa::aligned16(v_cache)) return PA_ERR_INVALID;
+  const int64_t tile_vecs =
+      int64_t(num_heads) * block_size * head_dim * pa::elem_bytes(dtype) / 16;
+  int64_t gx = (tile_vecs + pa::kCwThreads - 1) / pa::kCwThreads;
+  if (gx > 64) gx = 64;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(pa::copy_blocks_kernel, dim3(unsigned(gx), unsigned(num_pairs)),
+                     dim3(pa::kCwThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), block_pairs,
+                     tile_vecs);
+  return pa::launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,457 @@
+// PagedAttention decode for gfx950: one query token per sequence attends over
+// K/V stored in fixed-size blocks scattered across a shared pool.
+//
+// What is computed (polomodov.tech "vLLM and PagedAttention" slides 9-10;
+// comfyai.app "6.4 PagedAttention" 6.4.1; brentwoodlivery "5.3.18", the
+// card saying paging leaves the attention arithmetic unchanged): for each
+// sequence s and head h, softmax(scale * q K^T) V over the sequence's first
+// context_lens[s] tokens, where token t lives in physical block
+// block_tables[s, t / bs] at offset t % bs.
+//
+// How (MI355X design, not taken from the pages):
+//  * The work of one (sequence, head) is split into context partitions of
+//    part_tokens tokens; one 256-thread workgroup (4 waves) handles one
+//    (partition, head, sequence).  Partitions give the 256 CUs enough
+//    workgroups when there are few sequences or long contexts, and even out
+//    the work when context lengths differ.
+//  * A (block, head) tile is bs * D contiguous elements.  A lane owns a
+//    16-byte slice of one token row, so one wave-wide load instruction reads
+//    64 x 16 B = 1 KiB of consecutive bytes of one tile: fully coalesced.
+//    Each lane consumes exactly the bytes it loaded, so K/V go from HBM
+//    straight to registers; there is no LDS staging in the streaming loop.
+//  * A wave works on chunks of U load instructions for K and U for V issued
+//    back to back, so each lane has 2U 16-byte loads in flight.
+//  * q.k partial dots use v_dot2_f32_{f16,bf16} (exact products, float32
+//    sums); the lanes of one token row are summed with DPP butterflies; the
+//    softmax is the online (running max / running sum) form in base 2 with
+//    scale*log2(e) folded into the logit; P.V accumulates in float32
+//    (v_fma_mix_f32 for fp16).
+//  * The partition's table entries are loaded once per wave into one VGPR
+//    (lane j = j-th block of the partition) and read with v_readlane, so a
+//    block's address is wave-uniform scalar arithmetic.
+//  * Waves merge (max, sum, accumulator) across token rows with shuffles,
+//    then across waves through LDS.  A sequence with one partition stores its
+//    output row directly; otherwise the partial (max, sum, normalised output)
+//    goes to the workspace and a second kernel merges partitions with the
+//    log-sum-exp rule.
+#include "launch_common.hpp"
+#include "pa_device.hpp"
+
+namespace pa {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so max - max never is NaN
+
+struct DecodeParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* ws_ml;  // [S, H, max_parts, 2]: running max (log2 units), sum
+  float* ws_o;   // [S, H, max_parts, D]: partition output normalised by its sum
+  int H;
+  int maxB;
+  int log2_bs;
+  int part_tokens;
+  int max_parts;
+  float qk_scale;  // scale * log2(e)
+};
+
+template <class DT, int D, int U>
+struct Shape {
+  static constexpr int kVec = DT::kVec;
+  static constexpr int kLPT = D / kVec;          // lanes per token row
+  static constexpr int kTPI = kWave / kLPT;      // token rows per wave load
+  static constexpr int kChunk = kTPI * U;        // tokens per wave chunk
+  static_assert(kLPT >= 4 && kLPT <= 64, "row width");
+};
+
+__device__ __forceinline__ u32x4 load16(const char* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Per-wave state for streaming one partition's chunks.
+struct ChunkCtx {
+  const char* kc;
+  const char* vc;
+  size_t tile_bytes;   // bytes of one (block, head) tile: bs * D * elem
+  size_t head_off;     // h * tile_bytes
+  size_t block_stride; // H * tile_bytes
+  uint32_t lane_off;   // this lane's byte offset inside a group of token rows
+  int tbl;             // this lane's table entry (lane j = j-th block of the partition)
+  int log2_bs;
+  int bs_mask;
+  int row;             // this lane's token row inside a load group
+  int ntok;            // tokens in the partition
+  int last_group;      // first token of the last group holding a valid token
+  float qk_scale;
+};
+
+// One chunk of U token-row groups: issue 2U 16-byte loads (K and V), then
+// q.k, online softmax update and P.V.  kMasked is the partition's last,
+// partial chunk: its loads are clamped to rows of groups that hold valid
+// tokens (so no extra memory is touched and no table entry past the
+// sequence is read) and the loaded values of invalid tokens are zeroed.
+template <class DT, int D, int U, bool kMasked>
+__device__ __forceinline__ void chunk_step(const ChunkCtx& cx, int t0, u32x4 qv, float& m,
+                                           float& l, float* acc) {
+  using Sh = Shape<DT, D, U>;
+  constexpr int kVec = DT::kVec;
+  constexpr uint32_t kRowBytes = uint32_t(D) * sizeof(typename DT::T);
+  u32x4 kr[U], vr[U];
+  bool ok[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    int tt = t0 + i * Sh::kTPI;  // wave-uniform token offset in the partition
+    uint32_t off = cx.lane_off;
+    ok[i] = true;
+    if constexpr (kMasked) {
+      ok[i] = tt + cx.row < cx.ntok;
+      tt = min(tt, cx.last_group);
+      if (tt + cx.row >= cx.ntok) off = cx.lane_off - uint32_t(cx.row) * kRowBytes;  // row 0
+    }
+    const int pb = __builtin_amdgcn_readlane(cx.tbl, tt >> cx.log2_bs);
+    const size_t tile = size_t(pb) * cx.block_stride + cx.head_off +
+                        size_t(tt & cx.bs_mask) * kRowBytes;
+    kr[i] = load16(cx.kc + tile + off);
+    vr[i] = load16(cx.vc + tile + off);
+  }
+  // Keep all 2U loads in flight before any of them is consumed: without this
+  // fence the scheduler interleaves the dot products with the loads to save
+  // registers, which serialises the memory latency.
+  __builtin_amdgcn_sched_barrier(0);
+  float sc[U];
+  float mx = kNegBig;
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const float d = group_sum<Sh::kLPT>(dot16(DT{}, kr[i], qv, 0.f));
+    sc[i] = d * cx.qk_scale;
+    if constexpr (kMasked) {
+      sc[i] = ok[i] ? sc[i] : -__builtin_inff();
+      vr[i] = ok[i] ? vr[i] : u32x4{0, 0, 0, 0};
+    }
+    mx = fmaxf(mx, sc[i]);
+  }
+  const float mn = fmaxf(m, mx);
+  const float alpha = fast_exp2(m - mn);
+  l *= alpha;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) acc[e] *= alpha;
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const float p = fast_exp2(sc[i] - mn);
+    l += p;
+    axpy16(DT{}, acc, vr[i], p);
+  }
+  m = mn;
+}
+
+template <class DT, int D, int U>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams P) {
+  using T = typename DT::T;
+  using Sh = Shape<DT, D, U>;
+  constexpr int kVec = DT::kVec;
+  constexpr size_t kRowBytes = size_t(D) * sizeof(T);
+
+  const int part = blockIdx.x;
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = wave_uniform(threadIdx.x / kWave);
+  const int H = P.H;
+  const int log2_bs = P.log2_bs;
+  const size_t row_id = size_t(s) * H + h;
+
+  int ctx = P.context_lens[s];
+  // never read past the table row or past the launched partitions
+  ctx = min(ctx, min(P.maxB << log2_bs, P.max_parts * P.part_tokens));
+  const int nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
+  if (part >= nparts) {
+    if (part == 0) {  // empty context: zero output row
+      T* o = reinterpret_cast<T*>(P.out) + row_id * D;
+      for (int d = threadIdx.x; d < D; d += kThreads) o[d] = to_store(DT{}, 0.f);
+    }
+    return;
+  }
+  const int p0 = part * P.part_tokens;
+  const int ntok = min(P.part_tokens, ctx - p0);
+
+  const int row = lane / Sh::kLPT;
+  const int col = lane % Sh::kLPT;
+
+  const u32x4 qv = load16(reinterpret_cast<const char*>(P.q) + row_id * kRowBytes + col * 16);
+
+  // Table entries of this partition, one per lane (partition start is a
+  // multiple of the block size; a partition spans at most 64 blocks).
+  const int blk0 = p0 >> log2_bs;
+  const int nblk = ((ntok - 1) >> log2_bs) + 1;
+  int tbl = 0;
+  if (lane < nblk) tbl = P.block_tables[size_t(s) * P.maxB + blk0 + lane];
+
+  const char* kc = reinterpret_cast<const char*>(P.k_cache);
+  const char* vc = reinterpret_cast<const char*>(P.v_cache);
+  const size_t tile_bytes = kRowBytes << log2_bs;
+  const int bs_mask = (1 << log2_bs) - 1;
+  const uint32_t lane_off = uint32_t(row) * uint32_t(kRowBytes) + uint32_t(col) * 16u;
+
+  float m = kNegBig, l = 0.f;
+  float acc[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) acc[e] = 0.f;
+
+  const int nchunks = (ntok + Sh::kChunk - 1) / Sh::kChunk;
+  const int nfull = ntok / Sh::kChunk;
+  // Last token-row group that holds a valid token (wave-uniform).
+  const int last_group = (ntok - 1) & ~(Sh::kTPI - 1);
+  ChunkCtx cx{kc, vc, tile_bytes, size_t(h) * tile_bytes, size_t(H) * tile_bytes, lane_off,
+              tbl, log2_bs, bs_mask, row, ntok, last_group, P.qk_scale};
+  int c = wave;
+  for (; c < nfull; c += kWaves) chunk_step<DT, D, U, false>(cx, c * Sh::kChunk, qv, m, l, acc);
+  if (c < nchunks) chunk_step<DT, D, U, true>(cx, c * Sh::kChunk, qv, m, l, acc);
+
+  // Merge the token rows of the wave (lanes with equal col).
+#pragma unroll
+  for (int off = Sh::kLPT; off < kWave; off <<= 1) {
+    const float mo = __shfl_xor(m, off, kWave);
+    const float lo = __shfl_xor(l, off, kWave);
+    const float mn = fmaxf(m, mo);
+    const float a = fast_exp2(m - mn), b = fast_exp2(mo - mn);
+    l = l * a + lo * b;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc[e] = acc[e] * a + __shfl_xor(acc[e], off, kWave) * b;
+    m = mn;
+  }
+
+  // Merge the waves through LDS.
+  __shared__ float s_ml[kWaves][2];
+  __shared__ float s_acc[kWaves][D];
+  if (row == 0) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) s_acc[wave][col * kVec + e] = acc[e];
+  }
+  if (lane == 0) {
+    s_ml[wave][0] = m;
+    s_ml[wave][1] = l;
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][0]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float a = fast_exp2(s_ml[w][0] - M);
+      L += s_ml[w][1] * a;
+      O += s_acc[w][d] * a;
+    }
+    if (nparts == 1) {
+      T* o = reinterpret_cast<T*>(P.out) + row_id * D;
+      o[d] = to_store(DT{}, L > 0.f ? O / L : 0.f);
+    } else {
+      const size_t pi = row_id * P.max_parts + part;
+      P.ws_o[pi * D + d] = O / L;
+      if (d == 0) {
+        P.ws_ml[2 * pi] = M;
+        P.ws_ml[2 * pi + 1] = L;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of a sequence's partitions: with M = max_p m_p and
+// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.
+template <class DT, int D>
+__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams P) {
+  using T = typename DT::T;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int d = threadIdx.x;
+  int ctx = P.context_lens[s];
+  ctx = min(ctx, min(P.maxB << P.log2_bs, P.max_parts * P.part_tokens));
+  const int nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
+  if (nparts <= 1) return;  // written by the partition kernel
+  const size_t row_id = size_t(s) * P.H + h;
+  const float* ml = P.ws_ml + row_id * P.max_parts * 2;
+  const float* po = P.ws_o + row_id * P.max_parts * D;
+  float M = kNegBig;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+  float L = 0.f, O = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+    L += w;
+    O += w * po[size_t(p) * D + d];
+  }
+  reinterpret_cast<T*>(P.out)[row_id * D + d] = to_store(DT{}, O / L);
+}
+
+// ------------------------------------------------------------------ host side
+constexpr int kUnroll = 8;
+
+struct Plan {
+  int part_tokens;
+  int max_parts;
+  size_t ws_bytes;
+};
+
+static int chunk_tokens(int32_t head_dim, int32_t dtype) {
+  const int vec = 16 / elem_bytes(dtype);
+  return (kWave / (head_dim / vec)) * kUnroll;
+}
+
+// Context-partition size.  Requested sizes must be multiples of 32 and of the
+// block size and span at most 64 blocks.  The automatic choice keeps
+// partitions short (better balance across CUs) unless the launch already has
+// many workgroups.
+static int make_plan(int32_t S, int32_t H, int32_t D, int32_t bs, int32_t max_ctx,
+                     int32_t dtype, int32_t requested, Plan* plan) {
+  int rc = check_shape(D, bs, dtype);
+  if (rc != PA_OK) return rc;
+  if (S < 0 || H <= 0 || max_ctx < 0 || requested < 0) return PA_ERR_INVALID;
+  if (S > 65535 || H > 65535) return PA_ERR_UNSUPPORTED;
+  const int max_tokens = 64 * bs;
+  int pt = requested;
+  if (pt == 0) {
+    const int64_t rows = int64_t(S) * H;
+    pt = 256;
+    // Larger partitions once there are plenty of workgroups anyway.
+    while (pt * 2 <= max_tokens && pt < 1024 &&
+           rows * ((int64_t(max_ctx) + 2 * pt - 1) / (2 * pt)) >= 16384)
+      pt *= 2;
+    if (pt < bs) pt = bs;
+    if (pt > max_tokens) pt = max_tokens;
+  } else {
+    if (pt % 32 != 0 || pt % bs != 0 || pt > max_tokens) return PA_ERR_INVALID;
+  }
+  (void)chunk_tokens;
+  const int parts = max_ctx == 0 ? 1 : (max_ctx + pt - 1) / pt;
+  plan->part_tokens = pt;
+  plan->max_parts = parts;
+  plan->ws_bytes = parts > 1 ? size_t(S) * H * parts * (size_t(D) + 2) * sizeof(float) : 0;
+  return PA_OK;
+}
+
+template <class DT, int D>
+static void launch_partitions(const DecodeParams& p, int S, hipStream_t st) {
+  dim3 grid(p.max_parts, p.H, S);
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
+}
+
+template <class DT, int D>
+static void launch_reduce(const DecodeParams& p, int S, hipStream_t st) {
+  dim3 grid(p.H, S);
+  hipLaunchKernelGGL((decode_reduce_kernel<DT, D>), grid, dim3(D), 0, st, p);
+}
+
+template <bool kPartitions>
+static void dispatch(int32_t dtype, int32_t D, const DecodeParams& p, int S, hipStream_t st) {
+#define PA_LAUNCH(DT_, D_)                       \
+  do {                                           \
+    if (kPartitions)                             \
+      launch_partitions<DT_, D_>(p, S, st);      \
+    else                                         \
+      launch_reduce<DT_, D_>(p, S, st);          \
+  } while (0)
+  if (dtype == PA_F32) {
+    if (D == 64) PA_LAUNCH(F32, 64); else PA_LAUNCH(F32, 128);
+  } else if (dtype == PA_F16) {
+    if (D == 64) PA_LAUNCH(F16, 64); else PA_LAUNCH(F16, 128);
+  } else {
+    if (D == 64) PA_LAUNCH(BF16, 64); else PA_LAUNCH(BF16, 128);
+  }
+#undef PA_LAUNCH
+}
+
+enum { kDoPartitions = 1, kDoReduce = 2 };
+
+static int decode_impl(int what, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t maxB, const int32_t* context_lens,
+                       int32_t S, int32_t H, int32_t D, int32_t bs, int64_t NB, float scale,
+                       int32_t max_ctx, int32_t dtype, void* out, void* workspace,
+                       size_t workspace_bytes, int32_t partition_tokens, void* stream) {
+  Plan plan;
+  int rc = make_plan(S, H, D, bs, max_ctx, dtype, partition_tokens, &plan);
+  if (rc != PA_OK) return rc;
+  if (S == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_INVALID;
+  if (maxB <= 0 || NB <= 0) return PA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return PA_ERR_INVALID;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_INVALID;
+  }
+  DecodeParams p;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.ws_ml = reinterpret_cast<float*>(workspace);
+  p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(workspace) + size_t(S) * H * plan.max_parts * 2
+                         : nullptr;
+  p.H = H;
+  p.maxB = maxB;
+  p.log2_bs = log2_exact(bs);
+  p.part_tokens = plan.part_tokens;
+  p.max_parts = plan.max_parts;
+  p.qk_scale = scale * kLog2e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (what & kDoPartitions) dispatch<true>(dtype, D, p, S, st);
+  if ((what & kDoReduce) && plan.max_parts > 1) dispatch<false>(dtype, D, p, S, st);
+  return launch_status();
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                   int32_t max_context_len, int32_t dtype, int32_t partition_tokens,
+                   int32_t* partition_tokens_out, int32_t* num_partitions_out,
+                   size_t* workspace_bytes_out) {
+  pa::Plan plan;
+  int rc = pa::make_plan(num_seqs, num_heads, head_dim, block_size, max_context_len, dtype,
+                         partition_tokens, &plan);
+  if (rc != PA_OK) return rc;
+  if (partition_tokens_out) *partition_tokens_out = plan.part_tokens;
+  if (num_partitions_out) *num_partitions_out = plan.max_parts;
+  if (workspace_bytes_out) *workspace_bytes_out = plan.ws_bytes;
+  return PA_OK;
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_context_len, int32_t dtype,
+                                int32_t partition_tokens) {
+  pa::Plan plan;
+  int rc = pa::make_plan(num_seqs, num_heads, head_dim, block_size, max_context_len, dtype,
+                         partition_tokens, &plan);
+  return rc == PA_OK ? plan.ws_bytes : size_t(-1);
+}
+
+#define PA_DECODE_ARGS                                                                      \
+  const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,    \
+      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,            \
+      int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,          \
+      float scale, int32_t max_context_len, int32_t dtype, void *out, void *workspace,      \
+      size_t workspace_bytes, int32_t partition_tokens, void *stream
+#define PA_DECODE_PASS                                                                      \
+  q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, \
+      head_dim, block_size, num_blocks, scale, max_context_len, dtype, out, workspace,      \
+      workspace_bytes, partition_tokens, stream
+
+int pa_decode(PA_DECODE_ARGS) {
+  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce, PA_DECODE_PASS);
+}
+int pa_decode_partitions(PA_DECODE_ARGS) {
+  return pa::decode_impl(pa::kDoPartitions, PA_DECODE_PASS);
+}
+int pa_decode_reduce(PA_DECODE_ARGS) { return pa::decode_impl(pa::kDoReduce, PA_DECODE_PASS); }
+
+}  // extern "C"

@@ -36,8 +36,8 @@ except Exception:  # pragma: no cover
     _torch = None
 
 __all__ = [
-    "DTYPES", "Workload", "make_workload", "to_storage", "CONFIG_NAMES",
-    "SWEEP_BLOCK_SIZES",
+    "DTYPES", "Workload", "make_workload", "make_custom", "to_storage", "CONFIG_NAMES",
+    "SWEEP_BLOCK_SIZES", "cache_draws", "to_torch",
 ]
 
 # storage dtype name -> (numpy storage dtype, bytes per element)
@@ -86,18 +86,59 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def to_torch(arr: np.ndarray, dtype: str, device="cuda"):
+    """A storage-typed array as a torch tensor on ``device`` (bf16 from its bits)."""
+    import torch
+    a = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.to(device)
+
+
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    if not _VALUES[0]:
+        return np.zeros(shape, dtype=DTYPES[dtype][0])
     return to_storage(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
+_VALUES = [True]
 
 
 def _draw_many(cfg: int, stream: int, jobs, dtype: str):
     """Draw one array per (sub, shape) job, each from its own seed stream
-    (cfg, stream, sub); threads only change the speed, never the values."""
+    (cfg, stream, sub); threads only change the speed, never the values.
+    Draws are cached per (cfg, stream, sub, shape, dtype) for the life of the
+    process when ``cache_draws(True)`` is on (the block-size sweep reuses one
+    set of logical K/V)."""
+    if not _VALUES[0]:
+        return [None] * len(jobs)
+
     def one(job):
         sub, shape = job
         return _normal(_rng(cfg, stream, sub), shape, dtype)
+    def cached(job):
+        key = (cfg, stream, job[0], tuple(job[1]), dtype)
+        if _CACHE_ON[0] and key in _CACHE:
+            return _CACHE[key]
+        arr = one(job)
+        if _CACHE_ON[0]:
+            _CACHE[key] = arr
+        return arr
     with ThreadPoolExecutor(max_workers=8) as ex:
-        return list(ex.map(one, jobs))
+        return list(ex.map(cached, jobs))
+
+
+_CACHE: dict = {}
+_CACHE_ON = [False]
+
+
+def cache_draws(on: bool):
+    """Keep drawn K/V arrays for reuse (on) or drop them (off)."""
+    _CACHE_ON[0] = bool(on)
+    if not on:
+        _CACHE.clear()
 
 
 @dataclass
@@ -251,12 +292,34 @@ def config5_ctx() -> np.ndarray:
 
 
 def make_workload(cfg: int, bs: int | None = None, cow: bool = False,
-                  S: int | None = None) -> Workload:
+                  S: int | None = None, values: bool = True) -> Workload:
     """Build workload ``cfg`` (1..5).
 
     ``bs`` selects the block size of the config-5 sweep; ``cow`` selects the
     copy-on-write variant of config 4; ``S`` (config 5 only) keeps the first S
-    sequences, for smaller CPU-side cases."""
+    sequences, for smaller CPU-side cases; ``values=False`` skips the K/V
+    draws (only the shapes and the op script are built)."""
+    _VALUES[0] = bool(values)
+    try:
+        return _make(cfg, bs, cow, S)
+    finally:
+        _VALUES[0] = True
+
+
+def make_custom(seed: int, H: int, D: int, dtype: str, bs: int, ctx, NB: int | None = None,
+                scale: float | None = None, part_tokens: int = 0) -> Workload:
+    """A small independent-sequence workload with the given shapes (kernel-instance
+    coverage): prefill of ctx-1 tokens, one step.  ``seed`` >= 100 keeps its
+    streams apart from the five named configs."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    demand = int(sum(max(1, math.ceil(int(c) / bs)) for c in ctx))
+    NB = NB or demand + 8
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    return _simple(seed, f"custom-{dtype}-D{D}-bs{bs}", H, D, dtype, bs, NB, ctx, sc,
+                   part_tokens=part_tokens)
+
+
+def _make(cfg, bs, cow, S):
     if cfg == 1:
         return _simple(1, CONFIG_NAMES[1], 4, 64, "f32", 16, 64, [1, 17, 33, 100],
                        1.0 / 8.0)

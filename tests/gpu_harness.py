@@ -1,0 +1,108 @@
+"""Test helpers: run a workload's op script through the library on the GPU and
+compare with the oracle.  Test infrastructure only."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+import oracle
+import synth
+
+TOL = 2e-3   # max |gpu - oracle| on attention outputs (fp32 accumulation, one final rounding)
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(name):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+def to_dev(arr, dtype_name, device="cuda"):
+    return synth.to_torch(arr, dtype_name, device)
+
+
+def bits(t):
+    """Raw storage bits of a device/host tensor as a numpy array."""
+    import torch
+    view = {2: torch.int16, 4: torch.int32}[t.element_size()]
+    return t.detach().contiguous().view(view).cpu().numpy()
+
+
+def oracle_bits(a, dtype_name):
+    if dtype_name == "bf16":
+        return np.ascontiguousarray(a).view(np.int16)
+    if dtype_name == "f16":
+        return np.ascontiguousarray(a).view(np.int16)
+    return np.ascontiguousarray(a).view(np.int32)
+
+
+def run_gpu(wl, partition_tokens=0, fill_nan=True):
+    """Execute wl.ops with PagedKVEngine; returns dict with the engine and the step output."""
+    import torch
+    from paged_kv_cache_write_amd.engine import PagedKVEngine
+    tdt = torch_dtype(wl.dtype)
+    eng = PagedKVEngine(wl.NB, wl.H, wl.D, wl.bs, tdt, wl.max_blocks_per_seq, wl.S,
+                        free_order=wl.free_order, pad_block=wl.poison_block,
+                        fill=float("nan") if fill_nan else 0.0)
+    out = None
+    for op in wl.ops:
+        if op[0] == "add":
+            _, seq, n = op
+            k, v = wl.kv(seq, 0, n)
+            eng.add_sequence(seq, to_dev(k, wl.dtype), to_dev(v, wl.dtype))
+        elif op[0] == "fork":
+            eng.fork(op[1], op[2])
+        elif op[0] == "extend":
+            _, seq, n = op
+            t = eng.bm.seq_len(seq)
+            k, v = wl.kv(seq, t, t + n)
+            eng.extend([seq] * n, to_dev(k, wl.dtype), to_dev(v, wl.dtype))
+        else:
+            seqs = np.array(op[1], dtype=np.int64)
+            ks, vs = [], []
+            for s in seqs:
+                t = eng.bm.seq_len(int(s))
+                k, v = wl.kv(int(s), t, t + 1)
+                ks.append(k[0])
+                vs.append(v[0])
+            q = to_dev(wl.q, wl.dtype)
+            out = eng.step(seqs, q, to_dev(np.stack(ks), wl.dtype), to_dev(np.stack(vs), wl.dtype),
+                           wl.scale, partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return dict(engine=eng, out=out)
+
+
+def compare_outputs(gpu_out, ref, seqs=None, tol=TOL, what=""):
+    """Element-wise check of GPU out (torch) against the oracle's fp64 out."""
+    g = gpu_out.float().cpu().numpy().astype(np.float64)
+    rows = list(range(ref.shape[0])) if seqs is None else list(seqs)
+    g, r = g[rows], ref[rows]
+    assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
+    err = np.abs(g - r)
+    worst = float(err.max()) if err.size else 0.0
+    rel = float((err / np.maximum(np.abs(r), 1e-3)).max()) if err.size else 0.0
+    log(f"{what}: max abs err {worst:.3e}, mean {float(err.mean()) if err.size else 0:.3e}, "
+        f"max rel {rel:.3e} over {len(rows)} seqs")
+    assert worst <= tol, f"{what}: max abs err {worst} > {tol}"
+    return worst
+
+
+def sample_seqs(ctx, k, seed=0):
+    """Up to k sequences: the longest, the shortest and a seeded random rest."""
+    S = len(ctx)
+    if S <= k:
+        return list(range(S))
+    order = np.argsort(ctx)
+    pick = {int(order[0]), int(order[-1])}
+    rng = np.random.default_rng(seed)
+    for s in rng.permutation(S):
+        if len(pick) >= k:
+            break
+        pick.add(int(s))
+    return sorted(pick)

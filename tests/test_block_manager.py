@@ -1,0 +1,203 @@
+"""The C++ block manager (libpa.so, host code) against the oracle's BlockPoolModel.
+
+No GPU: the block manager never touches device memory.  Tables, slots,
+copy-on-write pairs, refcounts and the free list must match bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def _bm(*a, **k):
+    import paged_kv_cache_write_amd as pk
+    return pk.BlockManager(*a, **k)
+
+
+def _same_state(bm, model):
+    assert bm.num_free == len(model.free)
+    assert bm.free_list() == list(model.free)
+    assert bm.refcounts() == model.ref
+    assert bm.num_seqs == len(model.tables)
+    for s, tab in model.tables.items():
+        assert bm.block_table(s) == tab
+        assert bm.seq_len(s) == model.lens[s]
+
+
+def test_cow_example_comfyai_643(golden):
+    g = golden("cow_example.json")
+    bm = _bm(g["num_blocks"], g["block_size"])
+    ids = {"A1": 0, "A2": 1, "B": 2}
+    bm.add_seq(0, 6)
+    bm.add_seq(2, 3)
+    bm.fork(0, 1)
+    a = g["after_fork"]
+    assert bm.block_table(0) == a["A1"] and bm.block_table(1) == a["A2"]
+    slot, cow = bm.append_slot(ids["A1"])
+    a = g["after_A1_append"]
+    assert (slot, list(cow)) == (a["A1_slot"], a["cow"])
+    assert bm.block_table(0) == a["A1"] and bm.block_table(1) == a["A2"]
+    assert {str(b): r for b, r in enumerate(bm.refcounts()) if r} == a["refcount"]
+    slot, cow = bm.append_slot(ids["A2"])
+    assert (slot, cow) == (g["after_A2_append"]["A2_slot"], None)
+
+
+def test_alloc_timeline_slide11(golden):
+    g = golden("alloc_timeline.json")
+    bm = _bm(len(g["free_order"]), g["block_size"], g["free_order"])
+    bm.add_seq(0, g["prompt_tokens"])
+    assert bm.block_table(0) == g["after_prefill"]["table"]
+    for key in ("step1", "step2"):
+        slot, cow = bm.append_slot(0)
+        assert cow is None and slot == g[key]["slot"] and bm.block_table(0) == g[key]["table"]
+        assert bm.num_free == g[key]["num_free"]
+
+
+def test_random_ops_match_model():
+    import paged_kv_cache_write_amd as pk
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        bs = int(rng.choice([2, 4, 8, 16]))
+        NB = int(rng.integers(4, 80))
+        order = rng.permutation(NB)[: int(rng.integers(1, NB + 1))]
+        bm, model = _bm(NB, bs, order), oracle.BlockPoolModel(NB, bs, order)
+        live, nxt = [], 100
+        for _ in range(250):
+            op = int(rng.integers(0, 5))
+            if op == 0 or not live:
+                n = int(rng.integers(0, 3 * bs))
+                try:
+                    model.add_seq(nxt, n)
+                    ok = True
+                except oracle.BlockPoolModel.NoBlocks:
+                    ok = False
+                if ok:
+                    bm.add_seq(nxt, n)
+                    live.append(nxt)
+                else:
+                    with pytest.raises(pk.PAError) as e:
+                        bm.add_seq(nxt, n)
+                    assert e.value.status == -4
+                nxt += 1
+            elif op == 1:
+                p = live[int(rng.integers(len(live)))]
+                model.fork(p, nxt)
+                bm.fork(p, nxt)
+                live.append(nxt)
+                nxt += 1
+            elif op == 2:
+                s = live[int(rng.integers(len(live)))]
+                try:
+                    want = model.append_slot(s)
+                except oracle.BlockPoolModel.NoBlocks:
+                    want = None
+                if want is None:
+                    with pytest.raises(pk.PAError):
+                        bm.append_slot(s)
+                else:
+                    got = bm.append_slot(s)
+                    assert got == want
+            elif op == 3:
+                batch = [live[int(i)] for i in rng.integers(0, len(live), size=int(rng.integers(1, 6)))]
+                snapshot_ok = True
+                want_slots, want_cows = [], []
+                try:
+                    for s in batch:
+                        slot, cow = model.append_slot(s)
+                        want_slots.append(slot)
+                        if cow:
+                            want_cows.append(cow)
+                except oracle.BlockPoolModel.NoBlocks:
+                    snapshot_ok = False
+                if snapshot_ok:
+                    slots, cows = bm.append_slots(batch)
+                    assert slots.tolist() == want_slots
+                    assert [tuple(c) for c in cows.tolist()] == want_cows
+                else:
+                    with pytest.raises(pk.PAError):
+                        bm.append_slots(batch)
+                    # the failed batch did its first appends; the model did too
+            else:
+                s = live.pop(int(rng.integers(len(live))))
+                model.free_seq(s)
+                bm.free_seq(s)
+            _same_state(bm, model)
+
+
+def test_workload_scripts_match_model():
+    """Execute each config's op script on both managers (no K/V data)."""
+    for cfg, kw in ((1, {}), (2, {}), (4, {}), (4, {"cow": True}), (5, {"bs": 8, "S": 40})):
+        wl = synth.make_workload(cfg, values=False, **kw)
+        bm, model = _bm(wl.NB, wl.bs, wl.free_order), oracle.BlockPoolModel(wl.NB, wl.bs, wl.free_order)
+        for op in wl.ops:
+            if op[0] == "add":
+                model.add_seq(op[1], op[2])
+                bm.add_seq(op[1], op[2])
+                assert bm.slots(op[1], 0, op[2]).tolist() == model.slots(op[1], 0, op[2])
+            elif op[0] == "fork":
+                model.fork(op[1], op[2])
+                bm.fork(op[1], op[2])
+            elif op[0] == "extend":
+                want = [model.append_slot(op[1]) for _ in range(op[2])]
+                slots, cows = bm.append_slots([op[1]] * op[2])
+                assert slots.tolist() == [w[0] for w in want]
+                assert [tuple(c) for c in cows.tolist()] == [w[1] for w in want if w[1]]
+            else:
+                seqs = np.array(op[1], dtype=np.int64)
+                want = [model.append_slot(int(s)) for s in seqs]
+                S, W = seqs.size, wl.max_blocks_per_seq
+                slots = np.empty(S, np.int64)
+                cows = np.empty(2 * S, np.int32)
+                tables = np.empty((S, W), np.int32)
+                ctx = np.empty(S, np.int32)
+                ncow = bm.step_into(seqs, slots, cows, tables, wl.poison_block, ctx)
+                assert slots.tolist() == [w[0] for w in want]
+                assert [tuple(c) for c in cows[:2 * ncow].reshape(-1, 2).tolist()] == \
+                    [w[1] for w in want if w[1]]
+                assert np.array_equal(tables, model.table_array(list(seqs), W, wl.poison_block))
+                assert ctx.tolist() == [model.lens[int(s)] for s in seqs]
+                assert ctx.tolist() == wl.ctx.tolist()
+        _same_state(bm, model)
+
+
+def test_cow_subcase_counts():
+    """Config-4 CoW variant: 7 of 8 siblings copy the shared last block, the last writes in place."""
+    wl = synth.make_workload(4, cow=True, values=False)
+    model = oracle.BlockPoolModel(wl.NB, wl.bs, wl.free_order)
+    cows = 0
+    for op in wl.ops:
+        if op[0] == "add":
+            model.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            model.fork(op[1], op[2])
+        elif op[0] == "extend":
+            cows += sum(model.append_slot(op[1])[1] is not None for _ in range(op[2]))
+        else:
+            cows += sum(model.append_slot(int(s))[1] is not None for s in op[1])
+    assert cows == 7 * 8
+
+
+def test_errors():
+    import paged_kv_cache_write_amd as pk
+    bm = _bm(4, 4)
+    bm.add_seq(1, 4)
+    with pytest.raises(pk.PAError) as e:
+        bm.add_seq(1, 1)
+    assert e.value.status == -7
+    with pytest.raises(pk.PAError) as e:
+        bm.fork(9, 10)
+    assert e.value.status == -6
+    with pytest.raises(pk.PAError) as e:
+        bm.add_seq(2, 17)
+    assert e.value.status == -4
+    assert bm.num_free == 3              # failed add changed nothing
+    with pytest.raises(pk.PAError) as e:
+        pk.BlockManager(4, 4, [0, 0])
+    assert e.value.status == -1
+    tables, ctx = bm.block_tables([1], 1, -1)
+    assert tables.tolist() == [[bm.block_table(1)[0]]] and ctx.tolist() == [4]
+    bm.append_slot(1)
+    with pytest.raises(pk.PAError) as e:
+        bm.block_tables([1], 1, -1)
+    assert e.value.status == -8

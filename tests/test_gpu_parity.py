@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Pools, tables, slot mappings and copy-on-write pairs must be bit-exact;
+attention outputs within 2e-3 absolute of the float64 oracle, finite, with
+never-written pool slots and unused table entries poisoned with NaN.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_harness import TOL, bits, compare_outputs, log, oracle_bits, run_gpu, sample_seqs, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _same_storage(gpu_t, ora, dtype, what):
+    g = bits(gpu_t)
+    o = oracle_bits(ora, dtype)
+    assert g.shape == o.shape, what
+    eq = g == o
+    if not eq.all():
+        fl = {"f32": np.float32, "f16": np.float16, "bf16": None}[dtype]
+        if fl is None:
+            gn = ((g.view(np.uint16) & 0x7F80) == 0x7F80) & ((g.view(np.uint16) & 0x7F) != 0)
+            on = ((o.view(np.uint16) & 0x7F80) == 0x7F80) & ((o.view(np.uint16) & 0x7F) != 0)
+        else:
+            gn, on = np.isnan(g.view(fl)), np.isnan(o.view(fl))
+        bad = ~eq & ~(gn & on)
+        assert not bad.any(), f"{what}: {int(bad.sum())} storage elements differ"
+
+
+def _check_workload(wl, seqs=None, partition_tokens=0, tol=TOL, compare_pools=True):
+    log(f"case {wl.name}: S={wl.S} H={wl.H} D={wl.D} {wl.dtype} bs={wl.bs} NB={wl.NB} "
+        f"sum(ctx)={int(wl.ctx.sum())} partition_tokens={partition_tokens}")
+    g = run_gpu(wl, partition_tokens=partition_tokens)
+    log("  gpu done; running oracle")
+    r = oracle.run_workload(wl, decode_seqs=seqs)
+    eng = g["engine"]
+    last = eng.last_step
+    assert np.array_equal(last["ctx"], r["ctx"]), "context lengths"
+    assert np.array_equal(last["slots"], r["step_slots"]), "step slot mapping"
+    assert np.array_equal(last["cows"].reshape(-1, 2), r["step_cows"]), "step CoW pairs"
+    tables, _ = eng.bm.block_tables(np.arange(wl.S), wl.max_blocks_per_seq, wl.poison_block)
+    assert np.array_equal(tables, r["tables"]), "block tables"
+    assert eng.bm.refcounts() == r["refcounts"].tolist(), "refcounts"
+    if compare_pools:
+        _same_storage(eng.k_cache, r["k_cache"], wl.dtype, "k_cache")
+        _same_storage(eng.v_cache, r["v_cache"], wl.dtype, "v_cache")
+        log("  pools bit-exact")
+    err = compare_outputs(g["out"], r["out"], seqs=seqs, tol=tol, what=wl.name)
+    return g, r, err
+
+
+# ------------------------------------------------------------ the 5 configs
+def test_config1_tiny_fp32():
+    wl = synth.make_workload(1)
+    g, r, _ = _check_workload(wl)
+    # ctx = 1: softmax weight exactly 1, so out == V of the only token, bit for bit
+    s0 = int(np.argmin(wl.ctx))
+    assert wl.ctx[s0] == 1
+    _, v = wl.kv(s0, 0, 1)
+    assert np.array_equal(bits(g["out"][s0]), oracle_bits(v[0], "f32"))
+
+
+def test_config2_llama13b_layer():
+    _check_workload(synth.make_workload(2))
+
+
+def test_config3_long_context_split():
+    wl = synth.make_workload(3)
+    _check_workload(wl, partition_tokens=wl.partition_tokens)
+
+
+@pytest.mark.parametrize("cow", [False, True])
+def test_config4_shared_prefix(cow):
+    wl = synth.make_workload(4, cow=cow)
+    g, r, _ = _check_workload(wl)
+    if cow:
+        assert r["all_cows"].shape[0] == 7 * 8
+
+
+@pytest.mark.parametrize("bs", synth.SWEEP_BLOCK_SIZES)
+def test_config5_block_size_sweep(bs):
+    synth.cache_draws(True)
+    wl = synth.make_workload(5, bs=bs)
+    seqs = sample_seqs(wl.ctx, 24, seed=bs)
+    _check_workload(wl, seqs=seqs)
+
+
+# ------------------------------------------------- every kernel instance
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64, 128])
+def test_kernel_instances(dtype, D, bs):
+    synth.cache_draws(False)
+    # ragged: single token, block boundaries +-1, several partitions with a tail
+    ctx = [1, bs - 1, bs, bs + 1, 3 * bs + 5, 1000, 2 * 64 * bs + 17]
+    seed = 100 + {"f32": 0, "f16": 1, "bf16": 2}[dtype] * 100 + D + bs
+    wl = synth.make_custom(seed, 3, D, dtype, bs, ctx)
+    g, r, _ = _check_workload(wl, partition_tokens=0)
+    # forced short partitions: the split path on every sequence longer than one
+    pt = max(32, bs)
+    g2 = run_gpu(wl, partition_tokens=pt)
+    compare_outputs(g2["out"], r["out"], what=f"{wl.name} split pt={pt}")
+
+
+# ---------------------------------------------------------- exact probes
+def _scatter_direct(ks, vs, H, D, dtype, bs, NB, free_order, poison, fill=float("nan")):
+    """Build a pool with the library from contiguous per-sequence K/V (host arrays)."""
+    from paged_kv_cache_write_amd.engine import PagedKVEngine
+    maxB = max(-(-k.shape[0] // bs) for k in ks)
+    eng = PagedKVEngine(NB, H, D, bs, {"f16": torch.float16, "bf16": torch.bfloat16,
+                                       "f32": torch.float32}[dtype], maxB, len(ks),
+                        free_order=free_order, pad_block=poison, fill=fill)
+    for s, (k, v) in enumerate(zip(ks, vs)):
+        eng.add_sequence(s, to_dev(k, dtype), to_dev(v, dtype))
+    tables, ctx = eng.bm.block_tables(np.arange(len(ks)), maxB, poison)
+    return eng, torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(), int(ctx.max())
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_one_hot_index_probe(dtype):
+    """q = e0 and one key 200/scale make the softmax a one-hot at t*; V encodes
+    position t as (t // 64, t % 64), exact in fp16/bf16: out decodes t* exactly."""
+    import paged_kv_cache_write_amd as pk
+    rng = np.random.default_rng(7)
+    S, H, D, bs = 12, 8, 128, 16
+    scale = 1 / math.sqrt(D)
+    ctx = rng.integers(1, 3000, size=S)
+    ctx[0], ctx[1] = 1, 2048
+    ks, vs, tstar = [], [], rng.integers(0, 1 << 30, size=(S, H)) % ctx[:, None]
+    for s in range(S):
+        L = int(ctx[s])
+        k = np.zeros((L, H, D), np.float32)
+        v = np.zeros((L, H, D), np.float32)
+        t = np.arange(L)
+        v[:, :, 0] = (t // 64)[:, None]
+        v[:, :, 1] = (t % 64)[:, None]
+        for h in range(H):
+            k[tstar[s, h], h, 0] = 200 / scale
+        ks.append(synth.to_storage(k, dtype))
+        vs.append(synth.to_storage(v, dtype))
+    NB = int(sum(-(-c // bs) for c in ctx)) + 5
+    order = rng.permutation(NB).astype(np.int32)
+    eng, tables, cl, mx = _scatter_direct(ks, vs, H, D, dtype, bs, NB, order[:-1], int(order[-1]))
+    q = np.zeros((S, H, D), np.float32)
+    q[:, :, 0] = 1
+    qd = to_dev(synth.to_storage(q, dtype), dtype)
+    for pt in (0, 32, 256):
+        out = pk.decode(qd, eng.k_cache, eng.v_cache, tables, cl, scale, mx, partition_tokens=pt)
+        o = out.float().cpu().numpy()
+        dec = o[:, :, 0] * 64 + o[:, :, 1]
+        assert np.array_equal(dec, tstar.astype(np.float32)), f"pt={pt}"
+        assert np.all(o[:, :, 2:] == 0)
+    log(f"one-hot probe {dtype}: {S * H} positions decoded exactly")
+
+
+def test_permutation_invariance_bit_exact():
+    """Same logical K/V at a different physical placement: identical output bits."""
+    import paged_kv_cache_write_amd as pk
+    wl = synth.make_custom(400, 4, 128, "f16", 16, [700, 33, 1500, 2048, 1])
+    ks = [wl.kv(s, 0, int(wl.ctx[s]))[0] for s in range(wl.S)]
+    vs = [wl.kv(s, 0, int(wl.ctx[s]))[1] for s in range(wl.S)]
+    outs = []
+    for seed in (1, 2):
+        order = np.random.default_rng(seed).permutation(wl.NB).astype(np.int32)
+        eng, tables, cl, mx = _scatter_direct(ks, vs, wl.H, wl.D, "f16", 16, wl.NB, order[:-1],
+                                              int(order[-1]))
+        q = to_dev(wl.q, "f16")
+        outs.append(bits(pk.decode(q, eng.k_cache, eng.v_cache, tables, cl, wl.scale, mx)))
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_split_matches_single_pass():
+    import paged_kv_cache_write_amd as pk
+    wl = synth.make_custom(401, 8, 128, "f16", 16, [1024, 777, 1, 1000, 513, 64])
+    r = oracle.run_workload(wl)
+    g = run_gpu(wl, partition_tokens=1024)          # one partition per sequence
+    e1 = compare_outputs(g["out"], r["out"], what="single pass")
+    for pt in (32, 64, 256, 512):
+        g2 = run_gpu(wl, partition_tokens=pt)
+        e2 = compare_outputs(g2["out"], r["out"], what=f"split pt={pt}")
+        diff = (g2["out"].float() - g["out"].float()).abs().max().item()
+        assert diff <= 2 * TOL
+    assert pk.decode_plan(wl.S, wl.H, wl.D, 16, 1024, 1, 1024)[1] == 1
+    del e1, e2
+
+
+def test_context_zero_and_negative_slots():
+    import paged_kv_cache_write_amd as pk
+    H, D, bs, NB = 2, 64, 16, 8
+    kc = torch.full((NB, H, bs, D), float("nan"), dtype=torch.float16, device="cuda")
+    vc = kc.clone()
+    slot_list = [3, -1, 0, 17, -5, 1, 40, 2]
+    k = torch.randn(len(slot_list), H, D, device="cuda").half()
+    v = torch.randn(len(slot_list), H, D, device="cuda").half()
+    slots = torch.tensor(slot_list, dtype=torch.int64, device="cuda")
+    before = bits(kc)
+    pk.cache_write(k, v, slots, kc, vc)
+    after = bits(kc)
+    written = np.zeros((NB, bs), bool)
+    for n, s in enumerate(slot_list):
+        if s >= 0:
+            written[s // bs, s % bs] = True
+            assert np.array_equal(after[s // bs, :, s % bs, :], bits(k[n]))
+            assert np.array_equal(bits(vc)[s // bs, :, s % bs, :], bits(v[n]))
+    assert np.array_equal(after[~written], before[~written].reshape(after[~written].shape))
+    # ctx = 0 rows are zero; their tables point at a NaN block
+    q = torch.randn(3, H, D, device="cuda").half()
+    tables = torch.tensor([[7, 7], [0, 7], [7, 7]], dtype=torch.int32, device="cuda")
+    cl = torch.tensor([0, 4, 0], dtype=torch.int32, device="cuda")
+    out = pk.decode(q, kc, vc, tables, cl, 0.125, 4)
+    o = out.float().cpu().numpy()
+    assert np.all(o[0] == 0) and np.all(o[2] == 0) and np.isfinite(o[1]).all()
+    # empty launches are no-ops
+    pk.cache_write(k[:0], v[:0], slots[:0], kc, vc)
+    pk.copy_blocks(kc, vc, torch.zeros((0, 2), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_copy_blocks_direct():
+    import paged_kv_cache_write_amd as pk
+    for dtype, H, D, bs in (("bf16", 40, 128, 16), ("f32", 3, 64, 128)):
+        NB = 64
+        rng = np.random.default_rng(3)
+        k = synth.to_storage(rng.standard_normal((NB, H, bs, D), dtype=np.float32), dtype)
+        v = synth.to_storage(rng.standard_normal((NB, H, bs, D), dtype=np.float32), dtype)
+        perm = rng.permutation(NB)
+        pairs = np.stack([perm[:20], perm[20:40]], axis=1).astype(np.int32)
+        kd, vd = to_dev(k, dtype), to_dev(v, dtype)
+        pk.copy_blocks(kd, vd, torch.from_numpy(pairs).cuda())
+        oracle.oracle_copy_blocks(k, v, pairs)
+        _same_storage(kd, k, dtype, "k after copy")
+        _same_storage(vd, v, dtype, "v after copy")

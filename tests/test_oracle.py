@@ -67,7 +67,7 @@ def test_kv_cache_worked_example(golden):
 
 
 def test_workload_shape_matches_13b_layer():
-    wl = synth.make_workload(2)
+    wl = synth.make_workload(2, values=False)
     per_layer = wl.H * wl.D * 2 * wl.elem_bytes
     assert per_layer * 40 == 819200
 
