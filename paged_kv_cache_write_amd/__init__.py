@@ -201,7 +201,7 @@ def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale
     dt = _dt(q)
     ws_need = decode_workspace_size(S, H, D, bs, int(max_context_len), dt, partition_tokens)
     if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = getattr(lib(), fn_name)(

@@ -9,16 +9,18 @@
 // block_tables[s, t / bs] at offset t % bs.
 //
 // How (MI355X design, not taken from the pages):
-//  * The work of one (sequence, head) is split into context partitions of
-//    part_tokens tokens; one 256-thread workgroup (4 waves) handles one
-//    (partition, head, sequence).  Partitions give the 256 CUs enough
-//    workgroups when there are few sequences or long contexts, and even out
-//    the work when context lengths differ.
+//  * The context of each (sequence, head) is cut into partitions of
+//    part_tokens tokens.  One wave (64 lanes) owns one (sequence, head,
+//    partition) from start to end; a workgroup packs kWaves waves for
+//    consecutive heads of the same (sequence, partition), which read the
+//    same table entries.  Partitions give the 256 CUs enough independent
+//    waves when there are few sequences or long contexts, and even out the
+//    work when context lengths differ.
 //  * A (block, head) tile is bs * D contiguous elements.  A lane owns a
 //    16-byte slice of one token row, so one wave-wide load instruction reads
 //    64 x 16 B = 1 KiB of consecutive bytes of one tile: fully coalesced.
 //    Each lane consumes exactly the bytes it loaded, so K/V go from HBM
-//    straight to registers; there is no LDS staging in the streaming loop.
+//    straight to registers; there is no LDS staging and no barrier.
 //  * A wave works on chunks of U load instructions for K and U for V issued
 //    back to back, so each lane has 2U 16-byte loads in flight.
 //  * q.k partial dots use v_dot2_f32_{f16,bf16} (exact products, float32
@@ -27,19 +29,28 @@
 //    scale*log2(e) folded into the logit; P.V accumulates in float32
 //    (v_fma_mix_f32 for fp16).
 //  * The partition's table entries are loaded once per wave into one VGPR
-//    (lane j = j-th block of the partition) and read with v_readlane, so a
-//    block's address is wave-uniform scalar arithmetic.
-//  * Waves merge (max, sum, accumulator) across token rows with shuffles,
-//    then across waves through LDS.  A sequence with one partition stores its
-//    output row directly; otherwise the partial (max, sum, normalised output)
-//    goes to the workspace and a second kernel merges partitions with the
-//    log-sum-exp rule.
+//    (lane j = j-th block of the partition), in parallel with the context
+//    length, and read with v_readlane, so a block's address is wave-uniform
+//    scalar arithmetic.
+//  * A wave merges (max, sum, accumulator) across its token rows with
+//    shuffles.  A sequence with one partition stores its output row
+//    directly.  Otherwise the partial (max, sum, normalised output) goes to
+//    the workspace and the partitions are merged with the log-sum-exp rule:
+//    by the last wave to finish that (sequence, head) (pa_decode, one launch,
+//    an agent-scope counter per row), or by a second kernel
+//    (pa_decode_partitions + pa_decode_reduce).
 #include "launch_common.hpp"
 #include "pa_device.hpp"
 
 namespace pa {
 
-constexpr int kWaves = 4;
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_UNROLL
+#define PA_DECODE_UNROLL 8
+#endif
+constexpr int kWaves = PA_DECODE_WAVES;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so max - max never is NaN
@@ -53,6 +64,7 @@ struct DecodeParams {
   void* out;
   float* ws_ml;  // [S, H, max_parts, 2]: running max (log2 units), sum
   float* ws_o;   // [S, H, max_parts, D]: partition output normalised by its sum
+  int* counters; // [S, H] partitions finished; NULL = leave the merge to the reduce kernel
   int H;
   int maxB;
   int log2_bs;
@@ -150,70 +162,66 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& cx, int t0, u32x4 qv,
   m = mn;
 }
 
+// One wave owns one (sequence, head, partition) from start to end; a
+// workgroup is kWaves independent waves for kWaves consecutive heads of the
+// same (sequence, partition), which read the same table entries.  No LDS and
+// no barrier: a wave merges its token rows with shuffles and stores its row.
 template <class DT, int D, int U>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams P) {
+__global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
   using T = typename DT::T;
   using Sh = Shape<DT, D, U>;
   constexpr int kVec = DT::kVec;
   constexpr size_t kRowBytes = size_t(D) * sizeof(T);
 
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
-  const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_uniform(threadIdx.x / kWave);
+  const int h = blockIdx.x * kWaves + wave;
+  const int part = blockIdx.y;
+  const int s = blockIdx.z;
   const int H = P.H;
+  if (h >= H) return;
+  const int lane = threadIdx.x & (kWave - 1);
   const int log2_bs = P.log2_bs;
   const size_t row_id = size_t(s) * H + h;
 
+  const int row = lane / Sh::kLPT;
+  const int col = lane % Sh::kLPT;
+  const int p0 = part * P.part_tokens;
+  const int blk0 = p0 >> log2_bs;
+  // The table entries of the whole partition window are read together with
+  // the context length (entries past the context are loaded as integers but
+  // never used as addresses), so the K/V loads wait for one round trip only.
+  int tbl = 0;
+  if (lane < (P.part_tokens >> log2_bs) && blk0 + lane < P.maxB)
+    tbl = P.block_tables[size_t(s) * P.maxB + blk0 + lane];
   int ctx = P.context_lens[s];
-  // never read past the table row or past the launched partitions
   ctx = min(ctx, min(P.maxB << log2_bs, P.max_parts * P.part_tokens));
   const int nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
   if (part >= nparts) {
-    if (part == 0) {  // empty context: zero output row
-      T* o = reinterpret_cast<T*>(P.out) + row_id * D;
-      for (int d = threadIdx.x; d < D; d += kThreads) o[d] = to_store(DT{}, 0.f);
+    if (part == 0 && row == 0) {  // empty context: zero output row
+      T* o = reinterpret_cast<T*>(P.out) + row_id * D + col * kVec;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, 0.f);
     }
     return;
   }
-  const int p0 = part * P.part_tokens;
   const int ntok = min(P.part_tokens, ctx - p0);
-
-  const int row = lane / Sh::kLPT;
-  const int col = lane % Sh::kLPT;
-
   const u32x4 qv = load16(reinterpret_cast<const char*>(P.q) + row_id * kRowBytes + col * 16);
 
-  // Table entries of this partition, one per lane (partition start is a
-  // multiple of the block size; a partition spans at most 64 blocks).
-  const int blk0 = p0 >> log2_bs;
-  const int nblk = ((ntok - 1) >> log2_bs) + 1;
-  int tbl = 0;
-  if (lane < nblk) tbl = P.block_tables[size_t(s) * P.maxB + blk0 + lane];
-
-  const char* kc = reinterpret_cast<const char*>(P.k_cache);
-  const char* vc = reinterpret_cast<const char*>(P.v_cache);
   const size_t tile_bytes = kRowBytes << log2_bs;
-  const int bs_mask = (1 << log2_bs) - 1;
   const uint32_t lane_off = uint32_t(row) * uint32_t(kRowBytes) + uint32_t(col) * 16u;
+  ChunkCtx cx{reinterpret_cast<const char*>(P.k_cache), reinterpret_cast<const char*>(P.v_cache),
+              tile_bytes, size_t(h) * tile_bytes, size_t(H) * tile_bytes, lane_off, tbl,
+              log2_bs, (1 << log2_bs) - 1, row, ntok, (ntok - 1) & ~(Sh::kTPI - 1), P.qk_scale};
 
   float m = kNegBig, l = 0.f;
   float acc[kVec];
 #pragma unroll
   for (int e = 0; e < kVec; ++e) acc[e] = 0.f;
-
-  const int nchunks = (ntok + Sh::kChunk - 1) / Sh::kChunk;
   const int nfull = ntok / Sh::kChunk;
-  // Last token-row group that holds a valid token (wave-uniform).
-  const int last_group = (ntok - 1) & ~(Sh::kTPI - 1);
-  ChunkCtx cx{kc, vc, tile_bytes, size_t(h) * tile_bytes, size_t(H) * tile_bytes, lane_off,
-              tbl, log2_bs, bs_mask, row, ntok, last_group, P.qk_scale};
-  int c = wave;
-  for (; c < nfull; c += kWaves) chunk_step<DT, D, U, false>(cx, c * Sh::kChunk, qv, m, l, acc);
-  if (c < nchunks) chunk_step<DT, D, U, true>(cx, c * Sh::kChunk, qv, m, l, acc);
+  int c = 0;
+  for (; c < nfull; ++c) chunk_step<DT, D, U, false>(cx, c * Sh::kChunk, qv, m, l, acc);
+  if (c * Sh::kChunk < ntok) chunk_step<DT, D, U, true>(cx, c * Sh::kChunk, qv, m, l, acc);
 
-  // Merge the token rows of the wave (lanes with equal col).
 #pragma unroll
   for (int off = Sh::kLPT; off < kWave; off <<= 1) {
     const float mo = __shfl_xor(m, off, kWave);
@@ -225,42 +233,78 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     for (int e = 0; e < kVec; ++e) acc[e] = acc[e] * a + __shfl_xor(acc[e], off, kWave) * b;
     m = mn;
   }
-
-  // Merge the waves through LDS.
-  __shared__ float s_ml[kWaves][2];
-  __shared__ float s_acc[kWaves][D];
-  if (row == 0) {
+  const float inv = 1.0f / l;  // l >= 1: the running max token contributes 2^0
+  if (nparts == 1) {
+    if (row != 0) return;
+    T* o = reinterpret_cast<T*>(P.out) + row_id * D + col * kVec;
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) s_acc[wave][col * kVec + e] = acc[e];
+    for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, acc[e] * inv);
+    return;
   }
-  if (lane == 0) {
-    s_ml[wave][0] = m;
-    s_ml[wave][1] = l;
-  }
-  __syncthreads();
-  for (int d = threadIdx.x; d < D; d += kThreads) {
-    float M = kNegBig;
+  const size_t pi0 = row_id * P.max_parts;
+  if (P.counters == nullptr) {  // two-launch form: the reduce kernel merges
+    if (row == 0) {
+      float* o = P.ws_o + (pi0 + part) * D + col * kVec;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][0]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float a = fast_exp2(s_ml[w][0] - M);
-      L += s_ml[w][1] * a;
-      O += s_acc[w][d] * a;
-    }
-    if (nparts == 1) {
-      T* o = reinterpret_cast<T*>(P.out) + row_id * D;
-      o[d] = to_store(DT{}, L > 0.f ? O / L : 0.f);
-    } else {
-      const size_t pi = row_id * P.max_parts + part;
-      P.ws_o[pi * D + d] = O / L;
-      if (d == 0) {
-        P.ws_ml[2 * pi] = M;
-        P.ws_ml[2 * pi + 1] = L;
+      for (int e = 0; e < kVec; ++e) o[e] = acc[e] * inv;
+      if (col == 0) {
+        P.ws_ml[2 * (pi0 + part)] = m;
+        P.ws_ml[2 * (pi0 + part) + 1] = l;
       }
     }
+    return;
   }
+  // Fused merge: the wave that finishes a (sequence, head) last merges all of
+  // its partitions.  Partials and the counter are exchanged only through
+  // agent-scope atomic accesses, which are coherent across the XCDs' L2s
+  // without cache-wide write-back/invalidate fences: the partial stores are
+  // complete (s_waitcnt) before this wave's counter increment is issued, and
+  // the merging wave issues its partial loads only after its increment
+  // returned the count of all the others.
+  if (row == 0) {
+    float* o = P.ws_o + (pi0 + part) * D + col * kVec;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e)
+      __hip_atomic_store(o + e, acc[e] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (col == 0) {
+      __hip_atomic_store(P.ws_ml + 2 * (pi0 + part), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.ws_ml + 2 * (pi0 + part) + 1, l, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // all counters zero: this wave's stores are complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(P.counters + row_id, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, kWave);
+  if (prev != nparts - 1) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (lane == 0)  // every partition has counted: reset for the next call
+    __hip_atomic_store(P.counters + row_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (row != 0) return;
+  const float* ml = P.ws_ml + 2 * pi0;
+  float M = kNegBig;
+  for (int p = 0; p < nparts; ++p)
+    M = fmaxf(M, __hip_atomic_load(ml + 2 * p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  float L = 0.f, O[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) O[e] = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float mp = __hip_atomic_load(ml + 2 * p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float lp = __hip_atomic_load(ml + 2 * p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float w = lp * fast_exp2(mp - M);
+    L += w;
+    const float* po = P.ws_o + (pi0 + p) * D + col * kVec;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e)
+      O[e] += w * __hip_atomic_load(po + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  T* o = reinterpret_cast<T*>(P.out) + row_id * D + col * kVec;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, O[e] / L);  // as the reduce kernel
 }
 
 // Log-sum-exp merge of a sequence's partitions: with M = max_p m_p and
@@ -290,13 +334,18 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams P) {
 }
 
 // ------------------------------------------------------------------ host side
-constexpr int kUnroll = 8;
+constexpr int kUnroll = PA_DECODE_UNROLL;  // 16-byte K loads (and V loads) per lane per chunk
 
 struct Plan {
   int part_tokens;
   int max_parts;
   size_t ws_bytes;
 };
+
+// Workspace: [S*H int32 counters, padded to 256 B][S*H*P*2 float (max, sum)][S*H*P*D float]
+static size_t counter_bytes(int32_t S, int32_t H) {
+  return (size_t(S) * H * sizeof(int) + 255) & ~size_t(255);
+}
 
 static int chunk_tokens(int32_t head_dim, int32_t dtype) {
   const int vec = 16 / elem_bytes(dtype);
@@ -331,14 +380,15 @@ static int make_plan(int32_t S, int32_t H, int32_t D, int32_t bs, int32_t max_ct
   const int parts = max_ctx == 0 ? 1 : (max_ctx + pt - 1) / pt;
   plan->part_tokens = pt;
   plan->max_parts = parts;
-  plan->ws_bytes = parts > 1 ? size_t(S) * H * parts * (size_t(D) + 2) * sizeof(float) : 0;
+  plan->ws_bytes = parts > 1 ? counter_bytes(S, H) + size_t(S) * H * parts * (size_t(D) + 2) * sizeof(float)
+                             : 0;
   return PA_OK;
 }
 
 template <class DT, int D>
 static void launch_partitions(const DecodeParams& p, int S, hipStream_t st) {
-  dim3 grid(p.max_parts, p.H, S);
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
+  dim3 grid((p.H + kWaves - 1) / kWaves, p.max_parts, S);
+  hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
 }
 
 template <class DT, int D>
@@ -366,7 +416,7 @@ static void dispatch(int32_t dtype, int32_t D, const DecodeParams& p, int S, hip
 #undef PA_LAUNCH
 }
 
-enum { kDoPartitions = 1, kDoReduce = 2 };
+enum { kDoPartitions = 1, kDoReduce = 2, kFused = 4 };
 
 static int decode_impl(int what, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, int32_t maxB, const int32_t* context_lens,
@@ -392,9 +442,11 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.out = out;
-  p.ws_ml = reinterpret_cast<float*>(workspace);
-  p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(workspace) + size_t(S) * H * plan.max_parts * 2
-                         : nullptr;
+  char* ws = reinterpret_cast<char*>(workspace);
+  const bool split = plan.ws_bytes > 0;
+  p.counters = (split && (what & kFused)) ? reinterpret_cast<int*>(ws) : nullptr;
+  p.ws_ml = split ? reinterpret_cast<float*>(ws + counter_bytes(S, H)) : nullptr;
+  p.ws_o = split ? p.ws_ml + size_t(S) * H * plan.max_parts * 2 : nullptr;
   p.H = H;
   p.maxB = maxB;
   p.log2_bs = log2_exact(bs);
@@ -404,7 +456,7 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (what & kDoPartitions) dispatch<true>(dtype, D, p, S, st);
-  if ((what & kDoReduce) && plan.max_parts > 1) dispatch<false>(dtype, D, p, S, st);
+  if ((what & kDoReduce) && !(what & kFused) && plan.max_parts > 1) dispatch<false>(dtype, D, p, S, st);
   return launch_status();
 }
 
@@ -447,7 +499,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
       workspace_bytes, partition_tokens, stream
 
 int pa_decode(PA_DECODE_ARGS) {
-  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce, PA_DECODE_PASS);
+  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, PA_DECODE_PASS);
 }
 int pa_decode_partitions(PA_DECODE_ARGS) {
   return pa::decode_impl(pa::kDoPartitions, PA_DECODE_PASS);

@@ -106,12 +106,14 @@ class PagedKVEngine:
         return slots, cows
 
     # --------------------------------------------------------------- step
-    def step(self, seqs, q, k_new, v_new, scale, out=None, partition_tokens=0, timing=None):
+    def step(self, seqs, q, k_new, v_new, scale, out=None, partition_tokens=0, timing=None,
+             two_launch=False):
         """One decode step for ``seqs`` (int64 array): append a slot to each, ship the
         tables, copy shared last blocks, write k_new/v_new [S, H, D], decode q [S, H, D].
 
         ``timing`` (optional) = (start_event, end_event) recorded around the
-        decode's partition kernel.  Returns out [S, H, D]."""
+        decode launch.  ``two_launch`` uses pa_decode_partitions + pa_decode_reduce
+        instead of the single-launch pa_decode.  Returns out [S, H, D]."""
         torch = self.torch
         seqs = np.ascontiguousarray(seqs, dtype=np.int64)
         S = seqs.size
@@ -138,16 +140,19 @@ class PagedKVEngine:
         _, _, ws = decode_plan(S, self.H, self.D, self.bs, max_ctx, self.dt_code,
                                partition_tokens)
         if ws and (self._workspace is None or self._workspace.numel() < ws):
-            self._workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+            # zero-filled: pa_decode's per-row counters must start at zero
+            self._workspace = torch.zeros(ws, dtype=torch.uint8, device=self.device)
         args = (q, self.k_cache, self.v_cache, d_tables, d_ctx, scale, max_ctx, out,
                 self._workspace, partition_tokens)
-        if timing is None:
-            decode(*args)
-        else:
+        if timing is not None:
             timing[0].record(stream)
+        if two_launch:
             decode_partitions(*args)
-            timing[1].record(stream)
             decode_reduce(*args)
+        else:
+            decode(*args)
+        if timing is not None:
+            timing[1].record(stream)
         self.last_step = dict(num_cow=ncow, max_ctx=max_ctx, ctx=h_ctx.copy(),
                               cows=h_cows[:2 * ncow].reshape(-1, 2).copy(),
                               slots=h_slots.copy())

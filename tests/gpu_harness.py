@@ -12,6 +12,14 @@ import synth
 
 TOL = 2e-3   # max |gpu - oracle| on attention outputs (fp32 accumulation, one final rounding)
 
+# Bound of the final round-to-nearest-even cast of a value x to the output type:
+# half an ulp, at most 2^-8 |x| for bfloat16 (8-bit significand) and 2^-11 |x|
+# for float16.  The configs' outputs are averages over hundreds of N(0,1)
+# tokens (|out| << 1), where 2e-3 alone holds; tests with a handful of tokens
+# give |out| near 1, where the cast by itself can exceed 2e-3 in bfloat16, so
+# those tests allow TOL + CAST_REL[dtype] * |oracle|.
+CAST_REL = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
 
 def log(msg):
     print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
@@ -78,18 +86,20 @@ def run_gpu(wl, partition_tokens=0, fill_nan=True):
     return dict(engine=eng, out=out)
 
 
-def compare_outputs(gpu_out, ref, seqs=None, tol=TOL, what=""):
-    """Element-wise check of GPU out (torch) against the oracle's fp64 out."""
+def compare_outputs(gpu_out, ref, seqs=None, tol=TOL, what="", cast_dtype=None):
+    """Element-wise check of GPU out (torch) against the oracle's fp64 out:
+    |gpu - ref| <= tol (+ CAST_REL[cast_dtype] * |ref| when cast_dtype is given)."""
     g = gpu_out.float().cpu().numpy().astype(np.float64)
     rows = list(range(ref.shape[0])) if seqs is None else list(seqs)
     g, r = g[rows], ref[rows]
     assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
     err = np.abs(g - r)
+    bound = tol + (CAST_REL[cast_dtype] * np.abs(r) if cast_dtype else 0.0)
     worst = float(err.max()) if err.size else 0.0
     rel = float((err / np.maximum(np.abs(r), 1e-3)).max()) if err.size else 0.0
     log(f"{what}: max abs err {worst:.3e}, mean {float(err.mean()) if err.size else 0:.3e}, "
         f"max rel {rel:.3e} over {len(rows)} seqs")
-    assert worst <= tol, f"{what}: max abs err {worst} > {tol}"
+    assert np.all(err <= bound), f"{what}: max abs err {worst} over the bound (tol {tol})"
     return worst
 
 
