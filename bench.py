@@ -41,14 +41,6 @@ def decode_bytes(ctx, H, D, elem, bs):
     return kv + 2 * S * H * D * elem + int((-(-ctx // bs)).sum()) * 4 + 4 * S, kv
 
 
-def partition_kernel_bytes(ctx, H, D, elem, bs):
-    """Bytes the partition kernel must read: K/V, q, table entries, context lengths."""
-    ctx = np.asarray(ctx, dtype=np.int64)
-    S = ctx.size
-    return int(ctx.sum()) * H * D * 2 * elem + S * H * D * elem + \
-        int((-(-ctx // bs)).sum()) * 4 + 4 * S
-
-
 def step_bytes(ctx, H, D, elem, bs, ncow):
     """Whole step: decode + cache write (read k, v; write both rows) + slots + CoW copies."""
     S = len(ctx)
@@ -56,7 +48,7 @@ def step_bytes(ctx, H, D, elem, bs, ncow):
     return dec + 4 * S * H * D * elem + 8 * S + ncow * 2 * 2 * H * bs * D * elem
 
 
-def build_state(wl, dtype):
+def build_state(wl, dtype, partition_tokens=0, extra_blocks=64):
     """Run the workload's cache-building ops (prefill, forks, extends) on the GPU.
     Returns the engine and the step's sequence list."""
     import torch
@@ -66,9 +58,9 @@ def build_state(wl, dtype):
     for op in wl.ops:
         if op[0] == "step":
             step_seqs = np.array(op[1], dtype=np.int64)
-    eng = PagedKVEngine(wl.NB, wl.H, wl.D, wl.bs, dtype, wl.max_blocks_per_seq + 64,
+    eng = PagedKVEngine(wl.NB, wl.H, wl.D, wl.bs, dtype, wl.max_blocks_per_seq + extra_blocks,
                         len(step_seqs), free_order=wl.free_order, pad_block=wl.poison_block,
-                        fill=0.0)
+                        fill=0.0, partition_tokens=partition_tokens)
     for op in wl.ops:
         if op[0] == "add":
             k, v = wl.kv(op[1], 0, op[2])
@@ -163,46 +155,55 @@ def main():
     t_setup = time.perf_counter()
     wl = synth.make_workload(args.config, bs=args.bs)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.dtype]
-    eng, seqs = build_state(wl, tdt)
+    pt_req = args.partition_tokens or wl.partition_tokens
+    grow = args.warmup + args.steps
+    eng, seqs = build_state(wl, tdt, pt_req, extra_blocks=-(-grow // wl.bs) + 1)
     from synth import to_torch as to_dev
     S = seqs.size
     q = to_dev(wl.q, wl.dtype)
-    k_new = torch.randn(S, wl.H, wl.D, device=dev).to(tdt)
-    v_new = torch.randn(S, wl.H, wl.D, device=dev).to(tdt)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    k_new = torch.randn(S, wl.H, wl.D, device=dev, generator=gen).to(tdt)
+    v_new = torch.randn(S, wl.H, wl.D, device=dev, generator=gen).to(tdt)
     out = torch.empty_like(q)
     eprint(f"setup {time.perf_counter() - t_setup:.1f} s: {wl.name}, S={S}, "
            f"sum(ctx)={int(wl.ctx.sum())}")
 
-    pt = args.partition_tokens or wl.partition_tokens
     for _ in range(args.warmup):
-        eng.step(seqs, q, k_new, v_new, wl.scale, out=out, partition_tokens=pt)
+        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
     torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    ctxs, ncows = [], []
+    for a, b in evs:                      # create the HIP events before timing
+        a.record()
+        b.record()
+    ncows, pts = 0, set()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        eng.step(seqs, q, k_new, v_new, wl.scale, out=out, partition_tokens=pt, timing=evs[i])
-        ctxs.append(eng.last_step["ctx"])
-        ncows.append(eng.last_step["num_cow"])
+        eng.set_decode_events(*evs[i])
+        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
+        ncows += eng.last_info.num_cow
+        pts.add(eng.last_info.partition_tokens)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    eng.set_decode_events(None, None)
 
+    # each step appends one token to every sequence: the contexts of timed
+    # step i are the workload's step contexts + warmup + i
+    ctxs = [wl.ctx + args.warmup + i for i in range(args.steps)]
     elem = wl.elem_bytes
-    total_step_bytes = sum(step_bytes(c, wl.H, wl.D, elem, wl.bs, n) for c, n in zip(ctxs, ncows))
+    total_step_bytes = sum(step_bytes(c, wl.H, wl.D, elem, wl.bs, 0) for c in ctxs) + \
+        ncows * 2 * 2 * wl.H * wl.bs * wl.D * elem
     dec_bytes = [decode_bytes(c, wl.H, wl.D, elem, wl.bs)[0] for c in ctxs]
-    part_bytes = [partition_kernel_bytes(c, wl.H, wl.D, elem, wl.bs) for c in ctxs]
     elapsed = t1 - t0
     ms_per_step = elapsed / args.steps * 1e3
     kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
     kern_s = float(kern_ms.mean()) / 1e3
-    achieved = float(np.mean(part_bytes)) / kern_s / 1e9
+    achieved = float(np.mean(dec_bytes)) / kern_s / 1e9
     value = total_step_bytes / elapsed / 1e9
-    pt_used, nparts, _ = pk.decode_plan(S, wl.H, wl.D, wl.bs, int(ctxs[-1].max()),
-                                        pk.DTYPE_CODES()[tdt], pt)
-    traffic = load_traffic("decode_partition_" + wl.name)
+    traffic = load_traffic("decode_" + wl.name)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -221,18 +222,19 @@ def main():
                    "block_size": wl.bs, "num_blocks": wl.NB,
                    "ctx_sum_first_step": int(ctxs[0].sum()),
                    "ctx_sum_last_step": int(ctxs[-1].sum()),
-                   "partition_tokens": pt_used, "partitions_max": nparts},
+                   "partition_tokens": sorted(pts)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S * args.steps / elapsed, 1),
         "decode_seq_steps_per_s": round(S / kern_s, 1),
-        "decode_partition_kernel_us": round(kern_s * 1e6, 2),
-        "decode_partition_kernel_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
-                                               round(float(np.percentile(kern_ms, 90)) * 1e3, 2)],
-        "decode_bytes_per_step": int(np.mean(dec_bytes)),
+        "decode_us": round(kern_s * 1e6, 2),
+        "decode_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+                              round(float(np.percentile(kern_ms, 90)) * 1e3, 2)],
+        "decode_gbps": round(achieved, 2),
+        "decode_pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_partition_kernel",
-                     "algorithmic_bytes_per_launch": int(np.mean(part_bytes))},
+                     "traffic": traffic, "kernel": "decode_wave_kernel (pa_decode_scheduled)",
+                     "algorithmic_bytes_per_launch": int(np.mean(dec_bytes))},
     }
     if not args.no_cpu_baseline:
         t = time.perf_counter()

@@ -15,7 +15,8 @@ import numpy as np
 
 __all__ = [
     "lib", "PAError", "cache_write", "copy_blocks", "decode", "decode_partitions",
-    "decode_reduce", "decode_plan", "decode_workspace_size", "BlockManager",
+    "decode_reduce", "decode_plan", "decode_workspace_size", "decode_schedule",
+    "decode_scheduled", "BlockManager",
     "DTYPE_CODES", "LIB_PATH",
 ]
 
@@ -39,6 +40,9 @@ _SIGNATURES = {
     "pa_decode": (_c.c_int, _DECODE_ARGS),
     "pa_decode_partitions": (_c.c_int, _DECODE_ARGS),
     "pa_decode_reduce": (_c.c_int, _DECODE_ARGS),
+    "pa_decode_scheduled": (_c.c_int, _DECODE_ARGS + [_vp, _i32]),
+    "pa_decode_schedule": (_c.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _pi32,
+                                      _pi32, _pi32]),
     "pa_decode_plan": (_c.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
                                   _c.POINTER(_sz)]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
@@ -58,7 +62,22 @@ _SIGNATURES = {
     "pa_bm_num_free": (_i64, [_vp]),
     "pa_bm_num_seqs": (_i64, [_vp]),
     "pa_bm_free_list": (_i64, [_vp, _vp, _i64]),
+    "pa_engine_staging_bytes": (_sz, [_i32, _i32, _i32]),
+    "pa_engine_create": (_c.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                    _vp, _i32, _vp, _c.POINTER(_vp)]),
+    "pa_engine_destroy": (None, [_vp]),
+    "pa_engine_workspace_bytes": (_sz, [_vp, _i32]),
+    "pa_engine_step": (_c.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _sz, _i32, _vp,
+                                  _vp]),
+    "pa_engine_last_step": (_c.c_int, [_vp, _i32, _vp, _vp, _vp, _i32]),
+    "pa_engine_set_decode_events": (_c.c_int, [_vp, _vp, _vp]),
 }
+
+
+class StepInfo(_c.Structure):
+    _fields_ = [("num_cow", _c.c_int32), ("max_context_len", _c.c_int32),
+                ("partition_tokens", _c.c_int32), ("num_items", _c.c_int32),
+                ("sum_context_len", _c.c_int64)]
 
 
 class PAError(RuntimeError):
@@ -181,7 +200,7 @@ def decode_workspace_size(num_seqs, num_heads, head_dim, block_size, max_context
 
 
 def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale,
-                 max_context_len, out, workspace, partition_tokens, stream):
+                 max_context_len, out, workspace, partition_tokens, stream, extra=()):
     torch = _torch()
     S, H, D = q.shape
     NB, Hc, bs, Dc = k_cache.shape
@@ -209,9 +228,38 @@ def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale
         _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
         _dev(context_lens, "context_lens", torch.int32), S, H, D, bs, NB, float(scale),
         int(max_context_len), dt, _dev(out, "out"), ws_ptr, ws_bytes, int(partition_tokens),
-        _stream(stream, q.device))
+        _stream(stream, q.device), *extra)
     _check(rc, fn_name)
     return out
+
+
+def decode_schedule(context_lens_host, num_heads, head_dim, block_size, dtype_code,
+                    partition_tokens=0):
+    """Host work list for pa_decode_scheduled: (items int32 [n, 2], partition_tokens,
+    max_context_len)."""
+    ctx = np.ascontiguousarray(context_lens_host, dtype=np.int32)
+    n, pt, mx = _c.c_int32(), _c.c_int32(), _c.c_int32()
+    rc = lib().pa_decode_schedule(_ptr(ctx), ctx.size, num_heads, head_dim, block_size,
+                                  dtype_code, partition_tokens, None, 0, _c.byref(n),
+                                  _c.byref(pt), _c.byref(mx))
+    if rc not in (PA_OK, -8):
+        _check(rc, "pa_decode_schedule")
+    items = np.empty((max(n.value, 1), 2), dtype=np.int32)
+    rc = lib().pa_decode_schedule(_ptr(ctx), ctx.size, num_heads, head_dim, block_size,
+                                  dtype_code, partition_tokens, _ptr(items), n.value,
+                                  _c.byref(n), _c.byref(pt), _c.byref(mx))
+    _check(rc, "pa_decode_schedule")
+    return items[:n.value], pt.value, mx.value
+
+
+def decode_scheduled(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                     items, partition_tokens, out=None, workspace=None, stream=None):
+    """pa_decode over a device work list ``items`` [n, 2] int32 from decode_schedule."""
+    torch = _torch()
+    n = int(items.shape[0])
+    return _decode_call("pa_decode_scheduled", q, k_cache, v_cache, block_tables, context_lens,
+                        scale, max_context_len, out, workspace, partition_tokens, stream,
+                        extra=(_dev(items, "items", torch.int32), n))
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=None,

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["decode.hip", "cache_ops.hip", "block_manager.cpp", "capi.cpp"]
+SOURCES = ["decode.hip", "cache_ops.hip", "block_manager.cpp", "capi.cpp", "engine.cpp"]
 ARCH = "gfx950"
 
 

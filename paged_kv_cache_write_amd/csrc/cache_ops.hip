@@ -9,6 +9,7 @@
 // Both are pure 16-byte moves: each lane carries one 16-byte slice of a
 // token row (D elements), so a wave moves 1 KiB of contiguous source per
 // instruction and writes whole 16-byte slices of contiguous destination rows.
+#include "internal.hpp"
 #include "launch_common.hpp"
 #include "pa_device.hpp"
 
@@ -54,6 +55,63 @@ __global__ __launch_bounds__(kCwThreads) void copy_blocks_kernel(
     kd[i] = a;
     vd[i] = b;
   }
+}
+
+// Engine step prologue.  Workgroups [0, copy_wgs) copy the staging bytes
+// from pinned host memory (read over the host link) to device memory; each
+// workgroup after them writes one new token: one lane reads the token's slot
+// from host memory, the workgroup then moves the token's H rows of K and V.
+__global__ __launch_bounds__(kCwThreads) void step_prologue_kernel(
+    const u32x4* __restrict__ host_src, u32x4* __restrict__ dev_dst, int64_t copy_vecs,
+    int copy_wgs, const int64_t* __restrict__ host_slots, const char* __restrict__ k,
+    const char* __restrict__ v, char* __restrict__ k_cache, char* __restrict__ v_cache, int H,
+    int vecs_per_row, int row_bytes, int log2_bs) {
+  if (int(blockIdx.x) < copy_wgs) {
+    for (int64_t i = int64_t(blockIdx.x) * kCwThreads + threadIdx.x; i < copy_vecs;
+         i += int64_t(copy_wgs) * kCwThreads)
+      dev_dst[i] = host_src[i];
+    return;
+  }
+  const int64_t n = int64_t(blockIdx.x) - copy_wgs;
+  __shared__ int64_t s_slot;
+  if (threadIdx.x == 0) s_slot = host_slots[n];
+  __syncthreads();
+  const int64_t slot = s_slot;
+  if (slot < 0) return;
+  const int64_t blk = slot >> log2_bs;
+  const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
+  const int total = H * vecs_per_row;
+  for (int i = threadIdx.x; i < total; i += kCwThreads) {
+    const int h = i / vecs_per_row;
+    const int col = i - h * vecs_per_row;
+    const int64_t dst = ((((blk * H + h) << log2_bs) + off) * row_bytes) + int64_t(col) * 16;
+    const int64_t src = (n * total + i) * 16;
+    *reinterpret_cast<u32x4*>(k_cache + dst) = *reinterpret_cast<const u32x4*>(k + src);
+    *reinterpret_cast<u32x4*>(v_cache + dst) = *reinterpret_cast<const u32x4*>(v + src);
+  }
+}
+
+int launch_step_prologue(const void* host_src, void* dev_dst, size_t copy_bytes,
+                         const int64_t* host_slots, const void* k, const void* v, int64_t n,
+                         void* k_cache, void* v_cache, int32_t num_heads, int32_t head_dim,
+                         int32_t block_size, int32_t dtype, hipStream_t stream) {
+  int rc = check_shape(head_dim, block_size, dtype);
+  if (rc != PA_OK) return rc;
+  if (copy_bytes % 16 || !aligned16(host_src) || !aligned16(dev_dst) || n < 0 || n > 65535)
+    return PA_ERR_INVALID;
+  if (n > 0 && (!k || !v || !aligned16(k) || !aligned16(v) || !host_slots)) return PA_ERR_INVALID;
+  const int64_t copy_vecs = int64_t(copy_bytes / 16);
+  int copy_wgs = int((copy_vecs + kCwThreads * 4 - 1) / (kCwThreads * 4));
+  if (copy_wgs < 1) copy_wgs = 1;
+  const int row_bytes = head_dim * elem_bytes(dtype);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(step_prologue_kernel, dim3(unsigned(copy_wgs + n)), dim3(kCwThreads), 0,
+                     stream, static_cast<const u32x4*>(host_src), static_cast<u32x4*>(dev_dst),
+                     copy_vecs, copy_wgs, host_slots, static_cast<const char*>(k),
+                     static_cast<const char*>(v), static_cast<char*>(k_cache),
+                     static_cast<char*>(v_cache), num_heads, row_bytes / 16, row_bytes,
+                     log2_exact(block_size));
+  return launch_status();
 }
 
 }  // namespace pa

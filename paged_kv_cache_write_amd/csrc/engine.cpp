@@ -1,0 +1,273 @@
+// One decode engine step in native code: host slot assignment, schedule,
+// table shipment, copy-on-write copies, slot-mapped cache write and
+// scheduled PagedAttention decode, all enqueued on the caller's stream.
+//
+// The step is the serving loop of the pages: the scheduler's block manager
+// gives each running sequence the slot of its new token (a new block when
+// the last is full, a copy when it is shared; comfyai.app "6.4 PagedAttention"
+// 6.4.3, polomodov.tech "vLLM and PagedAttention" slides 11-13), and the
+// block tables travel to the GPU workers every step (slide 16).
+//
+// Staging: the caller gives `ring` pinned host slots and one device slot of
+// pa_engine_staging_bytes() each.  A step fills host slot i (slots, context
+// lengths, CoW pairs, block tables, work items), copies exactly the used
+// bytes to the device slot with one hipMemcpyAsync, and records an event;
+// host slot i is reused only after that event.  The device slot is reused in
+// stream order.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "internal.hpp"
+#include "pa.h"
+
+struct pa_engine {
+  pa_bm* bm = nullptr;
+  void* k_cache = nullptr;
+  void* v_cache = nullptr;
+  int64_t num_blocks = 0;
+  int32_t H = 0, D = 0, bs = 0, dtype = 0;
+  int32_t max_batch = 0, max_blocks = 0, pad = 0;
+  char* host = nullptr;
+  char* host_dev = nullptr;  // device-visible address of `host` (NULL: use hipMemcpyAsync)
+  char* dev = nullptr;
+  size_t slot_bytes = 0;
+  int32_t ring = 0, next = 0;
+  std::vector<hipEvent_t> events;
+  std::vector<char> pending;
+  std::vector<int32_t> ctx_pre;
+  hipEvent_t ev_start = nullptr, ev_end = nullptr;  // optional, around the decode launch
+};
+
+namespace {
+
+// Work items are bounded by one per 32 tokens (the smallest partition) plus
+// one per sequence.
+int64_t item_capacity(int32_t max_batch, int32_t max_blocks, int32_t bs) {
+  const int64_t tokens = int64_t(max_blocks) * bs;
+  return int64_t(max_batch) * ((tokens + 31) / 32 + 1);
+}
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_engine_staging_bytes(int32_t max_batch, int32_t max_blocks_per_seq,
+                               int32_t block_size) {
+  if (max_batch <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;
+  const size_t B = size_t(max_batch);
+  return align16(8 * B + 4 * B + 8 * B + 4 * B * size_t(max_blocks_per_seq) +
+                8 * size_t(item_capacity(max_batch, max_blocks_per_seq, block_size)));
+}
+
+int pa_engine_create(pa_bm* bm, void* k_cache, void* v_cache, int64_t num_blocks,
+                     int32_t num_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                     int32_t max_batch, int32_t max_blocks_per_seq, int32_t pad_block,
+                     void* host_staging, int32_t ring, void* dev_staging, pa_engine** out) {
+  if (!out) return PA_ERR_INVALID;
+  *out = nullptr;
+  if (!bm || !k_cache || !v_cache || !host_staging || !dev_staging || ring <= 0 ||
+      num_blocks <= 0 || num_heads <= 0 || max_batch <= 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_INVALID;
+  if (size_t(host_staging) % 16 || size_t(dev_staging) % 16) return PA_ERR_INVALID;
+  size_t ws;
+  int rc = pa_decode_plan(1, num_heads, head_dim, block_size, 0, dtype, 0, nullptr, nullptr, &ws);
+  if (rc != PA_OK) return rc;
+  pa_engine* e = new (std::nothrow) pa_engine;
+  if (!e) return PA_ERR_INVALID;
+  e->bm = bm;
+  e->k_cache = k_cache;
+  e->v_cache = v_cache;
+  e->num_blocks = num_blocks;
+  e->H = num_heads;
+  e->D = head_dim;
+  e->bs = block_size;
+  e->dtype = dtype;
+  e->max_batch = max_batch;
+  e->max_blocks = max_blocks_per_seq;
+  e->pad = pad_block;
+  e->host = static_cast<char*>(host_staging);
+  e->dev = static_cast<char*>(dev_staging);
+  e->slot_bytes = pa_engine_staging_bytes(max_batch, max_blocks_per_seq, block_size);
+  e->ring = ring;
+  {
+    // Pinned host memory is mapped for the device: the step prologue kernel
+    // reads the staging straight from it instead of a DMA copy.
+    void* dptr = nullptr;
+    if (hipHostGetDevicePointer(&dptr, host_staging, 0) == hipSuccess && dptr &&
+        size_t(dptr) % 16 == 0 && size_t(host_staging) % 16 == 0)
+      e->host_dev = static_cast<char*>(dptr);
+    else
+      (void)hipGetLastError();
+  }
+  e->events.assign(size_t(ring), nullptr);
+  e->pending.assign(size_t(ring), 0);
+  for (auto& ev : e->events) {
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+      pa_engine_destroy(e);
+      return PA_ERR_HIP;
+    }
+  }
+  *out = e;
+  return PA_OK;
+}
+
+void pa_engine_destroy(pa_engine* e) {
+  if (!e) return;
+  for (size_t i = 0; i < e->events.size(); ++i) {
+    if (e->events[i]) {
+      if (e->pending[i]) (void)hipEventSynchronize(e->events[i]);
+      (void)hipEventDestroy(e->events[i]);
+    }
+  }
+  delete e;
+}
+
+size_t pa_engine_workspace_bytes(const pa_engine* e, int32_t partition_tokens) {
+  if (!e) return size_t(-1);
+  // the schedule never picks partitions below 256 tokens (or the block-size
+  // limit); an explicit size is used as given
+  int32_t pt = partition_tokens;
+  if (pt == 0) pt = std::min<int32_t>(256, 64 * e->bs);
+  return pa_decode_workspace_size(e->max_batch, e->H, e->D, e->bs, e->max_blocks * e->bs,
+                                  e->dtype, pt);
+}
+
+int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
+                   const void* k_new, const void* v_new, float scale, void* out,
+                   void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                   void* stream, pa_step_info* info) {
+  if (!e || n < 0 || n > e->max_batch || (n > 0 && !seqs)) return PA_ERR_INVALID;
+  if (info) std::memset(info, 0, sizeof(*info));
+  if (n == 0) return PA_OK;
+  // Every argument the launches check is checked here, before the block
+  // manager commits the appends.
+  for (const void* p : {q, k_new, v_new, static_cast<const void*>(out)})
+    if (!p || size_t(p) % 16) return PA_ERR_INVALID;
+  if (workspace && size_t(workspace) % 16) return PA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // 1. The lengths after this step, to plan the decode before touching the
+  //    block manager (a step that cannot run changes nothing).
+  e->ctx_pre.resize(size_t(n));
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t len = pa_bm_seq_len(e->bm, seqs[i]);
+    if (len < 0) return int(len);
+    e->ctx_pre[i] = int32_t(len + 1);
+  }
+  // repeated sequences in one step append several tokens
+  {
+    std::vector<int64_t> sorted(seqs, seqs + n);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return PA_ERR_INVALID;
+  }
+  for (int32_t i = 0; i < n; ++i)
+    if (e->ctx_pre[i] > e->max_blocks * e->bs) return PA_ERR_CAPACITY;
+
+  // 2. Host staging slot.
+  const int32_t slot = e->next;
+  if (e->pending[slot]) {
+    if (hipEventSynchronize(e->events[slot]) != hipSuccess) return PA_ERR_HIP;
+    e->pending[slot] = 0;
+  }
+  char* h = e->host + size_t(slot) * e->slot_bytes;
+  const size_t off_slots = 0, off_ctx = 8 * size_t(n), off_cow = off_ctx + 4 * size_t(n);
+  const size_t off_tab = off_cow + 8 * size_t(n);
+  const size_t off_items = off_tab + 4 * size_t(n) * size_t(e->max_blocks);
+  int64_t* h_slots = reinterpret_cast<int64_t*>(h + off_slots);
+  int32_t* h_ctx = reinterpret_cast<int32_t*>(h + off_ctx);
+  int32_t* h_cow = reinterpret_cast<int32_t*>(h + off_cow);
+  int32_t* h_tab = reinterpret_cast<int32_t*>(h + off_tab);
+  int32_t* h_items = reinterpret_cast<int32_t*>(h + off_items);
+  const int64_t cap_items = item_capacity(e->max_batch, e->max_blocks, e->bs);
+
+  // 3. Schedule first (from the lengths after the step), then check the
+  //    workspace, then commit the appends.
+  int32_t n_items = 0, pt = 0, max_ctx = 0;
+  int rc = pa_decode_schedule(e->ctx_pre.data(), n, e->H, e->D, e->bs, e->dtype, partition_tokens,
+                              h_items, int32_t(cap_items), &n_items, &pt, &max_ctx);
+  if (rc != PA_OK) return rc;
+  const size_t ws_need = pa_decode_workspace_size(n, e->H, e->D, e->bs, max_ctx, e->dtype, pt);
+  if (ws_need == size_t(-1)) return PA_ERR_INVALID;
+  if (ws_need > workspace_bytes || (ws_need > 0 && !workspace)) return PA_ERR_WORKSPACE;
+  int32_t ncow = 0;
+  rc = pa_bm_step(e->bm, seqs, n, h_slots, h_cow, &ncow, h_tab, e->max_blocks, e->pad, h_ctx);
+  if (rc != PA_OK) return rc;
+
+  // 4. Ship the used bytes, copy shared last blocks, write the new tokens.
+  //    Copies must land before the writes into the copied blocks; without
+  //    copies, one prologue launch ships the staging and writes the tokens.
+  const size_t used = (off_items + 8 * size_t(n_items) + 15) & ~size_t(15);
+  char* d = e->dev;
+  const bool fused = e->host_dev != nullptr && ncow == 0;
+  if (fused) {
+    char* hd = e->host_dev + size_t(slot) * e->slot_bytes;
+    rc = pa::launch_step_prologue(hd, d, used, reinterpret_cast<const int64_t*>(hd + off_slots),
+                                  k_new, v_new, n, e->k_cache, e->v_cache, e->H, e->D, e->bs,
+                                  e->dtype, st);
+    if (rc != PA_OK) return rc;
+  } else if (hipMemcpyAsync(d, h, used, hipMemcpyHostToDevice, st) != hipSuccess) {
+    return PA_ERR_HIP;
+  }
+  if (!fused) {
+    if (ncow > 0) {
+      rc = pa_copy_blocks(e->k_cache, e->v_cache, reinterpret_cast<const int32_t*>(d + off_cow),
+                          ncow, e->num_blocks, e->H, e->D, e->bs, e->dtype, stream);
+      if (rc != PA_OK) return rc;
+    }
+    rc = pa_cache_write(k_new, v_new, reinterpret_cast<const int64_t*>(d + off_slots), n,
+                        e->k_cache, e->v_cache, e->num_blocks, e->H, e->D, e->bs, e->dtype,
+                        stream);
+    if (rc != PA_OK) return rc;
+  }
+  if (e->ev_start && hipEventRecord(e->ev_start, st) != hipSuccess) return PA_ERR_HIP;
+  rc = pa_decode_scheduled(q, e->k_cache, e->v_cache, reinterpret_cast<const int32_t*>(d + off_tab),
+                           e->max_blocks, reinterpret_cast<const int32_t*>(d + off_ctx), n, e->H,
+                           e->D, e->bs, e->num_blocks, scale, max_ctx, e->dtype, out, workspace,
+                           workspace_bytes, pt, stream,
+                           reinterpret_cast<const int32_t*>(d + off_items), n_items);
+  if (rc != PA_OK) return rc;
+  if (e->ev_end && hipEventRecord(e->ev_end, st) != hipSuccess) return PA_ERR_HIP;
+  // Host slot `slot` may be rewritten once this step has run (recorded at the
+  // end of the step: no marker between the prologue and the decode).
+  if (hipEventRecord(e->events[slot], st) != hipSuccess) return PA_ERR_HIP;
+  e->pending[slot] = 1;
+  e->next = (slot + 1) % e->ring;
+  if (info) {
+    info->num_cow = ncow;
+    info->max_context_len = max_ctx;
+    info->partition_tokens = pt;
+    info->num_items = n_items;
+    int64_t sum = 0;
+    for (int32_t i = 0; i < n; ++i) sum += h_ctx[i];
+    info->sum_context_len = sum;
+  }
+  return PA_OK;
+}
+
+int pa_engine_set_decode_events(pa_engine* e, void* start_event, void* end_event) {
+  if (!e) return PA_ERR_INVALID;
+  e->ev_start = static_cast<hipEvent_t>(start_event);
+  e->ev_end = static_cast<hipEvent_t>(end_event);
+  return PA_OK;
+}
+
+int pa_engine_last_step(const pa_engine* e, int32_t n, int64_t* slots, int32_t* context_lens,
+                        int32_t* cow_pairs, int32_t num_cow) {
+  if (!e || n < 0 || n > e->max_batch) return PA_ERR_INVALID;
+  const int32_t slot = (e->next + e->ring - 1) % e->ring;
+  const char* h = e->host + size_t(slot) * e->slot_bytes;
+  if (slots) std::memcpy(slots, h, 8 * size_t(n));
+  if (context_lens) std::memcpy(context_lens, h + 8 * size_t(n), 4 * size_t(n));
+  if (cow_pairs && num_cow > 0)
+    std::memcpy(cow_pairs, h + 12 * size_t(n), 8 * size_t(num_cow));
+  return PA_OK;
+}
+
+}  // extern "C"

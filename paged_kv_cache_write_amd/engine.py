@@ -1,39 +1,39 @@
 """One decode engine step on one GPU: host slot assignment, table shipment,
 copy-on-write copies, slot-mapped cache write and PagedAttention decode.
 
-The step follows the pages' serving loop: the scheduler's block manager gives
-every running sequence the slot of its new token (a fresh block when the last
-one is full, a copy when the last one is shared), the block tables travel to
-the GPU every step (polomodov.tech "vLLM and PagedAttention" slides 11-13 and
-16), the copies are made, the new K/V are written, then decode attends over
-the updated contexts.  All device work is enqueued on one stream, so the copy
-precedes the write and the write precedes the read without host waits.
-
-Host work is the C++ block manager (libpa.so); device work is libpa.so's HIP
-kernels.  torch provides the device memory, pinned staging and the stream.
+The step itself is native (pa_engine_step in libpa.so): the C++ block
+manager appends one slot per sequence, the scheduler orders the decode work,
+one host-to-device copy ships slots, tables, context lengths, copy pairs and
+work items, and the copy, cache-write and decode kernels are enqueued on the
+current stream.  This class owns the device memory (torch), the pinned
+staging ring and the handles; prefill (add_sequence) and forks are here too.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 
-from . import BlockManager, DTYPE_CODES, cache_write, copy_blocks, decode, decode_partitions, \
-    decode_plan, decode_reduce
+from . import (BlockManager, DTYPE_CODES, StepInfo, _check, _ptr, cache_write, copy_blocks,
+               lib)
 
 __all__ = ["PagedKVEngine"]
 
 
 class PagedKVEngine:
-    """Block pool + block manager + per-step staging for a batch of decoding sequences.
+    """Block pool + block manager + native step for a batch of decoding sequences.
 
     k_cache / v_cache: [num_blocks, num_heads, block_size, head_dim] of ``dtype``.
-    ``pad_block`` fills the unused tail of every exported table row (never read).
-    ``max_batch`` bounds the sequences of one step.
+    ``pad_block`` fills the unused tail of every exported table row (never used
+    as an address).  ``max_batch`` bounds the sequences of one step and
+    ``max_blocks_per_seq`` the table width (so contexts up to that many blocks).
     """
 
-    RING = 3  # pinned staging buffers in flight
+    RING = 3  # pinned staging slots in flight
 
     def __init__(self, num_blocks, num_heads, head_dim, block_size, dtype, max_blocks_per_seq,
-                 max_batch, free_order=None, pad_block=0, device="cuda", fill=None):
+                 max_batch, free_order=None, pad_block=0, device="cuda", fill=None,
+                 partition_tokens=0):
         import torch
         self.torch = torch
         self.NB, self.H, self.D, self.bs = int(num_blocks), int(num_heads), int(head_dim), \
@@ -42,6 +42,7 @@ class PagedKVEngine:
         self.dt_code = DTYPE_CODES()[dtype]
         self.maxB, self.max_batch = int(max_blocks_per_seq), int(max_batch)
         self.pad = int(pad_block)
+        self.partition_tokens = int(partition_tokens)
         self.device = torch.device(device)
         shape = (self.NB, self.H, self.bs, self.D)
         if fill is None:
@@ -51,35 +52,30 @@ class PagedKVEngine:
             self.k_cache = torch.full(shape, fill, dtype=dtype, device=self.device)
             self.v_cache = torch.full(shape, fill, dtype=dtype, device=self.device)
         self.bm = BlockManager(self.NB, self.bs, free_order)
-        # Packed per-step staging: slots int64[B] | ctx int32[B] | cow int32[2B] | tables int32[B*maxB]
-        B = self.max_batch
-        self._n_i32 = B + 2 * B + B * self.maxB
-        nbytes = 8 * B + 4 * self._n_i32
-        self._host = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
-                      for _ in range(self.RING)]
-        self._events = [None] * self.RING
-        self._ring = 0
-        self._dev = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-        self._workspace = None
-        self.last_step = {}
+        L = lib()
+        slot = int(L.pa_engine_staging_bytes(self.max_batch, self.maxB, self.bs))
+        self._host = torch.empty(slot * self.RING, dtype=torch.uint8, pin_memory=True)
+        self._dev = torch.empty(slot, dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        rc = L.pa_engine_create(self.bm._h, self.k_cache.data_ptr(), self.v_cache.data_ptr(),
+                                self.NB, self.H, self.D, self.bs, self.dt_code, self.max_batch,
+                                self.maxB, self.pad, self._host.data_ptr(), self.RING,
+                                self._dev.data_ptr(), ctypes.byref(h))
+        _check(rc, "pa_engine_create")
+        self._e = h
+        ws = int(L.pa_engine_workspace_bytes(self._e, self.partition_tokens))
+        # zero-filled once: the decode's per-row counters start at zero and
+        # every completed decode leaves them at zero
+        self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=self.device)
+        self._info = StepInfo()
+        self._seqs_cache = (None, None)
+        self.last_info = None
 
-    # ------------------------------------------------------------- views
-    def _views(self, buf, n):
-        B = self.max_batch
-        raw = buf.numpy() if buf.device.type == "cpu" else None
-        if raw is not None:
-            slots = raw[:8 * B].view(np.int64)[:n]
-            i32 = raw[8 * B:].view(np.int32)
-            ctx = i32[:B][:n]
-            cows = i32[B:3 * B]
-            tables = i32[3 * B:3 * B + B * self.maxB][:n * self.maxB].reshape(n, self.maxB)
-            return slots, ctx, cows, tables
-        slots = buf[:8 * B].view(self.torch.int64)[:n]
-        i32 = buf[8 * B:].view(self.torch.int32)
-        ctx = i32[:B][:n]
-        cows = i32[B:3 * B]
-        tables = i32[3 * B:3 * B + B * self.maxB][:n * self.maxB].view(n, self.maxB)
-        return slots, ctx, cows, tables
+    def __del__(self):
+        e = getattr(self, "_e", None)
+        if e is not None:
+            lib().pa_engine_destroy(e)
+            self._e = None
 
     # ------------------------------------------------------ cache building
     def add_sequence(self, seq, k=None, v=None, num_tokens=None):
@@ -106,54 +102,54 @@ class PagedKVEngine:
         return slots, cows
 
     # --------------------------------------------------------------- step
-    def step(self, seqs, q, k_new, v_new, scale, out=None, partition_tokens=0, timing=None,
-             two_launch=False):
-        """One decode step for ``seqs`` (int64 array): append a slot to each, ship the
+    def step(self, seqs, q, k_new, v_new, scale, out=None, stream=None):
+        """One decode step for ``seqs`` (distinct ids): append a slot to each, ship the
         tables, copy shared last blocks, write k_new/v_new [S, H, D], decode q [S, H, D].
-
-        ``timing`` (optional) = (start_event, end_event) recorded around the
-        decode launch.  ``two_launch`` uses pa_decode_partitions + pa_decode_reduce
-        instead of the single-launch pa_decode.  Returns out [S, H, D]."""
+        Returns out [S, H, D]."""
         torch = self.torch
-        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
-        S = seqs.size
-        assert S <= self.max_batch
-        i = self._ring
-        self._ring = (i + 1) % self.RING
-        if self._events[i] is not None:
-            self._events[i].synchronize()          # staging buffer i is free again
-        host = self._host[i]
-        h_slots, h_ctx, h_cows, h_tables = self._views(host, S)
-        ncow = self.bm.step_into(seqs, h_slots, h_cows, h_tables, self.pad, h_ctx)
-        max_ctx = int(h_ctx.max()) if S else 0
-        stream = torch.cuda.current_stream(self.device)
-        self._dev.copy_(host, non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        self._events[i] = ev
-        d_slots, d_ctx, d_cows, d_tables = self._views(self._dev, S)
-        if ncow:
-            copy_blocks(self.k_cache, self.v_cache, d_cows[:2 * ncow].view(ncow, 2))
-        cache_write(k_new, v_new, d_slots, self.k_cache, self.v_cache)
+        cached, arr = self._seqs_cache
+        if cached is not seqs:
+            arr = np.ascontiguousarray(seqs, dtype=np.int64)
+            self._seqs_cache = (seqs, arr)
+        S = arr.size
+        for t in (q, k_new, v_new):
+            if tuple(t.shape) != (S, self.H, self.D) or t.dtype != self.dtype or \
+                    not t.is_contiguous() or not t.is_cuda:
+                raise ValueError("q, k_new, v_new must be contiguous [S, H, D] device tensors")
         if out is None:
             out = torch.empty_like(q)
-        _, _, ws = decode_plan(S, self.H, self.D, self.bs, max_ctx, self.dt_code,
-                               partition_tokens)
-        if ws and (self._workspace is None or self._workspace.numel() < ws):
-            # zero-filled: pa_decode's per-row counters must start at zero
-            self._workspace = torch.zeros(ws, dtype=torch.uint8, device=self.device)
-        args = (q, self.k_cache, self.v_cache, d_tables, d_ctx, scale, max_ctx, out,
-                self._workspace, partition_tokens)
-        if timing is not None:
-            timing[0].record(stream)
-        if two_launch:
-            decode_partitions(*args)
-            decode_reduce(*args)
-        else:
-            decode(*args)
-        if timing is not None:
-            timing[1].record(stream)
-        self.last_step = dict(num_cow=ncow, max_ctx=max_ctx, ctx=h_ctx.copy(),
-                              cows=h_cows[:2 * ncow].reshape(-1, 2).copy(),
-                              slots=h_slots.copy())
+        st = (torch.cuda.current_stream(self.device) if stream is None else stream).cuda_stream
+        rc = lib().pa_engine_step(self._e, _ptr(arr), S, q.data_ptr(), k_new.data_ptr(),
+                                  v_new.data_ptr(), float(scale), out.data_ptr(),
+                                  self.workspace.data_ptr(), self.workspace.numel(),
+                                  self.partition_tokens, st, ctypes.byref(self._info))
+        _check(rc, "pa_engine_step")
+        self.last_info = self._info
         return out
+
+    def set_decode_events(self, start=None, end=None):
+        """Record torch.cuda.Event ``start``/``end`` around the decode launch of the
+        following steps (None = stop)."""
+        if start is None or end is None:
+            _check(lib().pa_engine_set_decode_events(self._e, None, None), "set events")
+            return
+        stream = self.torch.cuda.current_stream(self.device)
+        for ev in (start, end):
+            if ev.cuda_event == 0:     # torch creates the HIP event on first record
+                ev.record(stream)
+        _check(lib().pa_engine_set_decode_events(self._e, start.cuda_event, end.cuda_event),
+               "pa_engine_set_decode_events")
+
+    @property
+    def last_step(self):
+        """Host copies of the last step: dict(ctx, slots, cows, num_cow, ...)."""
+        info = self.last_info
+        S = self._seqs_cache[1].size
+        slots = np.empty(S, dtype=np.int64)
+        ctx = np.empty(S, dtype=np.int32)
+        cows = np.empty((max(info.num_cow, 1), 2), dtype=np.int32)
+        _check(lib().pa_engine_last_step(self._e, S, _ptr(slots), _ptr(ctx), _ptr(cows),
+                                         info.num_cow), "pa_engine_last_step")
+        return dict(ctx=ctx, slots=slots, cows=cows[:info.num_cow], num_cow=info.num_cow,
+                    max_ctx=info.max_context_len, partition_tokens=info.partition_tokens,
+                    num_items=info.num_items, sum_ctx=info.sum_context_len)

@@ -57,7 +57,8 @@ def run_gpu(wl, partition_tokens=0, fill_nan=True):
     tdt = torch_dtype(wl.dtype)
     eng = PagedKVEngine(wl.NB, wl.H, wl.D, wl.bs, tdt, wl.max_blocks_per_seq, wl.S,
                         free_order=wl.free_order, pad_block=wl.poison_block,
-                        fill=float("nan") if fill_nan else 0.0)
+                        fill=float("nan") if fill_nan else 0.0,
+                        partition_tokens=partition_tokens)
     out = None
     for op in wl.ops:
         if op[0] == "add":
@@ -81,7 +82,7 @@ def run_gpu(wl, partition_tokens=0, fill_nan=True):
                 vs.append(v[0])
             q = to_dev(wl.q, wl.dtype)
             out = eng.step(seqs, q, to_dev(np.stack(ks), wl.dtype), to_dev(np.stack(vs), wl.dtype),
-                           wl.scale, partition_tokens=partition_tokens)
+                           wl.scale)
     torch.cuda.synchronize()
     return dict(engine=eng, out=out)
 
