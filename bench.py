@@ -139,6 +139,9 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run 3 plain elementwise copies (neg) of this many MiB: a "
+                         "known-size reference for the HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
@@ -168,6 +171,17 @@ def main():
     out = torch.empty_like(q)
     eprint(f"setup {time.perf_counter() - t_setup:.1f} s: {wl.name}, S={S}, "
            f"sum(ctx)={int(wl.ctx.sum())}")
+
+    if args.copy_calibration_mib:
+        # a plain elementwise kernel that reads and writes exactly nbytes each
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 2, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        eprint(f"copy calibration: 3 elementwise kernels reading and writing {nbytes} bytes")
 
     for _ in range(args.warmup):
         eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
