@@ -16,7 +16,7 @@ import numpy as np
 __all__ = [
     "lib", "PAError", "cache_write", "copy_blocks", "decode", "decode_partitions",
     "decode_reduce", "decode_plan", "decode_workspace_size", "decode_schedule",
-    "decode_scheduled", "BlockManager",
+    "decode_scheduled", "decode_schedule_shared", "decode_scheduled_shared", "BlockManager",
     "DTYPE_CODES", "LIB_PATH",
 ]
 
@@ -41,6 +41,10 @@ _SIGNATURES = {
     "pa_decode_partitions": (_c.c_int, _DECODE_ARGS),
     "pa_decode_reduce": (_c.c_int, _DECODE_ARGS),
     "pa_decode_scheduled": (_c.c_int, _DECODE_ARGS + [_vp, _i32]),
+    "pa_decode_scheduled_shared": (_c.c_int, _DECODE_ARGS + [_vp, _i32, _vp, _i32, _vp]),
+    "pa_decode_schedule_shared": (_c.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                             _vp, _i32, _pi32, _vp, _i32, _pi32, _vp, _i32,
+                                             _pi32, _pi32, _pi32, _c.POINTER(_sz)]),
     "pa_decode_schedule": (_c.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _pi32,
                                       _pi32, _pi32]),
     "pa_decode_plan": (_c.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
@@ -71,13 +75,14 @@ _SIGNATURES = {
                                   _vp]),
     "pa_engine_last_step": (_c.c_int, [_vp, _i32, _vp, _vp, _vp, _i32]),
     "pa_engine_set_decode_events": (_c.c_int, [_vp, _vp, _vp]),
+    "pa_engine_set_sharing": (_c.c_int, [_vp, _i32]),
 }
 
 
 class StepInfo(_c.Structure):
     _fields_ = [("num_cow", _c.c_int32), ("max_context_len", _c.c_int32),
                 ("partition_tokens", _c.c_int32), ("num_items", _c.c_int32),
-                ("sum_context_len", _c.c_int64)]
+                ("num_group_items", _c.c_int32), ("sum_context_len", _c.c_int64)]
 
 
 class PAError(RuntimeError):
@@ -200,7 +205,8 @@ def decode_workspace_size(num_seqs, num_heads, head_dim, block_size, max_context
 
 
 def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale,
-                 max_context_len, out, workspace, partition_tokens, stream, extra=()):
+                 max_context_len, out, workspace, partition_tokens, stream, extra=(),
+                 ws_min_part=0):
     torch = _torch()
     S, H, D = q.shape
     NB, Hc, bs, Dc = k_cache.shape
@@ -219,6 +225,9 @@ def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale
             raise TypeError("q and the caches must share a dtype")
     dt = _dt(q)
     ws_need = decode_workspace_size(S, H, D, bs, int(max_context_len), dt, partition_tokens)
+    if ws_min_part:  # shared-prefix launches also use partitions of ws_min_part tokens
+        ws_need = max(ws_need, decode_workspace_size(S, H, D, bs, int(max_context_len), dt,
+                                                     ws_min_part))
     if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
         workspace = torch.zeros(ws_need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -235,7 +244,7 @@ def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale
 
 def decode_schedule(context_lens_host, num_heads, head_dim, block_size, dtype_code,
                     partition_tokens=0):
-    """Host work list for pa_decode_scheduled: (items int32 [n, 2], partition_tokens,
+    """Host work list for pa_decode_scheduled: (items int32 [n, 5], partition_tokens,
     max_context_len)."""
     ctx = np.ascontiguousarray(context_lens_host, dtype=np.int32)
     n, pt, mx = _c.c_int32(), _c.c_int32(), _c.c_int32()
@@ -244,7 +253,7 @@ def decode_schedule(context_lens_host, num_heads, head_dim, block_size, dtype_co
                                   _c.byref(pt), _c.byref(mx))
     if rc not in (PA_OK, -8):
         _check(rc, "pa_decode_schedule")
-    items = np.empty((max(n.value, 1), 2), dtype=np.int32)
+    items = np.empty((max(n.value, 1), 5), dtype=np.int32)
     rc = lib().pa_decode_schedule(_ptr(ctx), ctx.size, num_heads, head_dim, block_size,
                                   dtype_code, partition_tokens, _ptr(items), n.value,
                                   _c.byref(n), _c.byref(pt), _c.byref(mx))
@@ -252,9 +261,48 @@ def decode_schedule(context_lens_host, num_heads, head_dim, block_size, dtype_co
     return items[:n.value], pt.value, mx.value
 
 
+def decode_schedule_shared(context_lens_host, block_tables_host, num_heads, head_dim,
+                           block_size, dtype_code, partition_tokens=0):
+    """Host work lists with shared-prefix groups: dict(items [n,5], groups [g,5],
+    members [m,2], partition_tokens, max_context_len, workspace_bytes)."""
+    ctx = np.ascontiguousarray(context_lens_host, dtype=np.int32)
+    tab = np.ascontiguousarray(block_tables_host, dtype=np.int32)
+    S, W = tab.shape
+    cap = S * (-(-int(W) * block_size // 32) + 1)
+    items = np.empty((cap, 5), np.int32)
+    groups = np.empty((cap, 5), np.int32)
+    members = np.empty((max(S, 1), 2), np.int32)
+    n, ng, nm, pt, mx = (_c.c_int32() for _ in range(5))
+    ws = _c.c_size_t()
+    rc = lib().pa_decode_schedule_shared(
+        _ptr(ctx), _ptr(tab), W, S, num_heads, head_dim, block_size, dtype_code,
+        partition_tokens, _ptr(items), cap, _c.byref(n), _ptr(groups), cap, _c.byref(ng),
+        _ptr(members), members.shape[0], _c.byref(nm), _c.byref(pt), _c.byref(mx),
+        _c.byref(ws))
+    _check(rc, "pa_decode_schedule_shared")
+    return dict(items=items[:n.value].copy(), groups=groups[:ng.value].copy(),
+                members=members[:nm.value].copy(), partition_tokens=pt.value,
+                max_context_len=mx.value, workspace_bytes=ws.value)
+
+
+def decode_scheduled_shared(q, k_cache, v_cache, block_tables, context_lens, scale,
+                            max_context_len, items, groups, members, partition_tokens,
+                            out=None, workspace=None, stream=None):
+    """pa_decode over device work lists from decode_schedule_shared."""
+    torch = _torch()
+    n, ng = int(items.shape[0]), int(groups.shape[0])
+    return _decode_call("pa_decode_scheduled_shared", q, k_cache, v_cache, block_tables,
+                        context_lens, scale, max_context_len, out, workspace, partition_tokens,
+                        stream,
+                        extra=(_dev(items, "items", torch.int32) if n else None, n,
+                               _dev(groups, "groups", torch.int32) if ng else None, ng,
+                               _dev(members, "members", torch.int32) if ng else None),
+                        ws_min_part=256 if ng else 0)
+
+
 def decode_scheduled(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                      items, partition_tokens, out=None, workspace=None, stream=None):
-    """pa_decode over a device work list ``items`` [n, 2] int32 from decode_schedule."""
+    """pa_decode over a device work list ``items`` [n, 5] int32 from decode_schedule."""
     torch = _torch()
     n = int(items.shape[0])
     return _decode_call("pa_decode_scheduled", q, k_cache, v_cache, block_tables, context_lens,

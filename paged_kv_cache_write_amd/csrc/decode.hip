@@ -9,39 +9,39 @@
 // block_tables[s, t / bs] at offset t % bs.
 //
 // How (MI355X design, not taken from the pages):
-//  * The context of each (sequence, head) is cut into partitions of
-//    part_tokens tokens.  One wave (64 lanes) owns one (sequence, head,
-//    partition) from start to end; a workgroup packs kWaves waves for
-//    consecutive heads of the same (sequence, partition), which read the
-//    same table entries.  Partitions give the 256 CUs enough independent
-//    waves when there are few sequences or long contexts, and even out the
-//    work when context lengths differ.
+//  * A row (sequence, head) is cut into partitions (token ranges).  One wave
+//    (64 lanes) owns one (row, partition) from start to end; a workgroup is
+//    kWaves waves of consecutive heads.  Partitions give the 256 CUs enough
+//    independent waves and even out unequal context lengths.
 //  * A (block, head) tile is bs * D contiguous elements.  A lane owns a
-//    16-byte slice of one token row, so one wave-wide load instruction reads
-//    64 x 16 B = 1 KiB of consecutive bytes of one tile: fully coalesced.
-//    Each lane consumes exactly the bytes it loaded, so K/V go from HBM
-//    straight to registers; there is no LDS staging and no barrier.
+//    16-byte slice of one token row, so one wave-wide load reads 64 x 16 B =
+//    1 KiB of consecutive bytes of one tile: fully coalesced.  Each lane
+//    consumes exactly the bytes it loaded, so K/V go from HBM to registers;
+//    there is no LDS staging and no barrier.
 //  * A wave works on chunks of U load instructions for K and U for V issued
-//    back to back, so each lane has 2U 16-byte loads in flight.
+//    back to back (non-temporal: K/V are read once).
 //  * q.k partial dots use v_dot2_f32_{f16,bf16} (exact products, float32
 //    sums); the lanes of one token row are summed with DPP butterflies; the
 //    softmax is the online (running max / running sum) form in base 2 with
 //    scale*log2(e) folded into the logit; P.V accumulates in float32
 //    (v_fma_mix_f32 for fp16).
 //  * The partition's table entries are loaded once per wave into one VGPR
-//    (lane j = j-th block of the partition), in parallel with the context
-//    length, and read with v_readlane, so a block's address is wave-uniform
-//    scalar arithmetic.
+//    (lane j = j-th block of the partition) and read with v_readlane, so a
+//    block's address is wave-uniform scalar arithmetic.
+//  * Shared prefixes (comfyai.app 6.4.2-6.4.3: sequences map logical blocks
+//    to the same physical blocks): a group wave streams each shared tile
+//    once and runs up to kGroup queries of the sharing sequences against it.
 //  * A wave merges (max, sum, accumulator) across its token rows with
-//    shuffles.  A sequence with one partition stores its output row
-//    directly.  Otherwise the partial (max, sum, normalised output) goes to
-//    the workspace and the partitions are merged with the log-sum-exp rule:
-//    by the last wave to finish that (sequence, head) (pa_decode, one launch,
-//    an agent-scope counter per row), or by a second kernel
-//    (pa_decode_partitions + pa_decode_reduce).
+//    shuffles.  A row with one partition is stored directly.  Otherwise the
+//    partial (max, sum, normalised output) goes to the workspace and the
+//    partitions are merged with the log-sum-exp rule: by the last wave to
+//    finish the row (one launch, an agent-scope counter per row), or by a
+//    second kernel (pa_decode_partitions + pa_decode_reduce).
 #include <algorithm>
+#include <unordered_map>
 #include <vector>
 
+#include "internal.hpp"
 #include "launch_common.hpp"
 #include "pa_device.hpp"
 
@@ -55,8 +55,19 @@ namespace pa {
 #endif
 constexpr int kWaves = PA_DECODE_WAVES;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
+constexpr int kUnroll = PA_DECODE_UNROLL;  // 16-byte K loads (and V loads) per lane per chunk
+constexpr int kGroup = 8;                  // queries per group wave
+constexpr int kGroupUnroll = 4;            // chunk of a group wave (register budget)
+constexpr int kSharedPartTokens = 256;     // partition of a shared range
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so max - max never is NaN
+
+// Scheduled work items (int32 fields):
+//   single item [5]: sequence, partition index, first token, tokens, partitions of the row
+//   group item  [5]: first member, member count, partition index, first token, tokens
+//   member      [2]: sequence, partitions of its rows
+constexpr int kItemInts = 5;
+constexpr int kMemberInts = 2;
 
 struct DecodeParams {
   const void* q;
@@ -68,13 +79,16 @@ struct DecodeParams {
   float* ws_ml;  // [S, H, max_parts, 2]: running max (log2 units), sum
   float* ws_o;   // [S, H, max_parts, D]: partition output normalised by its sum
   int* counters; // [S, H] partitions finished; NULL = leave the merge to the reduce kernel
-  const int32_t* items;  // [n, 2] (sequence, partition) in launch order; NULL = grid order
+  const int32_t* items;          // single items in launch order; NULL = grid order
+  const int32_t* group_items;    // group items
+  const int32_t* group_members;  // members of the group items
   int H;
   int maxB;
   int log2_bs;
-  int part_tokens;
-  int max_parts;
-  float qk_scale;  // scale * log2(e)
+  int part_tokens;    // partition of the grid order
+  int window_tokens;  // partition window of the launch (table entries loaded per wave)
+  int max_parts;      // partition stride of the workspace
+  float qk_scale;     // scale * log2(e)
 };
 
 template <class DT, int D, int U>
@@ -117,19 +131,15 @@ struct ChunkCtx {
   float qk_scale;
 };
 
-// One chunk of U token-row groups: issue 2U 16-byte loads (K and V), then
-// q.k, online softmax update and P.V.  kMasked is the partition's last,
-// partial chunk: its loads are clamped to rows of groups that hold valid
-// tokens (so no extra memory is touched and no table entry past the
-// sequence is read) and the loaded values of invalid tokens are zeroed.
+// Issue the 2U 16-byte loads (K and V) of one chunk.  kMasked is the
+// partition's last, partial chunk: its loads are clamped to rows of groups
+// that hold valid tokens (no extra memory is touched and no table entry past
+// the partition is used) and ok[] marks the valid rows.
 template <class DT, int D, int U, bool kMasked>
-__device__ __forceinline__ void chunk_step(const ChunkCtx& cx, int t0, u32x4 qv, float& m,
-                                           float& l, float* acc) {
+__device__ __forceinline__ void chunk_load(const ChunkCtx& cx, int t0, u32x4 (&kr)[U],
+                                           u32x4 (&vr)[U], bool (&ok)[U]) {
   using Sh = Shape<DT, D, U>;
-  constexpr int kVec = DT::kVec;
   constexpr uint32_t kRowBytes = uint32_t(D) * sizeof(typename DT::T);
-  u32x4 kr[U], vr[U];
-  bool ok[U];
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     int tt = t0 + i * Sh::kTPI;  // wave-uniform token offset in the partition
@@ -151,16 +161,26 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& cx, int t0, u32x4 qv,
   // fence the scheduler interleaves the dot products with the loads to save
   // registers, which serialises the memory latency.
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kMasked) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) vr[i] = ok[i] ? vr[i] : u32x4{0, 0, 0, 0};
+  }
+}
+
+// q.k, online softmax update and P.V of one query over one loaded chunk.
+template <class DT, int D, int U, bool kMasked>
+__device__ __forceinline__ void chunk_apply(const ChunkCtx& cx, const u32x4 (&kr)[U],
+                                            const u32x4 (&vr)[U], const bool (&ok)[U], u32x4 qv,
+                                            float& m, float& l, float* acc) {
+  using Sh = Shape<DT, D, U>;
+  constexpr int kVec = DT::kVec;
   float sc[U];
   float mx = kNegBig;
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     const float d = group_sum<Sh::kLPT>(dot16(DT{}, kr[i], qv, 0.f));
     sc[i] = d * cx.qk_scale;
-    if constexpr (kMasked) {
-      sc[i] = ok[i] ? sc[i] : -__builtin_inff();
-      vr[i] = ok[i] ? vr[i] : u32x4{0, 0, 0, 0};
-    }
+    if constexpr (kMasked) sc[i] = ok[i] ? sc[i] : -__builtin_inff();
     mx = fmaxf(mx, sc[i]);
   }
   const float mn = fmaxf(m, mx);
@@ -175,6 +195,24 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& cx, int t0, u32x4 qv,
     axpy16(DT{}, acc, vr[i], p);
   }
   m = mn;
+}
+
+// Merge the token rows of a wave (lanes with equal col): afterwards every
+// lane holds the wave's (max, sum, accumulator) for its columns.
+template <class DT, int D, int U>
+__device__ __forceinline__ void merge_rows(float& m, float& l, float* acc) {
+  using Sh = Shape<DT, D, U>;
+#pragma unroll
+  for (int off = Sh::kLPT; off < kWave; off <<= 1) {
+    const float mo = __shfl_xor(m, off, kWave);
+    const float lo = __shfl_xor(l, off, kWave);
+    const float mn = fmaxf(m, mo);
+    const float a = fast_exp2(m - mn), b = fast_exp2(mo - mn);
+    l = l * a + lo * b;
+#pragma unroll
+    for (int e = 0; e < DT::kVec; ++e) acc[e] = acc[e] * a + __shfl_xor(acc[e], off, kWave) * b;
+    m = mn;
+  }
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, head) row by one
@@ -251,10 +289,124 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, size_t row
   for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, O[e] / L);
 }
 
-// One wave owns one (sequence, head, partition) from start to end; a
-// workgroup is kWaves independent waves for kWaves consecutive heads of the
-// same (sequence, partition), which read the same table entries.  No LDS and
-// no barrier: a wave merges its token rows with shuffles and stores its row.
+// End of a (row, partition) for the NQ queries of one wave (rows row_id[g],
+// nparts[g]; the wave's token rows are already merged).  A row with one
+// partition is stored directly.  Otherwise the partial goes to the
+// workspace; in the one-launch form the partials are then counted: the
+// partial stores are complete (s_waitcnt) before the counter increments are
+// issued, and the wave whose increment returns the count of all the others
+// merges that row (after its increment returned, so every partial is
+// visible) and resets its counter.  Partials and counters are exchanged only
+// through agent-scope atomic accesses, coherent across the XCDs' L2s without
+// cache-wide write-back/invalidate fences.
+template <class DT, int D, int U, int NQ>
+__device__ __forceinline__ void finish(const DecodeParams& P, const size_t (&row_id)[NQ],
+                                       const int (&nparts)[NQ], int nq, int part,
+                                       const float (&m)[NQ], const float (&l)[NQ],
+                                       const float (&acc)[NQ][DT::kVec], int lane) {
+  using T = typename DT::T;
+  using Sh = Shape<DT, D, U>;
+  constexpr int kVec = DT::kVec;
+  const int row = lane / Sh::kLPT;
+  const int col = lane % Sh::kLPT;
+  const bool fused = P.counters != nullptr;
+  bool any_split = false;
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
+    if (g >= nq) break;
+    const float inv = 1.0f / l[g];  // l >= 1: the running max token contributes 2^0
+    if (nparts[g] <= 1) {
+      if (row == 0) {
+        T* o = reinterpret_cast<T*>(P.out) + row_id[g] * D + col * kVec;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, acc[g][e] * inv);
+      }
+      continue;
+    }
+    any_split = true;
+    if (row != 0) continue;
+    const size_t pi = row_id[g] * P.max_parts + part;
+    float* o = P.ws_o + pi * D + col * kVec;
+    if (fused) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e)
+        __hip_atomic_store(o + e, acc[g][e] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (col == 0) {
+        __hip_atomic_store(P.ws_ml + 2 * pi, m[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(P.ws_ml + 2 * pi + 1, l[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) o[e] = acc[g][e] * inv;
+      if (col == 0) {
+        P.ws_ml[2 * pi] = m[g];
+        P.ws_ml[2 * pi + 1] = l[g];
+      }
+    }
+  }
+  if (!fused || !any_split) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // all counters zero: this wave's stores are complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // lane g increments query g's row counter
+  int target = 0;
+  size_t my_row = 0;
+#pragma unroll
+  for (int g = 0; g < NQ; ++g)
+    if (lane == g && g < nq && nparts[g] > 1) {
+      my_row = row_id[g];
+      target = nparts[g] - 1;
+    }
+  int prev = -1;
+  if (target > 0)
+    prev = __hip_atomic_fetch_add(P.counters + my_row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int last = (target > 0 && prev == target) ? 1 : 0;
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
+    if (g >= nq) break;
+    if (!__shfl(last, g, kWave)) continue;  // wave-uniform
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0)  // every partition of this row has counted: reset for the next call
+      __hip_atomic_store(P.counters + row_id[g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_partials<DT, D, U>(P, row_id[g], nparts[g], lane);
+  }
+}
+
+// Table entries of a partition window, one per lane, and the chunk context.
+template <class DT, int D, int U>
+__device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h, int t0,
+                                             int lane) {
+  using Sh = Shape<DT, D, U>;
+  constexpr uint32_t kRowBytes = uint32_t(D) * sizeof(typename DT::T);
+  constexpr int kLog2Row = __builtin_ctz(kRowBytes);
+  const int row = lane / Sh::kLPT;
+  const int col = lane % Sh::kLPT;
+  const int blk0 = t0 >> P.log2_bs;
+  // The whole window is loaded speculatively, in parallel with what decides
+  // its length: entries past the partition are loaded as integers but never
+  // used as addresses.
+  int tbl = 0;
+  if (lane < (P.window_tokens >> P.log2_bs) && blk0 + lane < P.maxB)
+    tbl = P.block_tables[size_t(s) * P.maxB + blk0 + lane];
+  ChunkCtx cx;
+  cx.kc = reinterpret_cast<const char*>(P.k_cache);
+  cx.vc = reinterpret_cast<const char*>(P.v_cache);
+  cx.log2_tile = kLog2Row + P.log2_bs;
+  cx.H = P.H;
+  cx.h = h;
+  cx.lane_off = uint32_t(row) * kRowBytes + uint32_t(col) * 16u;
+  cx.tbl = tbl;
+  cx.log2_bs = P.log2_bs;
+  cx.bs_mask = (1 << P.log2_bs) - 1;
+  cx.row = row;
+  cx.ntok = 0;
+  cx.last_group = 0;
+  cx.qk_scale = P.qk_scale;
+  return cx;
+}
+
+// One wave per (sequence, head, partition): grid order from context_lens, or
+// a host-scheduled work list of single items.
 template <class DT, int D, int U>
 __global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
   using T = typename DT::T;
@@ -263,125 +415,147 @@ __global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
   constexpr size_t kRowBytes = size_t(D) * sizeof(T);
 
   const int wave = wave_uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
   const int H = P.H;
-  int hg = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
+  const int ngroups = (H + kWaves - 1) / kWaves;
+  int hg, part, s, t0;
+  const int32_t* it = nullptr;
   if (P.items != nullptr) {  // scheduled launch: x = item * head_groups + head group
-    const int ngroups = (H + kWaves - 1) / kWaves;
     const int item = blockIdx.x / ngroups;
     hg = blockIdx.x - item * ngroups;
-    s = P.items[2 * item];
-    part = P.items[2 * item + 1];
+    it = P.items + kItemInts * item;
+    s = it[0];
+    part = it[1];
+    t0 = it[2];
+  } else {
+    hg = blockIdx.x;
+    part = blockIdx.y;
+    s = blockIdx.z;
+    t0 = part * P.part_tokens;
   }
   const int h = hg * kWaves + wave;
   if (h >= H) return;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int log2_bs = P.log2_bs;
   const size_t row_id = size_t(s) * H + h;
-
+  ChunkCtx cx = make_ctx<DT, D, U>(P, s, h, t0, lane);
+  int ntok, nparts;
+  if (it != nullptr) {
+    ntok = it[3];
+    nparts = it[4];
+  } else {
+    int ctx = P.context_lens[s];
+    // never read past the table row or past the launched partitions
+    ctx = min(ctx, min(P.maxB << P.log2_bs, P.max_parts * P.part_tokens));
+    nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
+    ntok = part < nparts ? min(P.part_tokens, ctx - t0) : 0;
+  }
   const int row = lane / Sh::kLPT;
   const int col = lane % Sh::kLPT;
-  const int p0 = part * P.part_tokens;
-  const int blk0 = p0 >> log2_bs;
-  // The table entries of the whole partition window are read together with
-  // the context length (entries past the context are loaded as integers but
-  // never used as addresses), so the K/V loads wait for one round trip only.
-  int tbl = 0;
-  if (lane < (P.part_tokens >> log2_bs) && blk0 + lane < P.maxB)
-    tbl = P.block_tables[size_t(s) * P.maxB + blk0 + lane];
-  int ctx = P.context_lens[s];
-  ctx = min(ctx, min(P.maxB << log2_bs, P.max_parts * P.part_tokens));
-  const int nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
-  if (part >= nparts) {
-    if (part == 0 && row == 0) {  // empty context: zero output row
+  if (ntok <= 0) {
+    if (part == 0 && nparts == 0 && row == 0) {  // empty context: zero output row
       T* o = reinterpret_cast<T*>(P.out) + row_id * D + col * kVec;
 #pragma unroll
       for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, 0.f);
     }
     return;
   }
-  const int ntok = min(P.part_tokens, ctx - p0);
+  cx.ntok = ntok;
+  cx.last_group = (ntok - 1) & ~(Sh::kTPI - 1);
   const u32x4 qv = load16(reinterpret_cast<const char*>(P.q) + row_id * kRowBytes + col * 16);
 
-  constexpr int kLog2Row = __builtin_ctz(unsigned(kRowBytes));
-  const uint32_t lane_off = uint32_t(row) * uint32_t(kRowBytes) + uint32_t(col) * 16u;
-  ChunkCtx cx{reinterpret_cast<const char*>(P.k_cache), reinterpret_cast<const char*>(P.v_cache),
-              kLog2Row + log2_bs, H, h, lane_off, tbl,
-              log2_bs, (1 << log2_bs) - 1, row, ntok, (ntok - 1) & ~(Sh::kTPI - 1), P.qk_scale};
-
-  float m = kNegBig, l = 0.f;
-  float acc[kVec];
+  float m[1] = {kNegBig}, l[1] = {0.f};
+  float acc[1][kVec];
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) acc[e] = 0.f;
+  for (int e = 0; e < kVec; ++e) acc[0][e] = 0.f;
   const int nfull = ntok / Sh::kChunk;
   int c = 0;
-  for (; c < nfull; ++c) chunk_step<DT, D, U, false>(cx, c * Sh::kChunk, qv, m, l, acc);
-  if (c * Sh::kChunk < ntok) chunk_step<DT, D, U, true>(cx, c * Sh::kChunk, qv, m, l, acc);
-
-#pragma unroll
-  for (int off = Sh::kLPT; off < kWave; off <<= 1) {
-    const float mo = __shfl_xor(m, off, kWave);
-    const float lo = __shfl_xor(l, off, kWave);
-    const float mn = fmaxf(m, mo);
-    const float a = fast_exp2(m - mn), b = fast_exp2(mo - mn);
-    l = l * a + lo * b;
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) acc[e] = acc[e] * a + __shfl_xor(acc[e], off, kWave) * b;
-    m = mn;
+  for (; c < nfull; ++c) {
+    u32x4 kr[U], vr[U];
+    bool ok[U];
+    chunk_load<DT, D, U, false>(cx, c * Sh::kChunk, kr, vr, ok);
+    chunk_apply<DT, D, U, false>(cx, kr, vr, ok, qv, m[0], l[0], acc[0]);
   }
-  const float inv = 1.0f / l;  // l >= 1: the running max token contributes 2^0
-  if (nparts == 1) {
-    if (row != 0) return;
-    T* o = reinterpret_cast<T*>(P.out) + row_id * D + col * kVec;
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, acc[e] * inv);
-    return;
+  if (c * Sh::kChunk < ntok) {
+    u32x4 kr[U], vr[U];
+    bool ok[U];
+    chunk_load<DT, D, U, true>(cx, c * Sh::kChunk, kr, vr, ok);
+    chunk_apply<DT, D, U, true>(cx, kr, vr, ok, qv, m[0], l[0], acc[0]);
   }
-  const size_t pi0 = row_id * P.max_parts;
-  if (P.counters == nullptr) {  // two-launch form: the reduce kernel merges
-    if (row == 0) {
-      float* o = P.ws_o + (pi0 + part) * D + col * kVec;
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) o[e] = acc[e] * inv;
-      if (col == 0) {
-        P.ws_ml[2 * (pi0 + part)] = m;
-        P.ws_ml[2 * (pi0 + part) + 1] = l;
-      }
-    }
-    return;
-  }
-  // Fused merge: the wave that finishes a (sequence, head) last merges all of
-  // its partitions.  Partials and the counter are exchanged only through
-  // agent-scope atomic accesses, which are coherent across the XCDs' L2s
-  // without cache-wide write-back/invalidate fences: the partial stores are
-  // complete (s_waitcnt) before this wave's counter increment is issued, and
-  // the merging wave issues its partial loads only after its increment
-  // returned the count of all the others.
-  if (row == 0) {
-    float* o = P.ws_o + (pi0 + part) * D + col * kVec;
-#pragma unroll
-    for (int e = 0; e < kVec; ++e)
-      __hip_atomic_store(o + e, acc[e] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (col == 0) {
-      __hip_atomic_store(P.ws_ml + 2 * (pi0 + part), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(P.ws_ml + 2 * (pi0 + part) + 1, l, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);  // all counters zero: this wave's stores are complete
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  int prev = 0;
-  if (lane == 0)
-    prev = __hip_atomic_fetch_add(P.counters + row_id, 1, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0, kWave);
-  if (prev != nparts - 1) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (lane == 0)  // every partition has counted: reset for the next call
-    __hip_atomic_store(P.counters + row_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  merge_partials<DT, D, U>(P, row_id, nparts, lane);
+  merge_rows<DT, D, U>(m[0], l[0], acc[0]);
+  const size_t rows[1] = {row_id};
+  const int nps[1] = {nparts};
+  finish<DT, D, U, 1>(P, rows, nps, 1, part, m, l, acc, lane);
 }
 
+// One wave per (group of sequences sharing a prefix, head, shared partition):
+// the shared tiles are streamed once for up to kGroup queries.  The members
+// share the physical blocks of this partition, so the first member's table
+// row addresses them for all.
+template <class DT, int D, int U>
+__global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeParams P) {
+  using T = typename DT::T;
+  using Sh = Shape<DT, D, U>;
+  constexpr int kVec = DT::kVec;
+  constexpr size_t kRowBytes = size_t(D) * sizeof(T);
+
+  const int wave = wave_uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int H = P.H;
+  const int ngroups = (H + kWaves - 1) / kWaves;
+  const int item = blockIdx.x / ngroups;
+  const int hg = blockIdx.x - item * ngroups;
+  const int h = hg * kWaves + wave;
+  if (h >= H) return;
+  const int32_t* it = P.group_items + kItemInts * item;
+  const int moff = it[0];
+  const int nq = min(int(it[1]), kGroup);
+  const int part = it[2];
+  const int t0 = it[3];
+  const int ntok = it[4];
+  const int32_t* mem = P.group_members + kMemberInts * moff;
+  ChunkCtx cx = make_ctx<DT, D, U>(P, mem[0], h, t0, lane);
+  if (ntok <= 0 || nq <= 0) return;
+  cx.ntok = ntok;
+  cx.last_group = (ntok - 1) & ~(Sh::kTPI - 1);
+  const int col = lane % Sh::kLPT;
+
+  size_t rows[kGroup];
+  int nps[kGroup];
+  u32x4 qv[kGroup];
+  float m[kGroup], l[kGroup], acc[kGroup][kVec];
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g) {
+    const int gi = g < nq ? g : 0;
+    rows[g] = size_t(mem[kMemberInts * gi]) * H + h;
+    nps[g] = mem[kMemberInts * gi + 1];
+    qv[g] = load16(reinterpret_cast<const char*>(P.q) + rows[g] * kRowBytes + col * 16);
+    m[g] = kNegBig;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc[g][e] = 0.f;
+  }
+  const int nfull = ntok / Sh::kChunk;
+  int c = 0;
+  for (; c < nfull; ++c) {
+    u32x4 kr[U], vr[U];
+    bool ok[U];
+    chunk_load<DT, D, U, false>(cx, c * Sh::kChunk, kr, vr, ok);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+      if (g < nq) chunk_apply<DT, D, U, false>(cx, kr, vr, ok, qv[g], m[g], l[g], acc[g]);
+  }
+  if (c * Sh::kChunk < ntok) {
+    u32x4 kr[U], vr[U];
+    bool ok[U];
+    chunk_load<DT, D, U, true>(cx, c * Sh::kChunk, kr, vr, ok);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+      if (g < nq) chunk_apply<DT, D, U, true>(cx, kr, vr, ok, qv[g], m[g], l[g], acc[g]);
+  }
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g)
+    if (g < nq) merge_rows<DT, D, U>(m[g], l[g], acc[g]);
+  finish<DT, D, U, kGroup>(P, rows, nps, nq, part, m, l, acc, lane);
+}
 
 // Second launch of the two-launch form: one wave per (sequence, head) row.
 template <class DT, int D, int U>
@@ -396,8 +570,6 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams P) {
 }
 
 // ------------------------------------------------------------------ host side
-constexpr int kUnroll = PA_DECODE_UNROLL;  // 16-byte K loads (and V loads) per lane per chunk
-
 constexpr int64_t kSchedTargetWaves = 1536;  // 256 CUs x 6
 
 struct Plan {
@@ -411,17 +583,20 @@ static size_t counter_bytes(int32_t S, int32_t H) {
   return (size_t(S) * H * sizeof(int) + 255) & ~size_t(255);
 }
 
-static int chunk_tokens(int32_t head_dim, int32_t dtype) {
-  const int vec = 16 / elem_bytes(dtype);
-  return (kWave / (head_dim / vec)) * kUnroll;
+static size_t ws_bytes_for(int32_t S, int32_t H, int32_t D, int max_parts) {
+  return max_parts > 1
+             ? counter_bytes(S, H) + size_t(S) * H * max_parts * (size_t(D) + 2) * sizeof(float)
+             : 0;
 }
 
 // Context-partition size.  Requested sizes must be multiples of 32 and of the
 // block size and span at most 64 blocks.  The automatic choice keeps
 // partitions short (better balance across CUs) unless the launch already has
-// many workgroups.
+// many waves.  `min_part` (0 = none) is a smaller partition also used in the
+// launch (shared prefixes): the workspace stride then counts partitions of
+// that size.
 static int make_plan(int32_t S, int32_t H, int32_t D, int32_t bs, int32_t max_ctx,
-                     int32_t dtype, int32_t requested, Plan* plan) {
+                     int32_t dtype, int32_t requested, Plan* plan, int min_part = 0) {
   int rc = check_shape(D, bs, dtype);
   if (rc != PA_OK) return rc;
   if (S < 0 || H <= 0 || max_ctx < 0 || requested < 0) return PA_ERR_INVALID;
@@ -431,7 +606,7 @@ static int make_plan(int32_t S, int32_t H, int32_t D, int32_t bs, int32_t max_ct
   if (pt == 0) {
     const int64_t rows = int64_t(S) * H;
     pt = 256;
-    // Larger partitions once there are plenty of workgroups anyway.
+    // Larger partitions once there are plenty of waves anyway.
     while (pt * 2 <= max_tokens && pt < 1024 &&
            rows * ((int64_t(max_ctx) + 2 * pt - 1) / (2 * pt)) >= 16384)
       pt *= 2;
@@ -440,59 +615,69 @@ static int make_plan(int32_t S, int32_t H, int32_t D, int32_t bs, int32_t max_ct
   } else {
     if (pt % 32 != 0 || pt % bs != 0 || pt > max_tokens) return PA_ERR_INVALID;
   }
-  (void)chunk_tokens;
-  const int parts = max_ctx == 0 ? 1 : (max_ctx + pt - 1) / pt;
+  const int stride_part = (min_part > 0 && min_part < pt) ? min_part : pt;
+  const int parts = max_ctx == 0 ? 1 : (max_ctx + stride_part - 1) / stride_part;
   plan->part_tokens = pt;
   plan->max_parts = parts;
-  plan->ws_bytes = parts > 1 ? counter_bytes(S, H) + size_t(S) * H * parts * (size_t(D) + 2) * sizeof(float)
-                             : 0;
+  plan->ws_bytes = ws_bytes_for(S, H, D, parts);
   return PA_OK;
 }
 
+enum class Launch { kSingles, kGroups, kReduce };
+
 template <class DT, int D>
-static void launch_partitions(const DecodeParams& p, int S, int num_items, hipStream_t st) {
+static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t st) {
   const int ngroups = (p.H + kWaves - 1) / kWaves;
-  const dim3 grid = p.items ? dim3(unsigned(num_items) * unsigned(ngroups), 1, 1)
-                            : dim3(ngroups, p.max_parts, S);
-  hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
-}
-
-template <class DT, int D>
-static void launch_reduce(const DecodeParams& p, int S, int, hipStream_t st) {
-  dim3 grid(p.H, S);
-  hipLaunchKernelGGL((decode_reduce_kernel<DT, D, kUnroll>), grid, dim3(kWave), 0, st, p);
-}
-
-template <bool kPartitions>
-static void dispatch(int32_t dtype, int32_t D, const DecodeParams& p, int S, int n_items,
-                     hipStream_t st) {
-#define PA_LAUNCH(DT_, D_)                               \
-  do {                                                   \
-    if (kPartitions)                                     \
-      launch_partitions<DT_, D_>(p, S, n_items, st);     \
-    else                                                 \
-      launch_reduce<DT_, D_>(p, S, n_items, st);         \
-  } while (0)
-  if (dtype == PA_F32) {
-    if (D == 64) PA_LAUNCH(F32, 64); else PA_LAUNCH(F32, 128);
-  } else if (dtype == PA_F16) {
-    if (D == 64) PA_LAUNCH(F16, 64); else PA_LAUNCH(F16, 128);
-  } else {
-    if (D == 64) PA_LAUNCH(BF16, 64); else PA_LAUNCH(BF16, 128);
+  switch (what) {
+    case Launch::kGroups:
+      hipLaunchKernelGGL((decode_group_kernel<DT, D, kGroupUnroll>),
+                         dim3(unsigned(n) * unsigned(ngroups)), dim3(kThreads), 0, st, p);
+      break;
+    case Launch::kSingles: {
+      const dim3 grid = p.items ? dim3(unsigned(n) * unsigned(ngroups), 1, 1)
+                                : dim3(ngroups, p.max_parts, S);
+      hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
+      break;
+    }
+    case Launch::kReduce:
+      hipLaunchKernelGGL((decode_reduce_kernel<DT, D, kUnroll>), dim3(p.H, S), dim3(kWave), 0,
+                         st, p);
+      break;
   }
-#undef PA_LAUNCH
+}
+
+static void dispatch(Launch what, int32_t dtype, int32_t D, const DecodeParams& p, int S, int n,
+                     hipStream_t st) {
+  if (dtype == PA_F32) {
+    if (D == 64) launch<F32, 64>(what, p, S, n, st); else launch<F32, 128>(what, p, S, n, st);
+  } else if (dtype == PA_F16) {
+    if (D == 64) launch<F16, 64>(what, p, S, n, st); else launch<F16, 128>(what, p, S, n, st);
+  } else {
+    if (D == 64) launch<BF16, 64>(what, p, S, n, st); else launch<BF16, 128>(what, p, S, n, st);
+  }
 }
 
 enum { kDoPartitions = 1, kDoReduce = 2, kFused = 4 };
+
+struct Schedule {
+  bool scheduled = false;  // work lists given (else grid order)
+  const int32_t* items = nullptr;
+  int32_t num_items = 0;
+  const int32_t* group_items = nullptr;
+  int32_t num_group_items = 0;
+  const int32_t* group_members = nullptr;
+};
 
 static int decode_impl(int what, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, int32_t maxB, const int32_t* context_lens,
                        int32_t S, int32_t H, int32_t D, int32_t bs, int64_t NB, float scale,
                        int32_t max_ctx, int32_t dtype, void* out, void* workspace,
                        size_t workspace_bytes, int32_t partition_tokens, void* stream,
-                       const int32_t* items = nullptr, int32_t num_items = 0) {
+                       const Schedule& sched = Schedule()) {
   Plan plan;
-  int rc = make_plan(S, H, D, bs, max_ctx, dtype, partition_tokens, &plan);
+  const bool shared = sched.num_group_items > 0;
+  int rc = make_plan(S, H, D, bs, max_ctx, dtype, partition_tokens, &plan,
+                     shared ? kSharedPartTokens : 0);
   if (rc != PA_OK) return rc;
   if (S == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_INVALID;
@@ -500,6 +685,7 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   if (uint64_t(NB) * uint64_t(H) > 0xFFFFFFFFull) return PA_ERR_UNSUPPORTED;  // 32-bit tile index
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return PA_ERR_INVALID;
+  if (shared && (kSharedPartTokens % bs != 0 || !sched.group_members)) return PA_ERR_INVALID;
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_INVALID;
@@ -516,24 +702,161 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.counters = (split && (what & kFused)) ? reinterpret_cast<int*>(ws) : nullptr;
   p.ws_ml = split ? reinterpret_cast<float*>(ws + counter_bytes(S, H)) : nullptr;
   p.ws_o = split ? p.ws_ml + size_t(S) * H * plan.max_parts * 2 : nullptr;
+  p.items = sched.items;
+  p.group_items = sched.group_items;
+  p.group_members = sched.group_members;
   p.H = H;
   p.maxB = maxB;
   p.log2_bs = log2_exact(bs);
   p.part_tokens = plan.part_tokens;
+  p.window_tokens = plan.part_tokens;
   p.max_parts = plan.max_parts;
   p.qk_scale = scale * kLog2e;
+  if (shared && !p.counters) return PA_ERR_INVALID;  // groups need the one-launch merge
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  p.items = items;
-  if (items && num_items <= 0) {
-    // empty schedule: nothing to attend to, but ctx = 0 rows still need zeros;
-    // fall back to grid order, whose empty partitions exit at once
-    p.items = nullptr;
+  if (what & kDoPartitions) {
+    if (shared) {
+      DecodeParams pg = p;
+      pg.window_tokens = kSharedPartTokens;
+      dispatch(Launch::kGroups, dtype, D, pg, S, sched.num_group_items, st);
+    }
+    if (!sched.scheduled) {
+      dispatch(Launch::kSingles, dtype, D, p, S, 0, st);
+    } else if (sched.num_items > 0 && sched.items) {
+      dispatch(Launch::kSingles, dtype, D, p, S, sched.num_items, st);
+    }
   }
-  if (what & kDoPartitions) dispatch<true>(dtype, D, p, S, num_items, st);
   if ((what & kDoReduce) && !(what & kFused) && plan.max_parts > 1)
-    dispatch<false>(dtype, D, p, S, num_items, st);
+    dispatch(Launch::kReduce, dtype, D, p, S, 0, st);
   return launch_status();
+}
+
+// ---- host schedule -------------------------------------------------------
+
+// Work of one decode, built on the host from the context lengths (and, when
+// the block tables are given, the shared prefixes):
+//  * Sequences whose tables start with the same physical blocks share those
+//    blocks' K/V ([C] 6.4.2-6.4.3).  A group (up to kGroup members per group
+//    item) covers the longest run of shared blocks common to its members, in
+//    partitions of kSharedPartTokens, with one group item per partition.
+//  * Every sequence's remaining tokens are cut into partitions of
+//    part_tokens.  Single items are ordered longest first: every full
+//    partition, then the partial last partitions from longest to shortest,
+//    then one item per empty sequence (which only zeroes its row).
+int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t bs,
+                   int32_t dtype, int32_t requested, const int32_t* tables, int32_t maxB,
+                   HostSchedule* hs) {
+  int rc = check_shape(D, bs, dtype);
+  if (rc != PA_OK) return rc;
+  if (!ctx || S < 0 || H <= 0 || (tables && maxB <= 0)) return PA_ERR_INVALID;
+  int32_t max_ctx = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    if (ctx[s] < 0) return PA_ERR_INVALID;
+    max_ctx = std::max(max_ctx, ctx[s]);
+  }
+  std::vector<int32_t> shared(static_cast<size_t>(S), 0);
+  std::vector<std::vector<int32_t>> groups;
+  if (tables && kSharedPartTokens % bs == 0) {
+    std::unordered_map<int32_t, int32_t> bucket_of;  // first block -> bucket index
+    std::vector<std::vector<int32_t>> buckets;
+    for (int32_t s = 0; s < S; ++s) {
+      if (ctx[s] < kSharedPartTokens) continue;
+      const int32_t first = tables[size_t(s) * maxB];
+      auto ins = bucket_of.emplace(first, int32_t(buckets.size()));
+      if (ins.second) buckets.emplace_back();
+      buckets[ins.first->second].push_back(s);
+    }
+    for (auto& b : buckets) {
+      if (b.size() < 2) continue;
+      const int32_t lead = b[0];
+      const int32_t* tl = tables + size_t(lead) * maxB;
+      std::vector<int32_t> mem;
+      int32_t common = ctx[lead];
+      for (int32_t s : b) {
+        const int32_t* ts = tables + size_t(s) * maxB;
+        const int32_t nb = std::min({(ctx[lead] + bs - 1) / bs, (ctx[s] + bs - 1) / bs, maxB});
+        int32_t lcp = 0;
+        while (lcp < nb && ts[lcp] == tl[lcp]) ++lcp;
+        const int32_t tok = std::min({lcp * bs, ctx[lead], ctx[s]});
+        if (tok < kSharedPartTokens) continue;
+        mem.push_back(s);
+        common = std::min(common, tok);
+      }
+      if (mem.size() < 2) continue;
+      const int32_t sh = common / kSharedPartTokens * kSharedPartTokens;
+      for (int32_t s : mem) shared[s] = sh;
+      groups.push_back(std::move(mem));
+    }
+  }
+  int32_t pt = requested;
+  if (pt == 0) {
+    // Largest partition (up to 1024 tokens and 64 blocks) that still gives
+    // about six waves per CU: long waves stream without pause, the
+    // longest-first order evens out the end, and fewer partials are merged.
+    const int max_pt = std::min(64 * bs, 1024);
+    pt = max_pt;
+    int64_t gwaves = 0;
+    for (auto& g : groups)
+      gwaves += int64_t((g.size() + kGroup - 1) / kGroup) * (shared[g[0]] / kSharedPartTokens);
+    while (pt > 256 && pt > bs) {
+      int64_t waves = gwaves;
+      for (int32_t s = 0; s < S; ++s) waves += (ctx[s] - shared[s] + pt - 1) / pt;
+      if (waves * H >= kSchedTargetWaves) break;
+      pt /= 2;
+    }
+  }
+  Plan plan;
+  rc = make_plan(S, H, D, bs, max_ctx, dtype, pt, &plan, groups.empty() ? 0 : kSharedPartTokens);
+  if (rc != PA_OK) return rc;
+  pt = plan.part_tokens;
+  hs->part_tokens = pt;
+  hs->max_ctx = max_ctx;
+  hs->ws_bytes = plan.ws_bytes;
+  std::vector<int32_t> nparts(static_cast<size_t>(S), 0);
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t rest = ctx[s] - shared[s];
+    nparts[s] = shared[s] / kSharedPartTokens + (rest + pt - 1) / pt;
+  }
+  auto push = [](std::vector<int32_t>& v, std::initializer_list<int32_t> x) {
+    v.insert(v.end(), x.begin(), x.end());
+  };
+  hs->items.clear();
+  hs->groups.clear();
+  hs->members.clear();
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t base = shared[s] / kSharedPartTokens;
+    for (int32_t p = 0; p < (ctx[s] - shared[s]) / pt; ++p)
+      push(hs->items, {s, base + p, shared[s] + p * pt, pt, nparts[s]});
+  }
+  std::vector<int32_t> partial;
+  for (int32_t s = 0; s < S; ++s)
+    if ((ctx[s] - shared[s]) % pt != 0) partial.push_back(s);
+  std::stable_sort(partial.begin(), partial.end(), [&](int32_t a, int32_t b) {
+    return (ctx[a] - shared[a]) % pt > (ctx[b] - shared[b]) % pt;
+  });
+  for (int32_t s : partial) {
+    const int32_t rest = ctx[s] - shared[s];
+    const int32_t full = rest / pt;
+    push(hs->items, {s, shared[s] / kSharedPartTokens + full, shared[s] + full * pt, rest % pt,
+                     nparts[s]});
+  }
+  for (int32_t s = 0; s < S; ++s)
+    if (ctx[s] == 0) push(hs->items, {s, 0, 0, 0, 0});
+  for (auto& g : groups) {
+    const int32_t parts = shared[g[0]] / kSharedPartTokens;
+    // chunks of at most kGroup members, balanced so that none is a lone member
+    const size_t nchunks = (g.size() + kGroup - 1) / kGroup;
+    for (size_t c = 0, c0 = 0; c < nchunks; ++c) {
+      const int32_t moff = int32_t(hs->members.size() / kMemberInts);
+      const int32_t cnt = int32_t((g.size() - c0) / (nchunks - c));
+      for (int32_t i = 0; i < cnt; ++i) push(hs->members, {g[c0 + i], nparts[g[c0 + i]]});
+      for (int32_t p = 0; p < parts; ++p)
+        push(hs->groups, {moff, cnt, p, p * kSharedPartTokens, kSharedPartTokens});
+      c0 += size_t(cnt);
+    }
+  }
+  return PA_OK;
 }
 
 }  // namespace pa
@@ -563,76 +886,53 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
   return rc == PA_OK ? plan.ws_bytes : size_t(-1);
 }
 
+static int copy_out(const std::vector<int32_t>& v, int32_t per, int32_t* dst, int32_t cap,
+                    int32_t* n) {
+  if (n) *n = int32_t(v.size() / size_t(per));
+  if (int64_t(v.size() / size_t(per)) > cap) return PA_ERR_CAPACITY;
+  if (!v.empty()) std::copy(v.begin(), v.end(), dst);
+  return PA_OK;
+}
+
 int pa_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                        int32_t head_dim, int32_t block_size, int32_t dtype,
                        int32_t partition_tokens, int32_t* items, int32_t capacity,
                        int32_t* num_items, int32_t* partition_tokens_out,
                        int32_t* max_context_len_out) {
-  if (!context_lens || num_seqs < 0 || !num_items || (capacity > 0 && !items))
-    return PA_ERR_INVALID;
-  int32_t max_ctx = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    if (context_lens[s] < 0) return PA_ERR_INVALID;
-    max_ctx = context_lens[s] > max_ctx ? context_lens[s] : max_ctx;
-  }
-  int32_t req = partition_tokens;
-  if (req == 0) {
-    // Largest partition (up to 1024 tokens and 64 blocks) that still gives
-    // about six waves per CU: long waves stream without pause, the
-    // longest-first order evens out the end, and fewer partials are merged.
-    int rc0 = pa::check_shape(head_dim, block_size, dtype);
-    if (rc0 != PA_OK) return rc0;
-    if (num_heads <= 0) return PA_ERR_INVALID;
-    const int max_pt = 64 * block_size < 1024 ? 64 * block_size : 1024;
-    req = max_pt;
-    while (req > 256 && req > block_size) {
-      int64_t waves = 0;
-      for (int32_t s = 0; s < num_seqs; ++s) waves += (context_lens[s] + req - 1) / req;
-      if (waves * num_heads >= pa::kSchedTargetWaves) break;
-      req /= 2;
-    }
-  }
-  pa::Plan plan;
-  int rc = pa::make_plan(num_seqs, num_heads, head_dim, block_size, max_ctx, dtype, req, &plan);
+  if (!num_items || (capacity > 0 && !items)) return PA_ERR_INVALID;
+  pa::HostSchedule hs;
+  int rc = pa::build_schedule(context_lens, num_seqs, num_heads, head_dim, block_size, dtype,
+                              partition_tokens, nullptr, 0, &hs);
   if (rc != PA_OK) return rc;
-  const int pt = plan.part_tokens;
-  // Longest first: every full partition (in sequence order), then the partial
-  // last partitions from longest to shortest, then empty sequences (their
-  // item only writes the zero row).  Short items end the launch, so the last
-  // waves to start are the quickest to finish.
-  int64_t n = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) n += context_lens[s] / pt;
-  for (int32_t s = 0; s < num_seqs; ++s) n += (context_lens[s] % pt != 0 || context_lens[s] == 0);
-  *num_items = int32_t(n);
-  if (partition_tokens_out) *partition_tokens_out = pt;
-  if (max_context_len_out) *max_context_len_out = max_ctx;
-  if (n > capacity) return PA_ERR_CAPACITY;
-  int64_t k = 0;
-  for (int32_t s = 0; s < num_seqs; ++s)
-    for (int32_t p = 0; p < context_lens[s] / pt; ++p) {
-      items[2 * k] = s;
-      items[2 * k + 1] = p;
-      ++k;
-    }
-  // partial partitions by decreasing size (ties in sequence order)
-  std::vector<int32_t> partial;
-  for (int32_t s = 0; s < num_seqs; ++s)
-    if (context_lens[s] % pt != 0) partial.push_back(s);
-  std::stable_sort(partial.begin(), partial.end(), [&](int32_t a, int32_t b) {
-    return context_lens[a] % pt > context_lens[b] % pt;
-  });
-  for (int32_t s : partial) {
-    items[2 * k] = s;
-    items[2 * k + 1] = context_lens[s] / pt;
-    ++k;
-  }
-  for (int32_t s = 0; s < num_seqs; ++s)
-    if (context_lens[s] == 0) {
-      items[2 * k] = s;
-      items[2 * k + 1] = 0;
-      ++k;
-    }
-  return PA_OK;
+  if (partition_tokens_out) *partition_tokens_out = hs.part_tokens;
+  if (max_context_len_out) *max_context_len_out = hs.max_ctx;
+  return copy_out(hs.items, pa::kItemInts, items, capacity, num_items);
+}
+
+int pa_decode_schedule_shared(const int32_t* context_lens, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_heads,
+                              int32_t head_dim, int32_t block_size, int32_t dtype,
+                              int32_t partition_tokens, int32_t* items, int32_t items_capacity,
+                              int32_t* num_items, int32_t* group_items, int32_t group_capacity,
+                              int32_t* num_group_items, int32_t* members,
+                              int32_t members_capacity, int32_t* num_members,
+                              int32_t* partition_tokens_out, int32_t* max_context_len_out,
+                              size_t* workspace_bytes_out) {
+  if (!block_tables || !num_items || !num_group_items || !num_members ||
+      (items_capacity > 0 && !items) || (group_capacity > 0 && !group_items) ||
+      (members_capacity > 0 && !members))
+    return PA_ERR_INVALID;
+  pa::HostSchedule hs;
+  int rc = pa::build_schedule(context_lens, num_seqs, num_heads, head_dim, block_size, dtype,
+                              partition_tokens, block_tables, max_blocks_per_seq, &hs);
+  if (rc != PA_OK) return rc;
+  if (partition_tokens_out) *partition_tokens_out = hs.part_tokens;
+  if (max_context_len_out) *max_context_len_out = hs.max_ctx;
+  if (workspace_bytes_out) *workspace_bytes_out = hs.ws_bytes;
+  int rc1 = copy_out(hs.items, pa::kItemInts, items, items_capacity, num_items);
+  int rc2 = copy_out(hs.groups, pa::kItemInts, group_items, group_capacity, num_group_items);
+  int rc3 = copy_out(hs.members, pa::kMemberInts, members, members_capacity, num_members);
+  return rc1 != PA_OK ? rc1 : (rc2 != PA_OK ? rc2 : rc3);
 }
 
 #define PA_DECODE_ARGS                                                                      \
@@ -656,8 +956,28 @@ int pa_decode_reduce(PA_DECODE_ARGS) { return pa::decode_impl(pa::kDoReduce, PA_
 
 int pa_decode_scheduled(PA_DECODE_ARGS, const int32_t* items, int32_t num_items) {
   if (num_seqs > 0 && (!items || num_items <= 0)) return PA_ERR_INVALID;
-  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, PA_DECODE_PASS, items,
-                         num_items);
+  pa::Schedule sc;
+  sc.scheduled = true;
+  sc.items = items;
+  sc.num_items = num_items;
+  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, PA_DECODE_PASS, sc);
+}
+
+int pa_decode_scheduled_shared(PA_DECODE_ARGS, const int32_t* items, int32_t num_items,
+                               const int32_t* group_items, int32_t num_group_items,
+                               const int32_t* members) {
+  if (num_seqs > 0 && ((num_items > 0 && !items) || num_items < 0 || num_group_items < 0 ||
+                       (num_group_items > 0 && (!group_items || !members)) ||
+                       num_items + num_group_items <= 0))
+    return PA_ERR_INVALID;
+  pa::Schedule sc;
+  sc.scheduled = true;
+  sc.items = items;
+  sc.num_items = num_items;
+  sc.group_items = group_items;
+  sc.num_group_items = num_group_items;
+  sc.group_members = members;
+  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, PA_DECODE_PASS, sc);
 }
 
 }  // extern "C"

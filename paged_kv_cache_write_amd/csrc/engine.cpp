@@ -41,15 +41,18 @@ struct pa_engine {
   std::vector<char> pending;
   std::vector<int32_t> ctx_pre;
   hipEvent_t ev_start = nullptr, ev_end = nullptr;  // optional, around the decode launch
+  bool sharing = true;  // detect shared prefixes in the tables each step
+  pa::HostSchedule hs;
 };
 
 namespace {
 
-// Work items are bounded by one per 32 tokens (the smallest partition) plus
-// one per sequence.
-int64_t item_capacity(int32_t max_batch, int32_t max_blocks, int32_t bs) {
+// Work items (5 int32 each) are bounded by one per 32 tokens (the smallest
+// partition) plus one per sequence, for single and for group items; members
+// (2 int32) by one per sequence.
+int64_t item_ints(int32_t max_batch, int32_t max_blocks, int32_t bs) {
   const int64_t tokens = int64_t(max_blocks) * bs;
-  return int64_t(max_batch) * ((tokens + 31) / 32 + 1);
+  return 2 * 5 * int64_t(max_batch) * ((tokens + 31) / 32 + 1) + 2 * int64_t(max_batch);
 }
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -63,7 +66,7 @@ size_t pa_engine_staging_bytes(int32_t max_batch, int32_t max_blocks_per_seq,
   if (max_batch <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;
   const size_t B = size_t(max_batch);
   return align16(8 * B + 4 * B + 8 * B + 4 * B * size_t(max_blocks_per_seq) +
-                8 * size_t(item_capacity(max_batch, max_blocks_per_seq, block_size)));
+                4 * size_t(item_ints(max_batch, max_blocks_per_seq, block_size)));
 }
 
 int pa_engine_create(pa_bm* bm, void* k_cache, void* v_cache, int64_t num_blocks,
@@ -131,10 +134,9 @@ void pa_engine_destroy(pa_engine* e) {
 
 size_t pa_engine_workspace_bytes(const pa_engine* e, int32_t partition_tokens) {
   if (!e) return size_t(-1);
-  // the schedule never picks partitions below 256 tokens (or the block-size
-  // limit); an explicit size is used as given
-  int32_t pt = partition_tokens;
-  if (pt == 0) pt = std::min<int32_t>(256, 64 * e->bs);
+  // the schedule never picks partitions below 256 tokens, and shared
+  // prefixes use 256-token partitions; an explicit smaller size is used as given
+  int32_t pt = partition_tokens == 0 ? 256 : std::min<int32_t>(partition_tokens, 256);
   return pa_decode_workspace_size(e->max_batch, e->H, e->D, e->bs, e->max_blocks * e->bs,
                                   e->dtype, pt);
 }
@@ -153,22 +155,23 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
   if (workspace && size_t(workspace) % 16) return PA_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
-  // 1. The lengths after this step, to plan the decode before touching the
-  //    block manager (a step that cannot run changes nothing).
+  // 1. Checks that need no change of state: known, distinct sequences whose
+  //    contexts fit the tables, and a workspace that covers any step.
   e->ctx_pre.resize(size_t(n));
   for (int32_t i = 0; i < n; ++i) {
     const int64_t len = pa_bm_seq_len(e->bm, seqs[i]);
     if (len < 0) return int(len);
+    if (len + 1 > int64_t(e->max_blocks) * e->bs) return PA_ERR_CAPACITY;
     e->ctx_pre[i] = int32_t(len + 1);
   }
-  // repeated sequences in one step append several tokens
   {
     std::vector<int64_t> sorted(seqs, seqs + n);
     std::sort(sorted.begin(), sorted.end());
     if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return PA_ERR_INVALID;
   }
-  for (int32_t i = 0; i < n; ++i)
-    if (e->ctx_pre[i] > e->max_blocks * e->bs) return PA_ERR_CAPACITY;
+  const size_t ws_bound = pa_engine_workspace_bytes(e, partition_tokens);
+  if (ws_bound == size_t(-1)) return PA_ERR_INVALID;
+  if (ws_bound > workspace_bytes || (ws_bound > 0 && !workspace)) return PA_ERR_WORKSPACE;
 
   // 2. Host staging slot.
   const int32_t slot = e->next;
@@ -184,26 +187,28 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
   int32_t* h_ctx = reinterpret_cast<int32_t*>(h + off_ctx);
   int32_t* h_cow = reinterpret_cast<int32_t*>(h + off_cow);
   int32_t* h_tab = reinterpret_cast<int32_t*>(h + off_tab);
-  int32_t* h_items = reinterpret_cast<int32_t*>(h + off_items);
-  const int64_t cap_items = item_capacity(e->max_batch, e->max_blocks, e->bs);
 
-  // 3. Schedule first (from the lengths after the step), then check the
-  //    workspace, then commit the appends.
-  int32_t n_items = 0, pt = 0, max_ctx = 0;
-  int rc = pa_decode_schedule(e->ctx_pre.data(), n, e->H, e->D, e->bs, e->dtype, partition_tokens,
-                              h_items, int32_t(cap_items), &n_items, &pt, &max_ctx);
-  if (rc != PA_OK) return rc;
-  const size_t ws_need = pa_decode_workspace_size(n, e->H, e->D, e->bs, max_ctx, e->dtype, pt);
-  if (ws_need == size_t(-1)) return PA_ERR_INVALID;
-  if (ws_need > workspace_bytes || (ws_need > 0 && !workspace)) return PA_ERR_WORKSPACE;
+  // 3. Commit the appends, then schedule from the new tables and lengths.
   int32_t ncow = 0;
-  rc = pa_bm_step(e->bm, seqs, n, h_slots, h_cow, &ncow, h_tab, e->max_blocks, e->pad, h_ctx);
+  int rc = pa_bm_step(e->bm, seqs, n, h_slots, h_cow, &ncow, h_tab, e->max_blocks, e->pad, h_ctx);
   if (rc != PA_OK) return rc;
+  rc = pa::build_schedule(h_ctx, n, e->H, e->D, e->bs, e->dtype, partition_tokens,
+                          e->sharing ? h_tab : nullptr, e->max_blocks, &e->hs);
+  if (rc != PA_OK) return rc;
+  const pa::HostSchedule& hs = e->hs;
+  const int32_t n_items = int32_t(hs.items.size() / 5);
+  const int32_t n_groups = int32_t(hs.groups.size() / 5);
+  const size_t off_groups = off_items + 4 * hs.items.size();
+  const size_t off_members = off_groups + 4 * hs.groups.size();
+  if (!hs.items.empty()) std::memcpy(h + off_items, hs.items.data(), 4 * hs.items.size());
+  if (!hs.groups.empty()) std::memcpy(h + off_groups, hs.groups.data(), 4 * hs.groups.size());
+  if (!hs.members.empty()) std::memcpy(h + off_members, hs.members.data(), 4 * hs.members.size());
+  const int32_t pt = hs.part_tokens, max_ctx = hs.max_ctx;
 
   // 4. Ship the used bytes, copy shared last blocks, write the new tokens.
   //    Copies must land before the writes into the copied blocks; without
   //    copies, one prologue launch ships the staging and writes the tokens.
-  const size_t used = (off_items + 8 * size_t(n_items) + 15) & ~size_t(15);
+  const size_t used = (off_members + 4 * hs.members.size() + 15) & ~size_t(15);
   char* d = e->dev;
   const bool fused = e->host_dev != nullptr && ncow == 0;
   if (fused) {
@@ -227,11 +232,21 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
     if (rc != PA_OK) return rc;
   }
   if (e->ev_start && hipEventRecord(e->ev_start, st) != hipSuccess) return PA_ERR_HIP;
-  rc = pa_decode_scheduled(q, e->k_cache, e->v_cache, reinterpret_cast<const int32_t*>(d + off_tab),
-                           e->max_blocks, reinterpret_cast<const int32_t*>(d + off_ctx), n, e->H,
-                           e->D, e->bs, e->num_blocks, scale, max_ctx, e->dtype, out, workspace,
-                           workspace_bytes, pt, stream,
-                           reinterpret_cast<const int32_t*>(d + off_items), n_items);
+  const int32_t* d_tab = reinterpret_cast<const int32_t*>(d + off_tab);
+  const int32_t* d_ctx = reinterpret_cast<const int32_t*>(d + off_ctx);
+  const int32_t* d_items = reinterpret_cast<const int32_t*>(d + off_items);
+  if (n_groups > 0) {
+    rc = pa_decode_scheduled_shared(q, e->k_cache, e->v_cache, d_tab, e->max_blocks, d_ctx, n,
+                                    e->H, e->D, e->bs, e->num_blocks, scale, max_ctx, e->dtype,
+                                    out, workspace, workspace_bytes, pt, stream,
+                                    n_items ? d_items : nullptr, n_items,
+                                    reinterpret_cast<const int32_t*>(d + off_groups), n_groups,
+                                    reinterpret_cast<const int32_t*>(d + off_members));
+  } else {
+    rc = pa_decode_scheduled(q, e->k_cache, e->v_cache, d_tab, e->max_blocks, d_ctx, n, e->H,
+                             e->D, e->bs, e->num_blocks, scale, max_ctx, e->dtype, out, workspace,
+                             workspace_bytes, pt, stream, d_items, n_items);
+  }
   if (rc != PA_OK) return rc;
   if (e->ev_end && hipEventRecord(e->ev_end, st) != hipSuccess) return PA_ERR_HIP;
   // Host slot `slot` may be rewritten once this step has run (recorded at the
@@ -244,10 +259,17 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
     info->max_context_len = max_ctx;
     info->partition_tokens = pt;
     info->num_items = n_items;
+    info->num_group_items = n_groups;
     int64_t sum = 0;
     for (int32_t i = 0; i < n; ++i) sum += h_ctx[i];
     info->sum_context_len = sum;
   }
+  return PA_OK;
+}
+
+int pa_engine_set_sharing(pa_engine* e, int32_t enable) {
+  if (!e) return PA_ERR_INVALID;
+  e->sharing = enable != 0;
   return PA_OK;
 }
 

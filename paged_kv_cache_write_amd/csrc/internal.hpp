@@ -4,7 +4,25 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace pa {
+
+// Decode work of one call, built on the host (see build_schedule in
+// decode.hip): single items and group items of 5 int32 each, members of 2.
+struct HostSchedule {
+  std::vector<int32_t> items;
+  std::vector<int32_t> groups;
+  std::vector<int32_t> members;
+  int part_tokens = 0;
+  int max_ctx = 0;
+  size_t ws_bytes = 0;
+};
+
+// `tables` (host [S, maxB], may be NULL) enables shared-prefix groups.
+int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t bs,
+                   int32_t dtype, int32_t requested, const int32_t* tables, int32_t maxB,
+                   HostSchedule* hs);
 
 // One launch at the start of an engine step: copy `copy_bytes` (a multiple of
 // 16) of staging from pinned host memory (device-visible address `host_src`)

@@ -127,6 +127,10 @@ class PagedKVEngine:
         self.last_info = self._info
         return out
 
+    def set_sharing(self, enable: bool):
+        """Shared-prefix groups in later steps (on by default)."""
+        _check(lib().pa_engine_set_sharing(self._e, 1 if enable else 0), "pa_engine_set_sharing")
+
     def set_decode_events(self, start=None, end=None):
         """Record torch.cuda.Event ``start``/``end`` around the decode launch of the
         following steps (None = stop)."""
@@ -152,4 +156,5 @@ class PagedKVEngine:
                                          info.num_cow), "pa_engine_last_step")
         return dict(ctx=ctx, slots=slots, cows=cows[:info.num_cow], num_cow=info.num_cow,
                     max_ctx=info.max_context_len, partition_tokens=info.partition_tokens,
-                    num_items=info.num_items, sum_ctx=info.sum_context_len)
+                    num_items=info.num_items, num_group_items=info.num_group_items,
+                    sum_ctx=info.sum_context_len)

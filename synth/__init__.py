@@ -9,7 +9,7 @@ its own attention.
 
 Randomness: ``numpy.random.default_rng(SeedSequence([cfg, stream, sub]))`` with
 one stream per kind of draw (0 context lengths, 1 placement, 2 q, 3 history K,
-4 history V, 5 step-token K/V, 6 tails, 7 fork offsets) and ``sub`` naming the
+4 history V, 5 step-token K/V, 6 tails, 7 fork offsets, 8 fork-tree shape) and ``sub`` naming the
 sequence (or prompt group, or block size for placements), so that a sequence's
 values do not depend on how many other sequences are drawn.  Values are drawn as
 float32 N(0, 1) and rounded to the storage type with round-to-nearest-even.
@@ -37,7 +37,7 @@ except Exception:  # pragma: no cover
 
 __all__ = [
     "DTYPES", "Workload", "make_workload", "make_custom", "to_storage", "CONFIG_NAMES",
-    "SWEEP_BLOCK_SIZES", "cache_draws", "to_torch",
+    "SWEEP_BLOCK_SIZES", "cache_draws", "to_torch", "make_fork_tree",
 ]
 
 # storage dtype name -> (numpy storage dtype, bytes per element)
@@ -54,6 +54,7 @@ SWEEP_BLOCK_SIZES = (8, 16, 32, 64, 128)
 
 _STREAM_CTX, _STREAM_PLACE, _STREAM_Q, _STREAM_K, _STREAM_V = 0, 1, 2, 3, 4
 _STREAM_STEP, _STREAM_TAIL, _STREAM_FORK = 5, 6, 7
+_STREAM_TREE = 8
 
 
 def _rng(cfg: int, stream: int, sub: int = 0) -> np.random.Generator:
@@ -343,3 +344,74 @@ def _make(cfg, bs, cow, S):
                      1.0 / math.sqrt(128), seed_sub=bs)
         return wl
     raise ValueError(f"unknown config {cfg}")
+
+
+def make_fork_tree(seed: int, H: int, D: int, dtype: str, bs: int, roots: int = 2,
+                   forks: int = 10, max_prompt: int = 1400, max_extend: int = 300,
+                   prompt_lens=None) -> Workload:
+    """A random fork tree (parallel sampling and beam-like branching, comfyai.app
+    "6.4 PagedAttention" 6.4.2-6.4.3): ``roots`` prompts, then ``forks`` times a
+    random existing sequence is forked and the child (and sometimes the parent)
+    generates a random number of tokens, so that sequences share prefixes of
+    every length, forks of forks included; then one step over every sequence in
+    a random order.  ``prompt_lens`` fixes the root prompt lengths.  ``seed`` >=
+    100 keeps the streams apart from the five named configs."""
+    rt = _rng(seed, _STREAM_TREE)
+    lens, segs, ops = {}, {}, []
+    sub = [0]
+
+    def new_tokens(seq, n):
+        if n <= 0:
+            return
+        k = _normal(_rng(seed, _STREAM_K, sub[0]), (n, H, D), dtype)
+        v = _normal(_rng(seed, _STREAM_V, sub[0]), (n, H, D), dtype)
+        sub[0] += 1
+        t = lens[seq]
+        segs[seq].append((t, t + n, k, v))
+        lens[seq] = t + n
+
+    for r in range(roots):
+        n = int(prompt_lens[r]) if prompt_lens is not None else int(rt.integers(0, max_prompt + 1))
+        lens[r], segs[r] = 0, []
+        new_tokens(r, n)
+        ops.append(("add", r, n))
+    nxt = roots
+    for _ in range(forks):
+        parent = int(rt.choice(sorted(lens)))
+        child = nxt
+        nxt += 1
+        L = lens[parent]
+        segs[child] = [(a, min(b, L), k[:min(b, L) - a], v[:min(b, L) - a])
+                       for (a, b, k, v) in segs[parent] if a < L]
+        lens[child] = L
+        ops.append(("fork", parent, child))
+        n = int(rt.integers(0, max_extend + 1))
+        new_tokens(child, n)
+        if n:
+            ops.append(("extend", child, n))
+        if rt.random() < 0.3:
+            n = int(rt.integers(1, max_extend + 1))
+            new_tokens(parent, n)
+            ops.append(("extend", parent, n))
+    seqs = [int(x) for x in rt.permutation(nxt)]
+    # the step appends one token to every sequence, in the listed order; the
+    # decode rows follow that order
+    rs = _rng(seed, _STREAM_STEP)
+    step_k = _normal(rs, (nxt, H, D), dtype)
+    step_v = _normal(rs, (nxt, H, D), dtype)
+    for i, s in enumerate(seqs):
+        t = lens[s]
+        segs[s].append((t, t + 1, step_k[i:i + 1], step_v[i:i + 1]))
+        lens[s] = t + 1
+    ops.append(("step", seqs))
+    # decode rows follow the step list
+    ctx = np.array([lens[s] for s in seqs], dtype=np.int64)
+    demand = sum(-(-lens[s] // bs) + 1 for s in seqs)
+    NB = demand + 8
+    poison, free_order = _placement(seed, NB)
+    q = _normal(_rng(seed, _STREAM_Q), (nxt, H, D), dtype)
+    maxb = int(math.ceil(int(ctx.max()) / bs))
+    return Workload(cfg=seed, name=f"fork-tree-{seed}-{dtype}-bs{bs}", H=H, D=D, dtype=dtype,
+                    bs=bs, NB=NB, scale=1.0 / math.sqrt(D), free_order=free_order,
+                    poison_block=poison, ctx=ctx, q=q, ops=ops, max_blocks_per_seq=maxb,
+                    _segments=segs, notes="random fork tree")

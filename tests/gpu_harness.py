@@ -50,7 +50,7 @@ def oracle_bits(a, dtype_name):
     return np.ascontiguousarray(a).view(np.int32)
 
 
-def run_gpu(wl, partition_tokens=0, fill_nan=True):
+def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True):
     """Execute wl.ops with PagedKVEngine; returns dict with the engine and the step output."""
     import torch
     from paged_kv_cache_write_amd.engine import PagedKVEngine
@@ -59,6 +59,7 @@ def run_gpu(wl, partition_tokens=0, fill_nan=True):
                         free_order=wl.free_order, pad_block=wl.poison_block,
                         fill=float("nan") if fill_nan else 0.0,
                         partition_tokens=partition_tokens)
+    eng.set_sharing(sharing)
     out = None
     for op in wl.ops:
         if op[0] == "add":
@@ -117,3 +118,46 @@ def sample_seqs(ctx, k, seed=0):
             break
         pick.add(int(s))
     return sorted(pick)
+
+
+def same_storage(gpu_t, ora, dtype, what):
+    g = bits(gpu_t)
+    o = oracle_bits(ora, dtype)
+    assert g.shape == o.shape, what
+    eq = g == o
+    if not eq.all():
+        fl = {"f32": np.float32, "f16": np.float16, "bf16": None}[dtype]
+        if fl is None:
+            gn = ((g.view(np.uint16) & 0x7F80) == 0x7F80) & ((g.view(np.uint16) & 0x7F) != 0)
+            on = ((o.view(np.uint16) & 0x7F80) == 0x7F80) & ((o.view(np.uint16) & 0x7F) != 0)
+        else:
+            gn, on = np.isnan(g.view(fl)), np.isnan(o.view(fl))
+        bad = ~eq & ~(gn & on)
+        assert not bad.any(), f"{what}: {int(bad.sum())} storage elements differ"
+
+
+def check_workload(wl, seqs=None, partition_tokens=0, tol=TOL, compare_pools=True,
+                   cast_bound=False, sharing=True):
+    """Run wl through the engine and the oracle: step bookkeeping and pools bit-exact,
+    outputs within tol.  Returns (gpu dict, oracle dict, max error)."""
+    log(f"case {wl.name}: S={wl.S} H={wl.H} D={wl.D} {wl.dtype} bs={wl.bs} NB={wl.NB} "
+        f"sum(ctx)={int(wl.ctx.sum())} partition_tokens={partition_tokens}")
+    g = run_gpu(wl, partition_tokens=partition_tokens, sharing=sharing)
+    log("  gpu done; running oracle")
+    r = oracle.run_workload(wl, decode_seqs=seqs)
+    eng = g["engine"]
+    last = eng.last_step
+    assert np.array_equal(last["ctx"], r["ctx"]), "context lengths"
+    assert np.array_equal(last["slots"], r["step_slots"]), "step slot mapping"
+    assert np.array_equal(last["cows"].reshape(-1, 2), r["step_cows"]), "step CoW pairs"
+    step = np.array([op for op in wl.ops if op[0] == "step"][-1][1], dtype=np.int64)
+    tables, _ = eng.bm.block_tables(step, wl.max_blocks_per_seq, wl.poison_block)
+    assert np.array_equal(tables, r["tables"]), "block tables"
+    assert eng.bm.refcounts() == r["refcounts"].tolist(), "refcounts"
+    if compare_pools:
+        same_storage(eng.k_cache, r["k_cache"], wl.dtype, "k_cache")
+        same_storage(eng.v_cache, r["v_cache"], wl.dtype, "v_cache")
+        log("  pools bit-exact")
+    err = compare_outputs(g["out"], r["out"], seqs=seqs, tol=tol, what=wl.name,
+                          cast_dtype=wl.dtype if cast_bound else None)
+    return g, r, err

@@ -81,27 +81,6 @@ def test_decode_plan(S, H, D, bs, L, req):
     assert pk.decode_workspace_size(S, H, D, bs, L, 1, req) == ws
 
 
-def test_decode_schedule_order():
-    """Full partitions first, then partial ones longest first, then empty rows."""
-    import numpy as np
-    import paged_kv_cache_write_amd as pk
-    ctx = np.array([0, 300, 256, 1000, 5, 512], dtype=np.int32)
-    items, pt, mx = pk.decode_schedule(ctx, 40, 128, 16, 1, 256)
-    assert (pt, mx) == (256, 1000)
-    assert items.tolist() == [[1, 0], [2, 0], [3, 0], [3, 1], [3, 2], [5, 0], [5, 1],
-                              [3, 3], [1, 1], [4, 0], [0, 0]]
-    # every (sequence, partition) exactly once
-    rng = np.random.default_rng(0)
-    for _ in range(20):
-        ctx = rng.integers(0, 5000, size=int(rng.integers(1, 50))).astype(np.int32)
-        items, pt, mx = pk.decode_schedule(ctx, 40, 128, 16, 1, 0)
-        want = sorted([(s, p) for s, c in enumerate(ctx) for p in range(-(-int(c) // pt))] +
-                      [(s, 0) for s, c in enumerate(ctx) if c == 0])
-        assert sorted(map(tuple, items.tolist())) == want
-        sizes = [min(pt, int(ctx[s]) - p * pt) for s, p in items.tolist()]
-        assert sizes == sorted(sizes, reverse=True)
-
-
 def test_engine_staging_and_errors():
     import paged_kv_cache_write_amd as pk
     lib = pk.lib()

@@ -127,8 +127,11 @@ def test_random_ops_match_model():
 
 def test_workload_scripts_match_model():
     """Execute each config's op script on both managers (no K/V data)."""
-    for cfg, kw in ((1, {}), (2, {}), (4, {}), (4, {"cow": True}), (5, {"bs": 8, "S": 40})):
-        wl = synth.make_workload(cfg, values=False, **kw)
+    cases = [synth.make_workload(cfg, values=False, **kw) for cfg, kw in
+             ((1, {}), (2, {}), (4, {}), (4, {"cow": True}), (5, {"bs": 8, "S": 40}))]
+    cases += [synth.make_fork_tree(seed, 1, 8, "f32", bs, forks=12, max_prompt=200,
+                                   max_extend=50) for seed, bs in ((510, 8), (511, 16))]
+    for wl in cases:
         bm, model = _bm(wl.NB, wl.bs, wl.free_order), oracle.BlockPoolModel(wl.NB, wl.bs, wl.free_order)
         for op in wl.ops:
             if op[0] == "add":

@@ -11,53 +11,16 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import TOL, bits, compare_outputs, log, oracle_bits, run_gpu, sample_seqs, to_dev
+from gpu_harness import (TOL, bits, compare_outputs, log, oracle_bits, run_gpu, sample_seqs,
+                         to_dev)
+from gpu_harness import check_workload as _check_workload
+from gpu_harness import same_storage as _same_storage
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
-
-
-def _same_storage(gpu_t, ora, dtype, what):
-    g = bits(gpu_t)
-    o = oracle_bits(ora, dtype)
-    assert g.shape == o.shape, what
-    eq = g == o
-    if not eq.all():
-        fl = {"f32": np.float32, "f16": np.float16, "bf16": None}[dtype]
-        if fl is None:
-            gn = ((g.view(np.uint16) & 0x7F80) == 0x7F80) & ((g.view(np.uint16) & 0x7F) != 0)
-            on = ((o.view(np.uint16) & 0x7F80) == 0x7F80) & ((o.view(np.uint16) & 0x7F) != 0)
-        else:
-            gn, on = np.isnan(g.view(fl)), np.isnan(o.view(fl))
-        bad = ~eq & ~(gn & on)
-        assert not bad.any(), f"{what}: {int(bad.sum())} storage elements differ"
-
-
-def _check_workload(wl, seqs=None, partition_tokens=0, tol=TOL, compare_pools=True,
-                    cast_bound=False):
-    log(f"case {wl.name}: S={wl.S} H={wl.H} D={wl.D} {wl.dtype} bs={wl.bs} NB={wl.NB} "
-        f"sum(ctx)={int(wl.ctx.sum())} partition_tokens={partition_tokens}")
-    g = run_gpu(wl, partition_tokens=partition_tokens)
-    log("  gpu done; running oracle")
-    r = oracle.run_workload(wl, decode_seqs=seqs)
-    eng = g["engine"]
-    last = eng.last_step
-    assert np.array_equal(last["ctx"], r["ctx"]), "context lengths"
-    assert np.array_equal(last["slots"], r["step_slots"]), "step slot mapping"
-    assert np.array_equal(last["cows"].reshape(-1, 2), r["step_cows"]), "step CoW pairs"
-    tables, _ = eng.bm.block_tables(np.arange(wl.S), wl.max_blocks_per_seq, wl.poison_block)
-    assert np.array_equal(tables, r["tables"]), "block tables"
-    assert eng.bm.refcounts() == r["refcounts"].tolist(), "refcounts"
-    if compare_pools:
-        _same_storage(eng.k_cache, r["k_cache"], wl.dtype, "k_cache")
-        _same_storage(eng.v_cache, r["v_cache"], wl.dtype, "v_cache")
-        log("  pools bit-exact")
-    err = compare_outputs(g["out"], r["out"], seqs=seqs, tol=tol, what=wl.name,
-                          cast_dtype=wl.dtype if cast_bound else None)
-    return g, r, err
 
 
 # ------------------------------------------------------------ the 5 configs
@@ -82,10 +45,16 @@ def test_config3_long_context_split():
 
 @pytest.mark.parametrize("cow", [False, True])
 def test_config4_shared_prefix(cow):
+    """With shared-prefix group items (32: 8 groups x 4 partitions of 256 tokens)
+    and without: both within tolerance of the oracle."""
     wl = synth.make_workload(4, cow=cow)
     g, r, _ = _check_workload(wl)
     if cow:
         assert r["all_cows"].shape[0] == 7 * 8
+    assert g["engine"].last_step["num_group_items"] == 32
+    g_off = run_gpu(wl, sharing=False)
+    assert g_off["engine"].last_step["num_group_items"] == 0
+    compare_outputs(g_off["out"], r["out"], what=wl.name + " no sharing")
 
 
 @pytest.mark.parametrize("bs", synth.SWEEP_BLOCK_SIZES)

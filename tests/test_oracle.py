@@ -223,6 +223,27 @@ def test_decode_equals_unpaged_attention(cfg):
             assert np.array_equal(r["out"][s, h], want)
 
 
+@pytest.mark.parametrize("seed,bs", [(500, 16), (501, 8), (502, 32)])
+def test_fork_tree_decode_equals_unpaged_attention(seed, bs):
+    """Random fork trees (forks of forks, parents extended after forking, copy on
+    write of half-full shared blocks): each decode row equals attention over the
+    sequence's logical K/V as drawn, so the script's sharing never leaks one
+    branch's tokens into another."""
+    wl = synth.make_fork_tree(seed, 2, 16, "f32", bs, roots=2, forks=8, max_prompt=120,
+                              max_extend=40)
+    r = oracle.run_workload(wl)
+    step = [op for op in wl.ops if op[0] == "step"][-1][1]
+    assert r["all_cows"].shape[0] > 0
+    for row, s in enumerate(step):
+        L = int(r["ctx"][row])
+        k, v = wl.kv(s, 0, L)
+        for h in range(wl.H):
+            logits = wl.scale * (k[:, h, :].astype(np.float64) @ wl.q[row, h].astype(np.float64))
+            e = np.exp(logits - logits.max())
+            want = (e / e.sum()) @ v[:, h, :].astype(np.float64)
+            assert np.array_equal(r["out"][row, h], want)
+
+
 def test_cache_write_places_every_token():
     """After the script, every token t of every sequence sits at
     pool[table[t//bs], :, t%bs, :], and nothing else was written."""
