@@ -38,6 +38,7 @@
 //    finish the row (one launch, an agent-scope counter per row), or by a
 //    second kernel (pa_decode_partitions + pa_decode_reduce).
 #include <algorithm>
+#include <type_traits>
 #include <unordered_map>
 #include <vector>
 
@@ -56,9 +57,13 @@ namespace pa {
 constexpr int kWaves = PA_DECODE_WAVES;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kUnroll = PA_DECODE_UNROLL;  // 16-byte K loads (and V loads) per lane per chunk
-constexpr int kGroup = 8;                  // queries per group wave
+constexpr int kGroup = 8;                  // queries per group wave (float32, vector ALU)
+constexpr int kGroupMfma = 16;             // queries per group wave on the matrix cores
 constexpr int kGroupUnroll = 4;            // chunk of a group wave (register budget)
-constexpr int kSharedPartTokens = 256;     // partition of a shared range
+#ifndef PA_SHARED_PART_TOKENS
+#define PA_SHARED_PART_TOKENS 256
+#endif
+constexpr int kSharedPartTokens = PA_SHARED_PART_TOKENS;  // partition of a shared range
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so max - max never is NaN
 
@@ -111,6 +116,17 @@ __device__ __forceinline__ u32x4 load_stream(const char* p) {
   return *reinterpret_cast<const u32x4*>(p);
 #else
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#endif
+}
+
+// Loads of the matrix-core group kernel: each K line is read by two load
+// instructions (half a row each), so these default to ordinary loads.
+template <class V>
+__device__ __forceinline__ V group_load(const char* p) {
+#ifdef PA_GROUP_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+#else
+  return *reinterpret_cast<const V*>(p);
 #endif
 }
 
@@ -557,6 +573,219 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeParams P) 
   finish<DT, D, U, kGroup>(P, rows, nps, nq, part, m, l, acc, lane);
 }
 
+// Shared prefixes on the matrix cores: one wave per (group of up to
+// kGroupMfma sequences sharing a prefix, head, shared partition), for
+// float16 / bfloat16 storage.  With several queries against one tile, q.K and
+// P.V are small dense products:
+//   S^T[t][q] = sum_d K[t][d] Q[q][d]   (A = 16 token rows of K, B = Q^T)
+//   O^T[d][q] += sum_t V^T[d][t] P^T[t][q]   (A = V^T, B = P^T)
+// The S^T result layout (lane l: tokens 4 (l/16) + r, query l % 16) is
+// exactly the B operand layout P^T needs, so P never leaves the lane.  The
+// V^T operand needs, in lane l, the same d of several token rows; the d
+// axis of the second product is permuted (product jd, row m <-> d = NJ m +
+// jd) so that lane l loads NJ consecutive elements of each of its token rows
+// with one plain load and takes element jd for product jd.  The output then
+// lands in lane l as query l % 16, d = NJ (4 (l/16) + r) + jd: contiguous.
+// P is split into storage-type hi + lo parts (two products), which keeps the
+// weights at float32-like precision; the sums l use the float32 P.  A step is
+// 32 tokens (two 16-token tiles); the next step's loads are in flight while
+// one is computed.
+template <class DT, int D>
+__global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParams P) {
+  using T = typename DT::T;
+  constexpr int NK = D / 32;  // q.K products per tile (32 d each)
+  constexpr int NJ = D / 16;  // P.V products per step (16 d each) = V elements per row load
+  constexpr uint32_t kRowBytes = uint32_t(D) * sizeof(T);
+  constexpr int kLog2Row = __builtin_ctz(kRowBytes);
+  using VRow = typename std::conditional<NJ == 8, u32x4, u32x2>::type;
+  static_assert(sizeof(T) == 2 && (NJ == 8 || NJ == 4), "16-bit storage, D 64 or 128");
+
+  const int lane = threadIdx.x;
+  const int H = P.H;
+  const int item = blockIdx.x / H;
+  const int h = blockIdx.x - item * H;
+  const int32_t* it = P.group_items + kItemInts * item;
+  const int moff = it[0];
+  const int nq = min(int(it[1]), kGroupMfma);
+  const int part = it[2];
+  const int t0 = it[3];
+  const int ntok = it[4];
+  // a group item is always one whole shared partition
+  if (nq <= 0 || ntok != kSharedPartTokens) return;
+  const int32_t* mem = P.group_members + kMemberInts * moff;
+  const int qi = lane & 15;  // this lane's query (B column, output column)
+  const int g = lane >> 4;   // this lane's k / row group
+  const bool has_q = qi < nq;
+  const int seq_q = mem[kMemberInts * (has_q ? qi : 0)];
+  const int nparts_q = mem[kMemberInts * (has_q ? qi : 0) + 1];
+  const size_t row_q = size_t(seq_q) * H + h;
+
+  // Table window of the first member (all members hold the same blocks here).
+  const int log2_bs = P.log2_bs;
+  const int bs_mask = (1 << log2_bs) - 1;
+  const int log2_tile = kLog2Row + log2_bs;
+  const int blk0 = t0 >> log2_bs;
+  int tbl = 0;
+  if (lane < (kSharedPartTokens >> log2_bs) && blk0 + lane < P.maxB)
+    tbl = P.block_tables[size_t(mem[0]) * P.maxB + blk0 + lane];
+
+  u32x4 qv[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j)
+    qv[j] = has_q ? load16(reinterpret_cast<const char*>(P.q) + row_q * kRowBytes +
+                           (32 * j + 8 * g) * sizeof(T))
+                  : u32x4{0, 0, 0, 0};
+
+  const char* kc = reinterpret_cast<const char*>(P.k_cache);
+  const char* vc = reinterpret_cast<const char*>(P.v_cache);
+  // Byte offset of token row tt + r of the partition (tt a multiple of 16,
+  // r < 16): a 16-token tile spans at most two blocks.
+  auto row_off = [&](int tt, int r) -> size_t {
+    const int b_lo = __builtin_amdgcn_readlane(tbl, tt >> log2_bs);
+    const int b_hi = __builtin_amdgcn_readlane(tbl, (tt + 15) >> log2_bs);
+    const int b = ((tt + r) >> log2_bs) == (tt >> log2_bs) ? b_lo : b_hi;
+    return (size_t(uint32_t(b) * uint32_t(H) + uint32_t(h)) << log2_tile) +
+           size_t((tt + r) & bs_mask) * kRowBytes;
+  };
+
+  // One step = 32 tokens = two 16-token tiles a.
+  //   K[a][j]: K[row l % 16 of tile a][32 j + 8 g ..]           (A of q.K)
+  //   V[4 a + i]: V[row 4 g + i of tile a][NJ (l % 16) ..]       (V^T of P.V)
+  struct KStep { u32x4 k[2][NK]; };
+  struct VStep { VRow v[8]; };
+  auto issue_k = [&](KStep& st, int c) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const char* kp = kc + row_off(32 * c + 16 * a, qi) + 8 * g * sizeof(T);
+#pragma unroll
+      for (int j = 0; j < NK; ++j) st.k[a][j] = group_load<u32x4>(kp + 32 * j * sizeof(T));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto issue_v = [&](VStep& st, int c) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const char* vp = vc + row_off(32 * c + 16 * a, 4 * g) + qi * NJ * sizeof(T);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st.v[4 * a + i] = group_load<VRow>(vp + i * kRowBytes);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  float m = kNegBig, l = 0.f;
+  f32x4 o[NJ];
+#pragma unroll
+  for (int jd = 0; jd < NJ; ++jd) o[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float qk_scale = P.qk_scale;
+
+  // S^T of the step's two tiles: element r of sc[a] is token 16 a + 4 g + r, query qi
+  auto qk = [&](const KStep& st, f32x4 (&sc)[2]) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      sc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NK; ++j) sc[a] = mma16x16x32(DT{}, st.k[a][j], qv[j], sc[a]);
+    }
+  };
+  auto softmax_pv = [&](const f32x4 (&sc)[2], const VStep& st) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sc[e >> 2][e & 3] * qk_scale;
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
+    u32x4 phi, plo;
+#pragma unroll
+    for (int p2 = 0; p2 < 4; ++p2) {
+      const float p0 = fast_exp2(x[2 * p2] - mn), p1 = fast_exp2(x[2 * p2 + 1] - mn);
+      l += p0 + p1;
+      uint32_t hw, lw;
+      split_pair(DT{}, p0, p1, hw, lw);
+      phi[p2] = hw;
+      plo[p2] = lw;
+    }
+#pragma unroll
+    for (int jd = 0; jd < NJ; ++jd) o[jd] *= alpha;
+#pragma unroll
+    for (int jd = 0; jd < NJ; ++jd) {
+      // V^T operand of product jd: element jd of the lane's eight row loads
+      const uint32_t sel = (jd & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 va;
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2)
+        va[p2] = __builtin_amdgcn_perm(uint32_t(st.v[2 * p2 + 1][jd >> 1]),
+                                       uint32_t(st.v[2 * p2][jd >> 1]), sel);
+      o[jd] = mma16x16x32(DT{}, va, phi, o[jd]);
+      o[jd] = mma16x16x32(DT{}, va, plo, o[jd]);
+    }
+  };
+
+  // Fully unrolled with a fixed step count.  Order per step c: K loads of
+  // c + 1, q.K of c, V loads of c + 1, softmax and P.V of c: one step of
+  // K and V is always in flight, and with a fixed count the compiler's wait
+  // counts are exact (a conditional issue would make it wait for everything
+  // at the join).
+  constexpr int kSteps = kSharedPartTokens / 32;
+  KStep ks[2];
+  VStep vs[2];
+  issue_k(ks[0], 0);
+  issue_v(vs[0], 0);
+#pragma unroll
+  for (int c = 0; c < kSteps; ++c) {
+    if (c + 1 < kSteps) issue_k(ks[(c + 1) & 1], c + 1);
+    f32x4 sc[2];
+    qk(ks[c & 1], sc);
+    if (c + 1 < kSteps) issue_v(vs[(c + 1) & 1], c + 1);
+    softmax_pv(sc, vs[c & 1]);
+  }
+
+  // the four lanes of a query hold partial sums over their token rows
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  const float inv = 1.0f / l;  // l >= 1: the running max token contributes 2^0
+  const bool split = nparts_q > 1;
+  if (has_q && !split) {
+    T* out = reinterpret_cast<T*>(P.out) + row_q * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      VRow w;
+#pragma unroll
+      for (int p2 = 0; p2 < NJ / 2; ++p2)
+        w[p2] = pack_store(DT{}, o[2 * p2][r] * inv, o[2 * p2 + 1][r] * inv);
+      *reinterpret_cast<VRow*>(out + NJ * (4 * g + r)) = w;
+    }
+  }
+  // Partials: the schedule keeps every member's last partition in the
+  // single-item launch that follows on the same stream, so no group wave is
+  // the last of its row; the partials are plain stores, made visible to the
+  // next launch by the kernel boundary, and only the row counter is counted.
+  if (has_q && split) {
+    const size_t pi = row_q * P.max_parts + part;
+    float* po = P.ws_o + pi * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int h4 = 0; h4 < NJ / 4; ++h4) {
+        const f32x4 w = f32x4{o[4 * h4][r], o[4 * h4 + 1][r], o[4 * h4 + 2][r], o[4 * h4 + 3][r]} * inv;
+        *reinterpret_cast<f32x4*>(po + NJ * (4 * g + r) + 4 * h4) = w;
+      }
+    }
+    if (g == 0) {
+      P.ws_ml[2 * pi] = m;
+      P.ws_ml[2 * pi + 1] = l;
+      if (P.counters)
+        __hip_atomic_fetch_add(P.counters + row_q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Second launch of the two-launch form: one wave per (sequence, head) row.
 template <class DT, int D, int U>
 __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams P) {
@@ -578,15 +807,22 @@ struct Plan {
   size_t ws_bytes;
 };
 
-// Workspace: [S*H int32 counters, padded to 256 B][S*H*P*2 float (max, sum)][S*H*P*D float]
+// Workspace: [S*H int32 counters, padded to 256 B][S*H*P*2 float (max, sum), padded to
+// 16 B][S*H*P*D float]
 static size_t counter_bytes(int32_t S, int32_t H) {
   return (size_t(S) * H * sizeof(int) + 255) & ~size_t(255);
 }
 
+// (max, sum) floats of all partials, padded so the outputs start 16-byte aligned
+static size_t ml_floats(int32_t S, int32_t H, int max_parts) {
+  return (size_t(S) * H * max_parts * 2 + 3) & ~size_t(3);
+}
+
 static size_t ws_bytes_for(int32_t S, int32_t H, int32_t D, int max_parts) {
-  return max_parts > 1
-             ? counter_bytes(S, H) + size_t(S) * H * max_parts * (size_t(D) + 2) * sizeof(float)
-             : 0;
+  return max_parts > 1 ? counter_bytes(S, H) +
+                             (ml_floats(S, H, max_parts) + size_t(S) * H * max_parts * D) *
+                                 sizeof(float)
+                       : 0;
 }
 
 // Context-partition size.  Requested sizes must be multiples of 32 and of the
@@ -630,8 +866,12 @@ static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t
   const int ngroups = (p.H + kWaves - 1) / kWaves;
   switch (what) {
     case Launch::kGroups:
-      hipLaunchKernelGGL((decode_group_kernel<DT, D, kGroupUnroll>),
-                         dim3(unsigned(n) * unsigned(ngroups)), dim3(kThreads), 0, st, p);
+      if constexpr (std::is_same<DT, F32>::value)
+        hipLaunchKernelGGL((decode_group_kernel<DT, D, kGroupUnroll>),
+                           dim3(unsigned(n) * unsigned(ngroups)), dim3(kThreads), 0, st, p);
+      else
+        hipLaunchKernelGGL((decode_group_mfma_kernel<DT, D>), dim3(unsigned(n) * unsigned(p.H)),
+                           dim3(kWave), 0, st, p);
       break;
     case Launch::kSingles: {
       const dim3 grid = p.items ? dim3(unsigned(n) * unsigned(ngroups), 1, 1)
@@ -701,7 +941,7 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   const bool split = plan.ws_bytes > 0;
   p.counters = (split && (what & kFused)) ? reinterpret_cast<int*>(ws) : nullptr;
   p.ws_ml = split ? reinterpret_cast<float*>(ws + counter_bytes(S, H)) : nullptr;
-  p.ws_o = split ? p.ws_ml + size_t(S) * H * plan.max_parts * 2 : nullptr;
+  p.ws_o = split ? p.ws_ml + ml_floats(S, H, plan.max_parts) : nullptr;
   p.items = sched.items;
   p.group_items = sched.group_items;
   p.group_members = sched.group_members;
@@ -744,6 +984,8 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
 //    part_tokens.  Single items are ordered longest first: every full
 //    partition, then the partial last partitions from longest to shortest,
 //    then one item per empty sequence (which only zeroes its row).
+int min_schedule_partition_tokens() { return std::min(256, kSharedPartTokens); }
+
 int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t bs,
                    int32_t dtype, int32_t requested, const int32_t* tables, int32_t maxB,
                    HostSchedule* hs) {
@@ -757,6 +999,9 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
   }
   std::vector<int32_t> shared(static_cast<size_t>(S), 0);
   std::vector<std::vector<int32_t>> groups;
+  // members per group wave: the matrix-core kernel takes 16 queries, the
+  // float32 (vector ALU) kernel 8
+  const size_t max_members = dtype == PA_F32 ? size_t(kGroup) : size_t(kGroupMfma);
   if (tables && kSharedPartTokens % bs == 0) {
     std::unordered_map<int32_t, int32_t> bucket_of;  // first block -> bucket index
     std::vector<std::vector<int32_t>> buckets;
@@ -784,7 +1029,12 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
         common = std::min(common, tok);
       }
       if (mem.size() < 2) continue;
+      // Every member keeps at least one token outside the shared run, so each
+      // row's last partition is a single item of the later launch and group
+      // waves never merge (their partials need no cross-XCD coherence).
+      for (int32_t s : mem) common = std::min(common, ctx[s] - 1);
       const int32_t sh = common / kSharedPartTokens * kSharedPartTokens;
+      if (sh < kSharedPartTokens) continue;
       for (int32_t s : mem) shared[s] = sh;
       groups.push_back(std::move(mem));
     }
@@ -798,7 +1048,8 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
     pt = max_pt;
     int64_t gwaves = 0;
     for (auto& g : groups)
-      gwaves += int64_t((g.size() + kGroup - 1) / kGroup) * (shared[g[0]] / kSharedPartTokens);
+      gwaves += int64_t((g.size() + max_members - 1) / max_members) *
+                (shared[g[0]] / kSharedPartTokens);
     while (pt > 256 && pt > bs) {
       int64_t waves = gwaves;
       for (int32_t s = 0; s < S; ++s) waves += (ctx[s] - shared[s] + pt - 1) / pt;
@@ -845,8 +1096,8 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
     if (ctx[s] == 0) push(hs->items, {s, 0, 0, 0, 0});
   for (auto& g : groups) {
     const int32_t parts = shared[g[0]] / kSharedPartTokens;
-    // chunks of at most kGroup members, balanced so that none is a lone member
-    const size_t nchunks = (g.size() + kGroup - 1) / kGroup;
+    // chunks of at most max_members, balanced so that none is a lone member
+    const size_t nchunks = (g.size() + max_members - 1) / max_members;
     for (size_t c = 0, c0 = 0; c < nchunks; ++c) {
       const int32_t moff = int32_t(hs->members.size() / kMemberInts);
       const int32_t cnt = int32_t((g.size() - c0) / (nchunks - c));

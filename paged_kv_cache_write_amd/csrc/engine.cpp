@@ -134,9 +134,10 @@ void pa_engine_destroy(pa_engine* e) {
 
 size_t pa_engine_workspace_bytes(const pa_engine* e, int32_t partition_tokens) {
   if (!e) return size_t(-1);
-  // the schedule never picks partitions below 256 tokens, and shared
-  // prefixes use 256-token partitions; an explicit smaller size is used as given
-  int32_t pt = partition_tokens == 0 ? 256 : std::min<int32_t>(partition_tokens, 256);
+  // the schedule's own partitions (automatic and shared-prefix) never go
+  // below this size; an explicit smaller size is used as given
+  const int32_t floor_pt = pa::min_schedule_partition_tokens();
+  int32_t pt = partition_tokens == 0 ? floor_pt : std::min<int32_t>(partition_tokens, floor_pt);
   return pa_decode_workspace_size(e->max_batch, e->H, e->D, e->bs, e->max_blocks * e->bs,
                                   e->dtype, pt);
 }

@@ -20,6 +20,10 @@ struct HostSchedule {
 };
 
 // `tables` (host [S, maxB], may be NULL) enables shared-prefix groups.
+// Smallest partition (tokens) that build_schedule uses on its own: the
+// automatic size and the shared-prefix partitions never go below it.
+int min_schedule_partition_tokens();
+
 int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t bs,
                    int32_t dtype, int32_t requested, const int32_t* tables, int32_t maxB,
                    HostSchedule* hs);

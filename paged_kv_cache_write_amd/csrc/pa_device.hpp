@@ -8,6 +8,8 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
@@ -111,6 +113,51 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Matrix cores, 16x16x32 with float32 accumulation (gfx950).  Lane l supplies
+// row (l % 16) of A and column (l % 16) of B, each over k = 8 (l / 16) ..
+// 8 (l / 16) + 7 (eight storage elements in one 16-byte vector), and receives
+// D[4 (l / 16) + r][l % 16] in element r.
+__device__ __forceinline__ f32x4 mma16x16x32(F16, u32x4 a, u32x4 b, f32x4 c) {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a),
+                                                __builtin_bit_cast(v8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16x16x32(BF16, u32x4 a, u32x4 b, f32x4 c) {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a),
+                                                 __builtin_bit_cast(v8, b), c, 0, 0, 0);
+}
+
+// Two float32 values as storage-type pairs hi + lo, packed two per word
+// (first value in the low half): hi is x truncated to the storage type and lo
+// the storage value of the exact remainder x - hi, so hi + lo equals x to
+// about 2^-15 (bfloat16) or 2^-20 (float16) relative.
+__device__ __forceinline__ void split_pair(F16, float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+  const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(x0, x1);  // toward zero
+  const float r0 = x0 - float(h.x), r1 = x1 - float(h.y);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+}
+__device__ __forceinline__ void split_pair(BF16, float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t b0 = __builtin_bit_cast(uint32_t, x0), b1 = __builtin_bit_cast(uint32_t, x1);
+  const float r0 = x0 - bits_as<float>(b0 & 0xffff0000u);
+  const float r1 = x1 - bits_as<float>(b1 & 0xffff0000u);
+  hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // high halves of b0, b1
+  lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, r1), __builtin_bit_cast(uint32_t, r0),
+                             0x07060302u);
+}
+
+// Two float32 values rounded (nearest even) to the storage type, packed.
+__device__ __forceinline__ uint32_t pack_store(F16, float a, float b) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (_Float16)a)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)b)) << 16);
+}
+__device__ __forceinline__ uint32_t pack_store(BF16, float a, float b) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)a)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)b)) << 16);
+}
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

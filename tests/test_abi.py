@@ -77,7 +77,8 @@ def test_decode_plan(S, H, D, bs, L, req):
         assert pt == req
     assert parts == -(-L // pt)
     counters = -(-(S * H * 4) // 256) * 256           # one int32 per row, padded to 256 B
-    assert ws == (0 if parts == 1 else counters + S * H * parts * (D + 2) * 4)
+    ml = -(-(S * H * parts * 2) // 4) * 4                # (max, sum) floats, padded to 16 B
+    assert ws == (0 if parts == 1 else counters + (ml + S * H * parts * D) * 4)
     assert pk.decode_workspace_size(S, H, D, bs, L, 1, req) == ws
 
 

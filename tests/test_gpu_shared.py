@@ -44,9 +44,10 @@ def test_fork_tree_forced_short_partitions():
 
 
 def _direct_case(dtype, bs, H=4, D=128, seed=540):
-    """Hand-built tables: pairs with identical rows (so the shared run covers the
-    whole context: contexts 256 and 512 give rows whose only partitions are group
-    partitions), a pair that diverges inside a block, a group of 11 and a loner."""
+    """Hand-built tables: pairs with identical rows (the shared run stops one
+    token short of the context: 256 gives no group, 512 one group partition and a
+    single item of 256 tokens), a pair that diverges inside a block, a group of 11
+    and a loner."""
     rng = np.random.default_rng(seed)
     spec = [(256, "A"), (256, "A"), (512, "B"), (512, "B"), (1000, "C"), (300, "C"),
             (777, None), (0, None)] + [(600 + 37 * i, "D") for i in range(11)]

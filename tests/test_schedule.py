@@ -67,9 +67,10 @@ def _tables_after_step(wl):
     return tables, ctx
 
 
-def check_shared_schedule(d, tables, ctx, bs):
+def check_shared_schedule(d, tables, ctx, bs, max_members=16):
     """Every (sequence, token) covered once; partition indices 0..n-1 once per row with
-    one agreed n; group items only over blocks that all members share."""
+    one agreed n; group items only over blocks that all members share, with 2 to
+    max_members members (16 on the matrix cores, 8 for float32)."""
     pt = d["partition_tokens"]
     S = ctx.size
     cover = {s: [] for s in range(S)}      # (t0, ntok, part, nparts)
@@ -80,17 +81,22 @@ def check_shared_schedule(d, tables, ctx, bs):
         assert 0 < n <= pt
         cover[s].append((t0, n, p, npart))
     for moff, cnt, p, t0, n in d["groups"].tolist():
-        assert 2 <= cnt <= 8 and n == 256 and t0 == 256 * p
+        assert 2 <= cnt <= max_members and n == 256 and t0 == 256 * p
         mem = d["members"][moff:moff + cnt]
         b0, b1 = t0 // bs, (t0 + n + bs - 1) // bs
         lead = tables[mem[0, 0], b0:b1]
         for s, npart in mem.tolist():
             assert np.array_equal(tables[s, b0:b1], lead), "group over unshared blocks"
             cover[s].append((t0, n, p, npart))
+    grouped = {int(s) for s in d["members"][:, 0]} if len(d["members"]) else set()
     for s in range(S):
         if ctx[s] == 0:
             assert not cover[s]
             continue
+        if s in grouped:   # the row's last partition is a single item
+            assert max(cover[s])[0] + max(cover[s])[1] == ctx[s]
+            last = max(cover[s])
+            assert any(it[0] == s and it[2] == last[0] for it in d["items"].tolist())
         segs = sorted(cover[s])
         nparts = {c[3] for c in segs}
         assert nparts == {len(segs)}, (s, segs)
@@ -170,7 +176,8 @@ def test_shared_schedule_random_forks():
 
 
 def test_shared_schedule_groups_of_more_than_eight():
-    """20 forks of one prompt: members are cut into balanced chunks of at most 8."""
+    """20 forks of one prompt: members are cut into balanced chunks of at most 8
+    (float32) or 16 (16-bit storage, matrix cores)."""
     pk = _pk()
     bs = 16
     m = oracle.BlockPoolModel(2048, bs, list(range(2048)))
@@ -182,11 +189,15 @@ def test_shared_schedule_groups_of_more_than_eight():
         m.append_slot(s)
     tables = np.asarray(m.table_array(seqs, 64, 2047), np.int32)
     ctx = np.array([m.lens[s] for s in seqs], np.int32)
-    d = pk.decode_schedule_shared(ctx, tables, 8, 64, bs, 0, 0)
-    check_shared_schedule(d, tables, ctx, bs)
+    d = pk.decode_schedule_shared(ctx, tables, 8, 64, bs, 0, 0)      # float32: 8 per chunk
+    check_shared_schedule(d, tables, ctx, bs, max_members=8)
     cnts = sorted({tuple(g[:2]) for g in d["groups"].tolist()})
     assert [c for _, c in cnts] == [6, 7, 7]
     assert len(d["groups"]) == 3 * 3     # 768 shared tokens = 3 group partitions
+    d = pk.decode_schedule_shared(ctx, tables, 8, 64, bs, 2, 0)      # bfloat16: 16 per chunk
+    check_shared_schedule(d, tables, ctx, bs)
+    cnts = sorted({tuple(g[:2]) for g in d["groups"].tolist()})
+    assert [c for _, c in cnts] == [10, 10]
 
 
 def test_shared_schedule_errors():
