@@ -72,8 +72,12 @@ def build_state(wl, dtype, partition_tokens=0, extra_blocks=64):
     for op in wl.ops:
         if op[0] == "step":
             step_seqs = np.array(op[1], dtype=np.int64)
-    eng = PagedKVEngine(wl.NB, wl.H, wl.D, wl.bs, dtype, wl.max_blocks_per_seq + extra_blocks,
-                        len(step_seqs), free_order=wl.free_order, pad_block=wl.poison_block,
+    # growth blocks for the timed steps go after the workload's pool, so the
+    # workload's own placement is unchanged
+    NB = wl.NB + len(step_seqs) * extra_blocks
+    free_order = np.concatenate([wl.free_order, np.arange(wl.NB, NB, dtype=np.int32)])
+    eng = PagedKVEngine(NB, wl.H, wl.D, wl.bs, dtype, wl.max_blocks_per_seq + extra_blocks,
+                        len(step_seqs), free_order=free_order, pad_block=wl.poison_block,
                         fill=0.0, partition_tokens=partition_tokens)
     for op in wl.ops:
         if op[0] == "add":
@@ -153,6 +157,12 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--placement", choices=["random", "identity"], default="random",
+                    help="block placement: seeded random (the workloads) or in id order")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps, each after writing 1 GiB of scratch (MALL/L2 flushed)")
+    ap.add_argument("--read-gib", type=int, default=4,
+                    help="GiB for the plain streaming-read reference (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run 3 plain elementwise copies (neg) of this many MiB: a "
                          "known-size reference for the HBM traffic counters")
@@ -170,10 +180,10 @@ def main():
     torch.cuda.set_device(dev)
 
     t_setup = time.perf_counter()
-    wl = synth.make_workload(args.config, bs=args.bs)
+    wl = synth.make_workload(args.config, bs=args.bs, placement=args.placement)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.dtype]
     pt_req = args.partition_tokens or wl.partition_tokens
-    grow = args.warmup + args.steps
+    grow = args.warmup + 2 * args.steps + args.cold_steps
     eng, seqs = build_state(wl, tdt, pt_req, extra_blocks=-(-grow // wl.bs) + 1)
     from synth import to_torch as to_dev
     S = seqs.size
@@ -201,37 +211,51 @@ def main():
         eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:                      # create the HIP events before timing
-        a.record()
-        b.record()
+    # Loop 1, the steps themselves: nothing but the steps is enqueued (event
+    # markers around every decode would add their own gaps to each step).
     ncows, pts, ngroups = 0, set(), set()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        eng.set_decode_events(*evs[i])
         eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
         ncows += eng.last_info.num_cow
         pts.add(eng.last_info.partition_tokens)
         ngroups.add(eng.last_info.num_group_items)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+
+    # Loop 2, the decode launch of each step between HIP events recorded on the
+    # step's stream (the roofline figure); the same steps, continued.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:                      # create the HIP events before timing
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        eng.set_decode_events(*evs[i])
+        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
+        pts.add(eng.last_info.partition_tokens)
+        ngroups.add(eng.last_info.num_group_items)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
     eng.set_decode_events(None, None)
 
-    # each step appends one token to every sequence: the contexts of timed
-    # step i are the workload's step contexts + warmup + i
+    # each step appends one token to every sequence: the contexts of step i of
+    # loop 1 are the workload's step contexts + warmup + i, loop 2 continues
     ctxs = [wl.ctx + args.warmup + i for i in range(args.steps)]
+    ctxs2 = [wl.ctx + args.warmup + args.steps + i for i in range(args.steps)]
     elem = wl.elem_bytes
     total_step_bytes = sum(step_bytes(c, wl.H, wl.D, elem, wl.bs, 0) for c in ctxs) + \
         ncows * 2 * 2 * wl.H * wl.bs * wl.D * elem
-    dec_bytes = [decode_bytes(c, wl.H, wl.D, elem, wl.bs)[0] for c in ctxs]
-    # distinct blocks: timed steps only append, so step i's tables are a prefix
+    dec_bytes = [decode_bytes(c, wl.H, wl.D, elem, wl.bs)[0] for c in ctxs2]
+    # distinct blocks: the steps only append, so step i's tables are a prefix
     # of the final ones
     tables, _ = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
     uniq_bytes = [b - decode_bytes(c, wl.H, wl.D, elem, wl.bs)[1] +
                   unique_kv_bytes(tables, c, wl.H, wl.D, elem, wl.bs)
-                  for b, c in zip(dec_bytes, ctxs)]
+                  for b, c in zip(dec_bytes, ctxs2)]
     elapsed = t1 - t0
     ms_per_step = elapsed / args.steps * 1e3
     kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
@@ -249,13 +273,15 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_with_decode_events": round((t3 - t2) / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "storage_dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "seqs": int(S), "heads": wl.H, "head_dim": wl.D,
+        "config": {"workload": wl.name, "placement": args.placement, "seqs": int(S),
+                   "heads": wl.H, "head_dim": wl.D,
                    "block_size": wl.bs, "num_blocks": wl.NB,
                    "ctx_sum_first_step": int(ctxs[0].sum()),
                    "ctx_sum_last_step": int(ctxs[-1].sum()),
@@ -278,6 +304,100 @@ def main():
                      "algorithmic_bytes_per_launch": int(np.mean(uniq_bytes)),
                      "bytes_counted": "distinct blocks once (shared prefixes once)"},
     }
+    # cold decode: the same steps after a 1 GiB write (the 256 MB MALL and the
+    # L2s hold no K/V when the decode starts); decode events only
+    cold = None
+    if args.cold_steps > 0:
+        # write 1 GiB (the protocol's flush), then read another 1 GiB so the
+        # dirty lines are written back before, not during, the timed decode
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        clean = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_steps)]
+        for a, b in cev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for i in range(args.cold_steps):
+            scratch.fill_(i & 0xFF)
+            clean.sum()
+            eng.set_decode_events(*cev[i])
+            eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
+        torch.cuda.synchronize()
+        eng.set_decode_events(None, None)
+        ctables, _ = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
+        cms = np.array([a.elapsed_time(b) for a, b in cev]) * 1e3
+        c0 = args.warmup + 2 * args.steps
+        cbytes = [decode_bytes(wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)[0]
+                  for i in range(args.cold_steps)]
+        cuniq = [b - decode_bytes(wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)[1] +
+                 unique_kv_bytes(ctables, wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)
+                 for i, b in enumerate(cbytes)]
+        med = float(np.median(cms))
+        cold = {"steps": args.cold_steps, "flush": "1 GiB written, then 1 GiB of another "
+                                                    "buffer read, before each step",
+                "decode_us_median": round(med, 2),
+                "decode_us_p10_p90": [round(float(np.percentile(cms, 10)), 2),
+                                      round(float(np.percentile(cms, 90)), 2)],
+                "decode_gbps": round(float(np.mean(cuniq)) / (med * 1e-6) / 1e9, 2)}
+        del scratch, clean
+    res["decode_cold"] = cold
+
+    # achievable read: the library's plain streaming read over a large buffer
+    if args.read_gib > 0:
+        buf = torch.zeros(args.read_gib << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        pk.stream_read(buf, sink)
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(5)]
+        for a, b in rev:
+            a.record()
+            pk.stream_read(buf, sink)
+            b.record()
+        torch.cuda.synchronize()
+        best = min(a.elapsed_time(b) for a, b in rev) * 1e-3
+        rgbps = buf.numel() / best / 1e9
+        res["achievable_read"] = {"gbps": round(rgbps, 1), "bytes": buf.numel(),
+                                  "kernel": "stream_read_kernel (pa_stream_read), best of 5"}
+        res["roofline"]["frac_of_achievable_read"] = round(achieved / rgbps, 4)
+        del buf
+
+    # secondary: the cache write and the copy-on-write copy on their own
+    sec = {}
+    last = eng.last_step
+    slots_d = torch.from_numpy(last["slots"]).to(dev)
+    pk.cache_write(k_new, v_new, slots_d, eng.k_cache, eng.v_cache)
+
+    def per_call(fn, n=20):
+        """Seconds per call of n back-to-back calls between one pair of events
+        (markers around every call would cost more than these short kernels)."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
+
+    wt = per_call(lambda: pk.cache_write(k_new, v_new, slots_d, eng.k_cache, eng.v_cache))
+    sec["cache_write_us"] = round(wt * 1e6, 2)
+    sec["cache_write_gbps"] = round(4 * S * wl.H * wl.D * elem / wt / 1e9, 2)
+    sec["cache_write_tokens"] = int(S)
+    free = eng.bm.free_list()
+    npairs = min(56, len(free))
+    if npairs:
+        # copies into free blocks, from blocks in use (the copy-on-write pattern)
+        used = tables[:, 0]
+        pairs = np.stack([np.resize(used, npairs), np.array(free[:npairs])], 1).astype(np.int32)
+        pd = torch.from_numpy(pairs).to(dev)
+        pk.copy_blocks(eng.k_cache, eng.v_cache, pd)
+        ct = per_call(lambda: pk.copy_blocks(eng.k_cache, eng.v_cache, pd))
+        sec["copy_blocks_us"] = round(ct * 1e6, 2)
+        sec["copy_blocks_gbps"] = round(npairs * 2 * 2 * wl.H * wl.bs * wl.D * elem / ct / 1e9, 2)
+        sec["copy_pairs"] = int(npairs)
+    res["secondary"] = sec
+
     if not args.no_cpu_baseline:
         t = time.perf_counter()
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -16,7 +16,8 @@ import numpy as np
 __all__ = [
     "lib", "PAError", "cache_write", "copy_blocks", "decode", "decode_partitions",
     "decode_reduce", "decode_plan", "decode_workspace_size", "decode_schedule",
-    "decode_scheduled", "decode_schedule_shared", "decode_scheduled_shared", "BlockManager",
+    "decode_scheduled", "decode_schedule_shared", "decode_scheduled_shared", "stream_read",
+    "BlockManager",
     "DTYPE_CODES", "LIB_PATH",
 ]
 
@@ -76,6 +77,7 @@ _SIGNATURES = {
     "pa_engine_last_step": (_c.c_int, [_vp, _i32, _vp, _vp, _vp, _i32]),
     "pa_engine_set_decode_events": (_c.c_int, [_vp, _vp, _vp]),
     "pa_engine_set_sharing": (_c.c_int, [_vp, _i32]),
+    "pa_stream_read": (_c.c_int, [_vp, _i64, _vp, _i32, _vp]),
 }
 
 
@@ -259,6 +261,15 @@ def decode_schedule(context_lens_host, num_heads, head_dim, block_size, dtype_co
                                   _c.byref(n), _c.byref(pt), _c.byref(mx))
     _check(rc, "pa_decode_schedule")
     return items[:n.value], pt.value, mx.value
+
+
+def stream_read(buf, sink, waves=0, stream=None):
+    """pa_stream_read over the bytes of device tensor ``buf`` (plain streaming read;
+    the achievable-bandwidth reference).  ``sink``: device int32 tensor of >= 1."""
+    torch = _torch()
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().pa_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink", torch.int32), waves,
+                                _stream(stream, buf.device)), "pa_stream_read")
 
 
 def decode_schedule_shared(context_lens_host, block_tables_host, num_heads, head_dim,

@@ -105,6 +105,17 @@ struct Shape {
   static_assert(kLPT >= 4 && kLPT <= 64, "row width");
 };
 
+// Element d of a partial output is stored at (d % kVec) * kLPT + d / kVec:
+// lane col's element e (d = col * kVec + e) goes to e * kLPT + col, so one
+// store (or load) instruction over the lanes of a token row touches
+// consecutive words.  Agent-scope stores are written through to memory one
+// instruction at a time; contiguous words avoid partial-line writes.
+template <class DT, int D>
+__device__ __forceinline__ int part_pos(int d) {
+  constexpr int kVec = DT::kVec, kLPT = D / DT::kVec;
+  return (d % kVec) * kLPT + d / kVec;
+}
+
 __device__ __forceinline__ u32x4 load16(const char* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -150,7 +161,8 @@ struct ChunkCtx {
 // Issue the 2U 16-byte loads (K and V) of one chunk.  kMasked is the
 // partition's last, partial chunk: its loads are clamped to rows of groups
 // that hold valid tokens (no extra memory is touched and no table entry past
-// the partition is used) and ok[] marks the valid rows.
+// the partition is used) and ok[] marks the valid rows (chunk_apply zeroes
+// the others, so the loads stay in flight until the chunk is used).
 template <class DT, int D, int U, bool kMasked>
 __device__ __forceinline__ void chunk_load(const ChunkCtx& cx, int t0, u32x4 (&kr)[U],
                                            u32x4 (&vr)[U], bool (&ok)[U]) {
@@ -177,17 +189,18 @@ __device__ __forceinline__ void chunk_load(const ChunkCtx& cx, int t0, u32x4 (&k
   // fence the scheduler interleaves the dot products with the loads to save
   // registers, which serialises the memory latency.
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kMasked) {
-#pragma unroll
-    for (int i = 0; i < U; ++i) vr[i] = ok[i] ? vr[i] : u32x4{0, 0, 0, 0};
-  }
 }
 
 // q.k, online softmax update and P.V of one query over one loaded chunk.
 template <class DT, int D, int U, bool kMasked>
 __device__ __forceinline__ void chunk_apply(const ChunkCtx& cx, const u32x4 (&kr)[U],
-                                            const u32x4 (&vr)[U], const bool (&ok)[U], u32x4 qv,
+                                            const u32x4 (&vr_in)[U], const bool (&ok)[U], u32x4 qv,
                                             float& m, float& l, float* acc) {
+  // rows past the partition may hold anything (NaN included): their values
+  // are zeroed and their weights are 0
+  u32x4 vr[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) vr[i] = (!kMasked || ok[i]) ? vr_in[i] : u32x4{0, 0, 0, 0};
   using Sh = Shape<DT, D, U>;
   constexpr int kVec = DT::kVec;
   float sc[U];
@@ -270,10 +283,11 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, size_t row
       const int p = row + k * Sh::kTPI;
       const float w = __shfl(wl, min(p, kWave - 1), kWave);
       if (p < nparts) {
-        const float* po = P.ws_o + (pi0 + p) * D + col * kVec;
+        const float* po = P.ws_o + (pi0 + p) * D + col;
 #pragma unroll
         for (int e = 0; e < kVec; ++e)
-          O[e] += w * __hip_atomic_load(po + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          O[e] += w * __hip_atomic_load(po + e * Sh::kLPT, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     L = wl;
@@ -293,10 +307,11 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, size_t row
       const float lp = __hip_atomic_load(ml + 2 * p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const float w = lp * fast_exp2(mp - M);
       L += w;
-      const float* po = P.ws_o + (pi0 + p) * D + col * kVec;
+      const float* po = P.ws_o + (pi0 + p) * D + col;
 #pragma unroll
       for (int e = 0; e < kVec; ++e)
-        O[e] += w * __hip_atomic_load(po + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        O[e] += w * __hip_atomic_load(po + e * Sh::kLPT, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (row != 0) return;
@@ -342,18 +357,19 @@ __device__ __forceinline__ void finish(const DecodeParams& P, const size_t (&row
     any_split = true;
     if (row != 0) continue;
     const size_t pi = row_id[g] * P.max_parts + part;
-    float* o = P.ws_o + pi * D + col * kVec;
+    float* o = P.ws_o + pi * D + col;  // element e at e * kLPT (part_pos)
     if (fused) {
 #pragma unroll
       for (int e = 0; e < kVec; ++e)
-        __hip_atomic_store(o + e, acc[g][e] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(o + e * Sh::kLPT, acc[g][e] * inv, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       if (col == 0) {
         __hip_atomic_store(P.ws_ml + 2 * pi, m[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(P.ws_ml + 2 * pi + 1, l[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < kVec; ++e) o[e] = acc[g][e] * inv;
+      for (int e = 0; e < kVec; ++e) o[e * Sh::kLPT] = acc[g][e] * inv;
       if (col == 0) {
         P.ws_ml[2 * pi] = m[g];
         P.ws_ml[2 * pi + 1] = l[g];
@@ -482,19 +498,51 @@ __global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
   float acc[1][kVec];
 #pragma unroll
   for (int e = 0; e < kVec; ++e) acc[0][e] = 0.f;
+  // Two chunk buffers: the loads of the next chunk are in flight while one
+  // is computed.  Loads inside the loop are unconditional, so the compiler's
+  // wait counts stay exact (a load issued on one path only makes it wait for
+  // everything where the paths join); the last chunks are peeled.
   const int nfull = ntok / Sh::kChunk;
-  int c = 0;
-  for (; c < nfull; ++c) {
-    u32x4 kr[U], vr[U];
-    bool ok[U];
-    chunk_load<DT, D, U, false>(cx, c * Sh::kChunk, kr, vr, ok);
+  const bool tail = nfull * Sh::kChunk < ntok;
+  const int t_tail = nfull * Sh::kChunk;
+  u32x4 ka[U], va[U], kb[U], vb[U];
+  bool ok[U], okm[U];
+  auto apply_full = [&](const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
     chunk_apply<DT, D, U, false>(cx, kr, vr, ok, qv, m[0], l[0], acc[0]);
-  }
-  if (c * Sh::kChunk < ntok) {
-    u32x4 kr[U], vr[U];
-    bool ok[U];
-    chunk_load<DT, D, U, true>(cx, c * Sh::kChunk, kr, vr, ok);
-    chunk_apply<DT, D, U, true>(cx, kr, vr, ok, qv, m[0], l[0], acc[0]);
+  };
+  auto apply_tail = [&](const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
+    chunk_apply<DT, D, U, true>(cx, kr, vr, okm, qv, m[0], l[0], acc[0]);
+  };
+  if (nfull > 0) {
+    chunk_load<DT, D, U, false>(cx, 0, ka, va, ok);
+    int c = 0;
+    for (; c + 2 < nfull; c += 2) {  // a holds chunk c
+      chunk_load<DT, D, U, false>(cx, (c + 1) * Sh::kChunk, kb, vb, ok);
+      apply_full(ka, va);
+      chunk_load<DT, D, U, false>(cx, (c + 2) * Sh::kChunk, ka, va, ok);
+      apply_full(kb, vb);
+    }
+    // a holds chunk c; one or two full chunks remain, then maybe the tail
+    if (c + 1 < nfull) {
+      chunk_load<DT, D, U, false>(cx, (c + 1) * Sh::kChunk, kb, vb, ok);
+      apply_full(ka, va);
+      if (tail) {
+        chunk_load<DT, D, U, true>(cx, t_tail, ka, va, okm);
+        apply_full(kb, vb);
+        apply_tail(ka, va);
+      } else {
+        apply_full(kb, vb);
+      }
+    } else if (tail) {
+      chunk_load<DT, D, U, true>(cx, t_tail, kb, vb, okm);
+      apply_full(ka, va);
+      apply_tail(kb, vb);
+    } else {
+      apply_full(ka, va);
+    }
+  } else {
+    chunk_load<DT, D, U, true>(cx, 0, ka, va, okm);
+    apply_tail(ka, va);
   }
   merge_rows<DT, D, U>(m[0], l[0], acc[0]);
   const size_t rows[1] = {row_id};
@@ -770,13 +818,9 @@ __global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParam
     const size_t pi = row_q * P.max_parts + part;
     float* po = P.ws_o + pi * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int h4 = 0; h4 < NJ / 4; ++h4) {
-        const f32x4 w = f32x4{o[4 * h4][r], o[4 * h4 + 1][r], o[4 * h4 + 2][r], o[4 * h4 + 3][r]} * inv;
-        *reinterpret_cast<f32x4*>(po + NJ * (4 * g + r) + 4 * h4) = w;
-      }
-    }
+      for (int jd = 0; jd < NJ; ++jd) po[part_pos<DT, D>(NJ * (4 * g + r) + jd)] = o[jd][r] * inv;
     if (g == 0) {
       P.ws_ml[2 * pi] = m;
       P.ws_ml[2 * pi + 1] = l;

@@ -200,7 +200,15 @@ class Workload:
         return int(self.ctx.sum()) * self.H * self.D * 2 * self.elem_bytes
 
 
+_IDENTITY = [False]
+
+
 def _placement(cfg: int, NB: int, sub: int = 0):
+    """(poison block, free-list order).  Seeded random placement, or with
+    ``placement="identity"`` in make_workload the blocks in id order (each
+    sequence's blocks contiguous and ascending), the poison block last."""
+    if _IDENTITY[0]:
+        return NB - 1, np.arange(NB - 1, dtype=np.int32)
     perm = _rng(cfg, _STREAM_PLACE, sub).permutation(NB).astype(np.int32)
     return int(perm[-1]), perm[:-1].copy()
 
@@ -293,18 +301,28 @@ def config5_ctx() -> np.ndarray:
 
 
 def make_workload(cfg: int, bs: int | None = None, cow: bool = False,
-                  S: int | None = None, values: bool = True) -> Workload:
+                  S: int | None = None, values: bool = True,
+                  placement: str = "random") -> Workload:
     """Build workload ``cfg`` (1..5).
 
     ``bs`` selects the block size of the config-5 sweep; ``cow`` selects the
     copy-on-write variant of config 4; ``S`` (config 5 only) keeps the first S
     sequences, for smaller CPU-side cases; ``values=False`` skips the K/V
-    draws (only the shapes and the op script are built)."""
+    draws (only the shapes and the op script are built); ``placement``
+    "identity" hands out blocks in id order (contiguous tables: the
+    indirection's cost is measured against it)."""
+    if placement not in ("random", "identity"):
+        raise ValueError(placement)
     _VALUES[0] = bool(values)
+    _IDENTITY[0] = placement == "identity"
     try:
-        return _make(cfg, bs, cow, S)
+        wl = _make(cfg, bs, cow, S)
+        if _IDENTITY[0]:
+            wl.name += "-identity"
+        return wl
     finally:
         _VALUES[0] = True
+        _IDENTITY[0] = False
 
 
 def make_custom(seed: int, H: int, D: int, dtype: str, bs: int, ctx, NB: int | None = None,

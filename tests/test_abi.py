@@ -64,6 +64,11 @@ def test_host_side_argument_checks_enqueue_nothing():
     assert lib.pa_decode(*args) == -5          # split plan, no workspace: rejected on the host
     args[17] = 48                              # partition not a multiple of 32
     assert lib.pa_decode(*args) == -1
+    # streaming read: zero bytes is a no-op; sizes must be whole 8 KiB chunks
+    assert lib.pa_stream_read(None, 0, None, 0, None) == 0
+    assert lib.pa_stream_read(256, 8192 + 16, 512, 0, None) == -1
+    assert lib.pa_stream_read(None, 8192, 512, 0, None) == -1
+    assert lib.pa_stream_read(264, 8192, 512, 0, None) == -1     # src not 16-byte aligned
 
 
 @pytest.mark.parametrize("S,H,D,bs,L,req", [(30, 40, 128, 16, 2048, 0), (8, 40, 128, 16, 4096, 512),
