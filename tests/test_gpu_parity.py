@@ -82,6 +82,24 @@ def test_kernel_instances(dtype, D, bs):
     compare_outputs(g2["out"], r["out"], what=f"{wl.name} split pt={pt}", cast_dtype=dtype)
 
 
+# ------------------------------------------------------------ size extremes
+def test_long_context_many_partitions():
+    """One ~100k-token context next to short ones (automatic partitions: ~98 of
+    1024 tokens, the merge's path for more partitions than lanes) and a 16k one."""
+    synth.cache_draws(False)
+    wl = synth.make_custom(700, 2, 128, "f16", 16, [100003, 1, 16384, 77])
+    _check_workload(wl, cast_bound=True)
+
+
+def test_many_sequences():
+    """4096 sequences of 1 to 40 tokens: 8192 rows, ragged tails, the work list
+    longest first."""
+    synth.cache_draws(False)
+    ctx = (np.arange(4096) % 40) + 1
+    wl = synth.make_custom(701, 2, 64, "bf16", 8, ctx)
+    _check_workload(wl, cast_bound=True)
+
+
 # ---------------------------------------------------------- exact probes
 def _scatter_direct(ks, vs, H, D, dtype, bs, NB, free_order, poison, fill=float("nan")):
     """Build a pool with the library from contiguous per-sequence K/V (host arrays)."""
