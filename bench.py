@@ -147,6 +147,52 @@ def load_traffic(kernel_tag):
     return rec.get("traffic_bytes_per_launch")
 
 
+def contiguous_compare(eng, seqs, q, wl, torch, pk, per_call):
+    """Paged decode vs the same decode over the same K/V in contiguous layouts,
+    [S, L, H, D] (token-major) and [S, H, L, D] (head-major): same contexts,
+    same work list, 20 back-to-back calls each.  The contiguous copies are
+    gathered from the pool with torch indexing (set-up, outside the timing)."""
+    tables, ctx = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
+    dev = q.device
+    S, bs = len(seqs), wl.bs
+    nb = int(-(-int(ctx.max()) // bs))
+    tab = torch.from_numpy(tables[:, :nb].astype(np.int64)).to(dev)
+    L = nb * bs
+    code = pk.DTYPE_CODES()[q.dtype]
+    pt = eng.last_info.partition_tokens
+    items, pt2, mx = pk.decode_schedule(ctx, wl.H, wl.D, bs, code, pt)
+    items_c, ptc, _ = pk.decode_schedule(ctx, wl.H, wl.D, 16, code, pt)
+    di, dic = torch.from_numpy(items).to(dev), torch.from_numpy(items_c).to(dev)
+    dt_, dc = torch.from_numpy(tables).to(dev), torch.from_numpy(ctx).to(dev)
+    ws = torch.zeros(max(pk.decode_workspace_size(S, wl.H, wl.D, bs, mx, code, pt2),
+                         pk.decode_workspace_size(S, wl.H, wl.D, 16, mx, code, ptc), 16),
+                     dtype=torch.uint8, device=dev)
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    paged = lambda: pk.decode_scheduled(q, eng.k_cache, eng.v_cache, dt_, dc, wl.scale, mx, di,
+                                        pt2, out=o1, workspace=ws)
+    paged()
+    tp = per_call(paged)
+    kv = decode_bytes(ctx, wl.H, wl.D, wl.elem_bytes, bs)[0]
+    res = {"partition_tokens": int(ptc), "paged_decode_us": round(tp * 1e6, 2),
+           "paged_gbps": round(kv / tp / 1e9, 1),
+           "timing": "20 back-to-back calls between one pair of events, each"}
+    for layout, perm in (("SLHD", (0, 1, 3, 2, 4)), ("SHLD", (0, 2, 1, 3, 4))):
+        def gather(cache):              # [NB, H, bs, D] -> [S, nb, H, bs, D] -> layout
+            g = cache[tab].permute(*perm)
+            shape = (S, L, wl.H, wl.D) if layout == "SLHD" else (S, wl.H, L, wl.D)
+            return g.reshape(shape).contiguous()
+        kc, vc = gather(eng.k_cache), gather(eng.v_cache)
+        contig = lambda: pk.decode_contiguous(q, kc, vc, dc, wl.scale, mx, layout=layout,
+                                              out=o2, workspace=ws, partition_tokens=ptc,
+                                              items=dic)
+        contig()
+        tc = per_call(contig)
+        res[layout] = {"decode_us": round(tc * 1e6, 2), "gbps": round(kv / tc / 1e9, 1),
+                       "paged_time_over_contiguous": round(tp / tc, 4)}
+        del kc, vc
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +209,9 @@ def main():
                     help="extra steps, each after writing 1 GiB of scratch (MALL/L2 flushed)")
     ap.add_argument("--read-gib", type=int, default=4,
                     help="GiB for the plain streaming-read reference (0 = skip)")
+    ap.add_argument("--contiguous", action="store_true",
+                    help="also time the decode over the same K/V gathered into a contiguous "
+                         "[S, L, H, D] layout (pa_decode_contiguous) next to the paged decode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run 3 plain elementwise copies (neg) of this many MiB: a "
                          "known-size reference for the HBM traffic counters")
@@ -397,6 +446,9 @@ def main():
         sec["copy_blocks_gbps"] = round(npairs * 2 * 2 * wl.H * wl.bs * wl.D * elem / ct / 1e9, 2)
         sec["copy_pairs"] = int(npairs)
     res["secondary"] = sec
+
+    if args.contiguous:
+        res["contiguous"] = contiguous_compare(eng, seqs, q, wl, torch, pk, per_call)
 
     if not args.no_cpu_baseline:
         t = time.perf_counter()

@@ -41,6 +41,7 @@ __all__ = [
     "oracle_copy_blocks", "BlockPoolModel", "kv_cache_bytes",
     "kv_bytes_per_token", "useful_kv_fraction", "run_workload",
     "attention_brute_force",
+    "oracle_decode_contiguous",
 ]
 
 
@@ -141,6 +142,29 @@ def oracle_decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype,
             if return_weights:
                 weights[(s, h)] = w
     return (out, weights) if return_weights else out
+
+
+def oracle_decode_contiguous(q, k, v, context_lens, scale, dtype, layout="SLHD"):
+    """Decode over non-paged K/V (polomodov.tech "vLLM and PagedAttention"
+    slide 19 compares the paged kernel with this; brentwoodlivery "5.3.18", the
+    card saying paging leaves the attention arithmetic unchanged): for each
+    sequence s and head h, attention of q[s,h] over the first context_lens[s]
+    token rows of k[s] / v[s], laid out [S, L, H, D] ("SLHD") or [S, H, L, D]
+    ("SHLD").  A zero context gives a zero row.  Returns float64 [S, H, D]."""
+    S, H, D = q.shape
+    out = np.zeros((S, H, D))
+    qf = widen(q, dtype)
+    for s in range(S):
+        L = int(context_lens[s])
+        if L == 0:
+            continue
+        ks = widen(k[s, :L] if layout == "SLHD" else k[s, :, :L], dtype)
+        vs = widen(v[s, :L] if layout == "SLHD" else v[s, :, :L], dtype)
+        for h in range(H):
+            kh = ks[:, h, :] if layout == "SLHD" else ks[h]
+            vh = vs[:, h, :] if layout == "SLHD" else vs[h]
+            out[s, h] = attention_one(qf[s, h], kh, vh, scale)[0]
+    return out
 
 
 def attention_brute_force(q, K, V, scale):

@@ -17,6 +17,7 @@ __all__ = [
     "lib", "PAError", "cache_write", "copy_blocks", "decode", "decode_partitions",
     "decode_reduce", "decode_plan", "decode_workspace_size", "decode_schedule",
     "decode_scheduled", "decode_schedule_shared", "decode_scheduled_shared", "stream_read",
+    "decode_contiguous",
     "BlockManager",
     "DTYPE_CODES", "LIB_PATH",
 ]
@@ -78,6 +79,9 @@ _SIGNATURES = {
     "pa_engine_set_decode_events": (_c.c_int, [_vp, _vp, _vp]),
     "pa_engine_set_sharing": (_c.c_int, [_vp, _i32]),
     "pa_stream_read": (_c.c_int, [_vp, _i64, _vp, _i32, _vp]),
+    "pa_decode_contiguous": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64,
+                                        _i64, _f32, _i32, _i32, _vp, _vp, _sz, _i32, _vp, _vp,
+                                        _i32]),
 }
 
 
@@ -261,6 +265,47 @@ def decode_schedule(context_lens_host, num_heads, head_dim, block_size, dtype_co
                                   _c.byref(n), _c.byref(pt), _c.byref(mx))
     _check(rc, "pa_decode_schedule")
     return items[:n.value], pt.value, mx.value
+
+
+def decode_contiguous(q, k, v, context_lens, scale, max_context_len, layout="SLHD", out=None,
+                      workspace=None, partition_tokens=0, items=None, stream=None):
+    """pa_decode_contiguous over non-paged K/V: ``layout`` "SLHD" ([S, L, H, D]) or
+    "SHLD" ([S, H, L, D]); ``items`` an optional device work list from
+    decode_schedule(..., block_size=16, ...)."""
+    torch = _torch()
+    S, H, D = q.shape
+    if k.shape != v.shape or k.dim() != 4 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k, v must be 4-d tensors of q's dtype with equal shapes")
+    if layout == "SLHD":
+        if (k.shape[0], k.shape[2], k.shape[3]) != (S, H, D):
+            raise ValueError("k must be [S, L, H, D]")
+        L = int(k.shape[1])
+        strides = (L * H * D, H * D, D)
+    elif layout == "SHLD":
+        if (k.shape[0], k.shape[1], k.shape[3]) != (S, H, D):
+            raise ValueError("k must be [S, H, L, D]")
+        L = int(k.shape[2])
+        strides = (H * L * D, D, L * D)
+    else:
+        raise ValueError(layout)
+    if context_lens.shape != (S,):
+        raise ValueError("context_lens must be [S]")
+    if out is None:
+        out = torch.empty_like(q)
+    dt = _dt(q)
+    ws_need = decode_workspace_size(S, H, D, 16, int(max_context_len), dt, partition_tokens)
+    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
+        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    n = int(items.shape[0]) if items is not None else 0
+    rc = lib().pa_decode_contiguous(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(context_lens, "context_lens", torch.int32),
+        S, H, D, strides[0], strides[1], strides[2], L, float(scale), int(max_context_len), dt,
+        _dev(out, "out"), ws_ptr, ws_bytes, int(partition_tokens), _stream(stream, q.device),
+        _dev(items, "items", torch.int32) if items is not None else None, n)
+    _check(rc, "pa_decode_contiguous")
+    return out
 
 
 def stream_read(buf, sink, waves=0, stream=None):

@@ -94,6 +94,10 @@ struct DecodeParams {
   int window_tokens;  // partition window of the launch (table entries loaded per wave)
   int max_parts;      // partition stride of the workspace
   float qk_scale;     // scale * log2(e)
+  // contiguous (non-paged) K/V: token t of sequence s, head h at element
+  // s * stride_s + t * stride_t + h * stride_h; max_tokens bounds t
+  bool contig;
+  int64_t stride_s, stride_t, stride_h, max_tokens;
 };
 
 template <class DT, int D, int U>
@@ -156,6 +160,12 @@ struct ChunkCtx {
   int ntok;            // tokens in the partition
   int last_group;      // first token of the last group holding a valid token
   float qk_scale;
+  // contiguous layout: the partition's first token row of this (s, h), the
+  // distance between token rows, and this lane's byte offset in a row group
+  const char* kbase;
+  const char* vbase;
+  uint64_t row_stride;
+  uint64_t lane_off_c;
 };
 
 // Issue the 2U 16-byte loads (K and V) of one chunk.  kMasked is the
@@ -163,7 +173,7 @@ struct ChunkCtx {
 // that hold valid tokens (no extra memory is touched and no table entry past
 // the partition is used) and ok[] marks the valid rows (chunk_apply zeroes
 // the others, so the loads stay in flight until the chunk is used).
-template <class DT, int D, int U, bool kMasked>
+template <class DT, int D, int U, bool kMasked, bool kContig = false>
 __device__ __forceinline__ void chunk_load(const ChunkCtx& cx, int t0, u32x4 (&kr)[U],
                                            u32x4 (&vr)[U], bool (&ok)[U]) {
   using Sh = Shape<DT, D, U>;
@@ -172,11 +182,21 @@ __device__ __forceinline__ void chunk_load(const ChunkCtx& cx, int t0, u32x4 (&k
   for (int i = 0; i < U; ++i) {
     int tt = t0 + i * Sh::kTPI;  // wave-uniform token offset in the partition
     uint32_t off = cx.lane_off;
+    uint64_t off_c = cx.lane_off_c;
     ok[i] = true;
     if constexpr (kMasked) {
       ok[i] = tt + cx.row < cx.ntok;
       tt = min(tt, cx.last_group);
-      if (tt + cx.row >= cx.ntok) off = cx.lane_off - uint32_t(cx.row) * kRowBytes;  // row 0
+      if (tt + cx.row >= cx.ntok) {  // row 0 of the group
+        off = cx.lane_off - uint32_t(cx.row) * kRowBytes;
+        off_c = cx.lane_off_c - uint64_t(cx.row) * cx.row_stride;
+      }
+    }
+    if constexpr (kContig) {
+      const uint64_t rows = uint64_t(tt) * cx.row_stride + off_c;
+      kr[i] = load_stream(cx.kbase + rows);
+      vr[i] = load_stream(cx.vbase + rows);
+      continue;
     }
     const int pb = __builtin_amdgcn_readlane(cx.tbl, tt >> cx.log2_bs);
     // (block, head) tile index fits 32 bits; tiles are a power of two in size
@@ -405,7 +425,7 @@ __device__ __forceinline__ void finish(const DecodeParams& P, const size_t (&row
 }
 
 // Table entries of a partition window, one per lane, and the chunk context.
-template <class DT, int D, int U>
+template <class DT, int D, int U, bool kContig = false>
 __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h, int t0,
                                              int lane) {
   using Sh = Shape<DT, D, U>;
@@ -413,6 +433,21 @@ __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h
   constexpr int kLog2Row = __builtin_ctz(kRowBytes);
   const int row = lane / Sh::kLPT;
   const int col = lane % Sh::kLPT;
+  ChunkCtx cx;
+  if constexpr (kContig) {
+    constexpr uint64_t kElem = sizeof(typename DT::T);
+    const uint64_t first = (uint64_t(s) * uint64_t(P.stride_s) + uint64_t(h) * uint64_t(P.stride_h) +
+                            uint64_t(t0) * uint64_t(P.stride_t)) * kElem;
+    cx.kbase = reinterpret_cast<const char*>(P.k_cache) + first;
+    cx.vbase = reinterpret_cast<const char*>(P.v_cache) + first;
+    cx.row_stride = uint64_t(P.stride_t) * kElem;
+    cx.lane_off_c = uint64_t(row) * cx.row_stride + uint64_t(col) * 16u;
+    cx.row = row;
+    cx.ntok = 0;
+    cx.last_group = 0;
+    cx.qk_scale = P.qk_scale;
+    return cx;
+  }
   const int blk0 = t0 >> P.log2_bs;
   // The whole window is loaded speculatively, in parallel with what decides
   // its length: entries past the partition are loaded as integers but never
@@ -420,7 +455,6 @@ __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h
   int tbl = 0;
   if (lane < (P.window_tokens >> P.log2_bs) && blk0 + lane < P.maxB)
     tbl = P.block_tables[size_t(s) * P.maxB + blk0 + lane];
-  ChunkCtx cx;
   cx.kc = reinterpret_cast<const char*>(P.k_cache);
   cx.vc = reinterpret_cast<const char*>(P.v_cache);
   cx.log2_tile = kLog2Row + P.log2_bs;
@@ -434,12 +468,14 @@ __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h
   cx.ntok = 0;
   cx.last_group = 0;
   cx.qk_scale = P.qk_scale;
+  cx.kbase = cx.vbase = nullptr;
+  cx.row_stride = cx.lane_off_c = 0;
   return cx;
 }
 
 // One wave per (sequence, head, partition): grid order from context_lens, or
 // a host-scheduled work list of single items.
-template <class DT, int D, int U>
+template <class DT, int D, int U, bool kContig = false>
 __global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
   using T = typename DT::T;
   using Sh = Shape<DT, D, U>;
@@ -468,15 +504,16 @@ __global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
   const int h = hg * kWaves + wave;
   if (h >= H) return;
   const size_t row_id = size_t(s) * H + h;
-  ChunkCtx cx = make_ctx<DT, D, U>(P, s, h, t0, lane);
+  ChunkCtx cx = make_ctx<DT, D, U, kContig>(P, s, h, t0, lane);
   int ntok, nparts;
   if (it != nullptr) {
     ntok = it[3];
     nparts = it[4];
   } else {
     int ctx = P.context_lens[s];
-    // never read past the table row or past the launched partitions
-    ctx = min(ctx, min(P.maxB << P.log2_bs, P.max_parts * P.part_tokens));
+    // never read past the table row (the token axis) or the launched partitions
+    const int cap = kContig ? int(min(P.max_tokens, int64_t(1) << 30)) : (P.maxB << P.log2_bs);
+    ctx = min(ctx, min(cap, P.max_parts * P.part_tokens));
     nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
     ntok = part < nparts ? min(P.part_tokens, ctx - t0) : 0;
   }
@@ -514,34 +551,34 @@ __global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
     chunk_apply<DT, D, U, true>(cx, kr, vr, okm, qv, m[0], l[0], acc[0]);
   };
   if (nfull > 0) {
-    chunk_load<DT, D, U, false>(cx, 0, ka, va, ok);
+    chunk_load<DT, D, U, false, kContig>(cx, 0, ka, va, ok);
     int c = 0;
     for (; c + 2 < nfull; c += 2) {  // a holds chunk c
-      chunk_load<DT, D, U, false>(cx, (c + 1) * Sh::kChunk, kb, vb, ok);
+      chunk_load<DT, D, U, false, kContig>(cx, (c + 1) * Sh::kChunk, kb, vb, ok);
       apply_full(ka, va);
-      chunk_load<DT, D, U, false>(cx, (c + 2) * Sh::kChunk, ka, va, ok);
+      chunk_load<DT, D, U, false, kContig>(cx, (c + 2) * Sh::kChunk, ka, va, ok);
       apply_full(kb, vb);
     }
     // a holds chunk c; one or two full chunks remain, then maybe the tail
     if (c + 1 < nfull) {
-      chunk_load<DT, D, U, false>(cx, (c + 1) * Sh::kChunk, kb, vb, ok);
+      chunk_load<DT, D, U, false, kContig>(cx, (c + 1) * Sh::kChunk, kb, vb, ok);
       apply_full(ka, va);
       if (tail) {
-        chunk_load<DT, D, U, true>(cx, t_tail, ka, va, okm);
+        chunk_load<DT, D, U, true, kContig>(cx, t_tail, ka, va, okm);
         apply_full(kb, vb);
         apply_tail(ka, va);
       } else {
         apply_full(kb, vb);
       }
     } else if (tail) {
-      chunk_load<DT, D, U, true>(cx, t_tail, kb, vb, okm);
+      chunk_load<DT, D, U, true, kContig>(cx, t_tail, kb, vb, okm);
       apply_full(ka, va);
       apply_tail(kb, vb);
     } else {
       apply_full(ka, va);
     }
   } else {
-    chunk_load<DT, D, U, true>(cx, 0, ka, va, okm);
+    chunk_load<DT, D, U, true, kContig>(cx, 0, ka, va, okm);
     apply_tail(ka, va);
   }
   merge_rows<DT, D, U>(m[0], l[0], acc[0]);
@@ -920,7 +957,11 @@ static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t
     case Launch::kSingles: {
       const dim3 grid = p.items ? dim3(unsigned(n) * unsigned(ngroups), 1, 1)
                                 : dim3(ngroups, p.max_parts, S);
-      hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
+      if (p.contig)
+        hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll, true>), grid, dim3(kThreads), 0,
+                           st, p);
+      else
+        hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
       break;
     }
     case Launch::kReduce:
@@ -943,8 +984,14 @@ static void dispatch(Launch what, int32_t dtype, int32_t D, const DecodeParams& 
 
 enum { kDoPartitions = 1, kDoReduce = 2, kFused = 4 };
 
+struct Contig {
+  bool on = false;
+  int64_t stride_s = 0, stride_t = 0, stride_h = 0, max_tokens = 0;
+};
+
 struct Schedule {
   bool scheduled = false;  // work lists given (else grid order)
+  Contig contig;           // contiguous K/V instead of blocks
   const int32_t* items = nullptr;
   int32_t num_items = 0;
   const int32_t* group_items = nullptr;
@@ -964,9 +1011,18 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
                      shared ? kSharedPartTokens : 0);
   if (rc != PA_OK) return rc;
   if (S == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_INVALID;
-  if (maxB <= 0 || NB <= 0) return PA_ERR_INVALID;
-  if (uint64_t(NB) * uint64_t(H) > 0xFFFFFFFFull) return PA_ERR_UNSUPPORTED;  // 32-bit tile index
+  const Contig& cg = sched.contig;
+  if (!q || !k_cache || !v_cache || (!block_tables && !cg.on) || !context_lens || !out)
+    return PA_ERR_INVALID;
+  if (cg.on) {
+    const int64_t eb = elem_bytes(dtype);
+    if (cg.max_tokens <= 0 || cg.stride_s < 0 || cg.stride_t <= 0 || cg.stride_h < 0 ||
+        (cg.stride_s * eb) % 16 || (cg.stride_t * eb) % 16 || (cg.stride_h * eb) % 16)
+      return PA_ERR_INVALID;
+  } else {
+    if (maxB <= 0 || NB <= 0) return PA_ERR_INVALID;
+    if (uint64_t(NB) * uint64_t(H) > 0xFFFFFFFFull) return PA_ERR_UNSUPPORTED;  // 32-bit tile index
+  }
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return PA_ERR_INVALID;
   if (shared && (kSharedPartTokens % bs != 0 || !sched.group_members)) return PA_ERR_INVALID;
@@ -996,7 +1052,13 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.window_tokens = plan.part_tokens;
   p.max_parts = plan.max_parts;
   p.qk_scale = scale * kLog2e;
+  p.contig = cg.on;
+  p.stride_s = cg.stride_s;
+  p.stride_t = cg.stride_t;
+  p.stride_h = cg.stride_h;
+  p.max_tokens = cg.max_tokens;
   if (shared && !p.counters) return PA_ERR_INVALID;  // groups need the one-launch merge
+  if (shared && cg.on) return PA_ERR_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (what & kDoPartitions) {
@@ -1273,6 +1335,34 @@ int pa_decode_scheduled_shared(PA_DECODE_ARGS, const int32_t* items, int32_t num
   sc.num_group_items = num_group_items;
   sc.group_members = members;
   return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, PA_DECODE_PASS, sc);
+}
+
+// Contiguous (non-paged) K/V: the same decode with token rows addressed by
+// strides instead of the block table.  Partitions follow the rules of a
+// 16-token block size (multiples of 32 up to 1024 tokens).
+int pa_decode_contiguous(const void* q, const void* k, const void* v, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                         int64_t stride_seq, int64_t stride_token, int64_t stride_head,
+                         int64_t max_tokens, float scale, int32_t max_context_len, int32_t dtype,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         int32_t partition_tokens, void* stream, const int32_t* items,
+                         int32_t num_items) {
+  if (num_seqs > 0 && ((items && num_items <= 0) || (!items && num_items != 0)))
+    return PA_ERR_INVALID;
+  if (max_context_len > max_tokens) return PA_ERR_INVALID;
+  pa::Schedule sc;
+  sc.scheduled = items != nullptr;
+  sc.items = items;
+  sc.num_items = num_items;
+  sc.contig.on = true;
+  sc.contig.stride_s = stride_seq;
+  sc.contig.stride_t = stride_token;
+  sc.contig.stride_h = stride_head;
+  sc.contig.max_tokens = max_tokens;
+  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, q, k, v, nullptr, 1,
+                         context_lens, num_seqs, num_heads, head_dim, 16, 1, scale,
+                         max_context_len, dtype, out, workspace, workspace_bytes,
+                         partition_tokens, stream, sc);
 }
 
 }  // extern "C"

@@ -161,3 +161,20 @@ def check_workload(wl, seqs=None, partition_tokens=0, tol=TOL, compare_pools=Tru
     err = compare_outputs(g["out"], r["out"], seqs=seqs, tol=tol, what=wl.name,
                           cast_dtype=wl.dtype if cast_bound else None)
     return g, r, err
+
+
+def contiguous_kv(wl, ctx, layout):
+    """The logical K/V of every sequence as drawn, in a contiguous [S, L, H, D] or
+    [S, H, L, D] array (rows past a context are NaN)."""
+    L = int(max(ctx.max(), 1))
+    dt = synth.DTYPES[wl.dtype][0]
+    nan = 0x7FC0 if wl.dtype == "bf16" else np.nan
+    k = np.full((wl.S, L, wl.H, wl.D), nan, dtype=dt)
+    v = k.copy()
+    for s in range(wl.S):
+        ks, vs = wl.kv(s, 0, int(ctx[s]))
+        k[s, :int(ctx[s])] = ks
+        v[s, :int(ctx[s])] = vs
+    if layout == "SHLD":
+        k, v = np.ascontiguousarray(k.transpose(0, 2, 1, 3)), np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    return k, v

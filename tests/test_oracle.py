@@ -11,6 +11,7 @@ import pytest
 import scipy.special
 
 import oracle
+from gpu_harness import contiguous_kv
 import synth
 from oracle import paged_attention as pa
 
@@ -242,6 +243,37 @@ def test_fork_tree_decode_equals_unpaged_attention(seed, bs):
             e = np.exp(logits - logits.max())
             want = (e / e.sum()) @ v[:, h, :].astype(np.float64)
             assert np.array_equal(r["out"][row, h], want)
+
+
+@pytest.mark.parametrize("layout", ["SLHD", "SHLD"])
+def test_contiguous_decode_equals_paged(layout):
+    """Non-paged decode on the K/V as drawn == the paged decode on the pool built
+    by the op script, bit for bit (the gather is exact, the arithmetic the same)."""
+    wl = synth.make_workload(1)
+    r = oracle.run_workload(wl)
+    k, v = contiguous_kv(wl, r["ctx"], layout)
+    got = oracle.oracle_decode_contiguous(wl.q, k, v, r["ctx"], wl.scale, wl.dtype, layout)
+    assert np.array_equal(got, r["out"])
+
+
+def test_contiguous_decode_closed_forms():
+    """ctx = 1 gives V_0 exactly; q = 0 gives the mean of V; ctx = 0 a zero row;
+    both layouts agree bit for bit."""
+    rng = np.random.default_rng(5)
+    S, L, H, D = 3, 7, 2, 4
+    k = rng.normal(size=(S, L, H, D)).astype(np.float32)
+    v = rng.normal(size=(S, L, H, D)).astype(np.float32)
+    q = rng.normal(size=(S, H, D)).astype(np.float32)
+    q[2] = 0.0
+    ctx = np.array([1, 0, 7])
+    a = oracle.oracle_decode_contiguous(q, k, v, ctx, 0.5, "f32", "SLHD")
+    b = oracle.oracle_decode_contiguous(q, np.ascontiguousarray(k.transpose(0, 2, 1, 3)),
+                                        np.ascontiguousarray(v.transpose(0, 2, 1, 3)), ctx, 0.5,
+                                        "f32", "SHLD")
+    assert np.array_equal(a, b)
+    assert np.array_equal(a[0], v[0, 0].astype(np.float64))
+    assert np.array_equal(a[1], np.zeros((H, D)))
+    np.testing.assert_allclose(a[2], v[2].astype(np.float64).mean(axis=0), rtol=0, atol=1e-15)
 
 
 def test_cache_write_places_every_token():
