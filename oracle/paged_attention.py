@@ -315,6 +315,14 @@ def run_workload(wl, decode=True, decode_seqs=None, fill=None):
             oracle_cache_write(k, v, bm.slots(seq, 0, n), k_cache, v_cache)
         elif kind == "fork":
             bm.fork(op[1], op[2])
+        elif kind == "free":
+            bm.free_seq(op[1])
+        elif kind == "select":
+            # beam selection: every (parent, child) fork, then the retired frees
+            for parent, child in op[1]:
+                bm.fork(parent, child)
+            for seq in op[2]:
+                bm.free_seq(seq)
         elif kind == "extend":
             _, seq, n = op
             for _ in range(n):

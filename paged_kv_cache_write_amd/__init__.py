@@ -60,6 +60,7 @@ _SIGNATURES = {
     "pa_bm_append_slots": (_c.c_int, [_vp, _vp, _i32, _vp, _vp, _pi32, _pi32]),
     "pa_bm_step": (_c.c_int, [_vp, _vp, _i32, _vp, _vp, _pi32, _vp, _i32, _i32, _vp]),
     "pa_bm_free_seq": (_c.c_int, [_vp, _i64]),
+    "pa_bm_select": (_c.c_int, [_vp, _vp, _vp, _i32, _vp, _i32]),
     "pa_bm_slots": (_c.c_int, [_vp, _i64, _i64, _i64, _vp]),
     "pa_bm_block_table": (_c.c_int, [_vp, _i64, _vp, _i32, _pi32]),
     "pa_bm_block_tables": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp]),
@@ -450,6 +451,16 @@ class BlockManager:
 
     def free_seq(self, seq: int):
         _check(lib().pa_bm_free_seq(self._h, seq), "pa_bm_free_seq")
+
+    def select(self, pairs, retire):
+        """Beam selection: fork child from parent for each (parent, child), then free
+        every sequence in ``retire`` (one call, checked before any change)."""
+        pr = np.ascontiguousarray([p for p, _ in pairs], dtype=np.int64)
+        ch = np.ascontiguousarray([c for _, c in pairs], dtype=np.int64)
+        rt = np.ascontiguousarray(list(retire), dtype=np.int64)
+        _check(lib().pa_bm_select(self._h, _ptr(pr) if pr.size else None,
+                                  _ptr(ch) if ch.size else None, int(pr.size),
+                                  _ptr(rt) if rt.size else None, int(rt.size)), "pa_bm_select")
 
     def slots(self, seq: int, start: int, n: int) -> np.ndarray:
         out = np.empty(n, dtype=np.int64)

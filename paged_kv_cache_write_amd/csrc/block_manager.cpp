@@ -199,6 +199,33 @@ int pa_bm_step(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots,
   return pa_bm_block_tables(bm, seqs, n, tables, max_blocks, pad, context_lens);
 }
 
+int pa_bm_select(pa_bm* bm, const int64_t* parents, const int64_t* children, int32_t n,
+                 const int64_t* retire, int32_t m) {
+  if (!bm || n < 0 || m < 0 || (n > 0 && (!parents || !children)) || (m > 0 && !retire))
+    return PA_ERR_INVALID;
+  // every check before any change: parents exist, children are new and
+  // distinct, retired sequences exist and are distinct
+  std::unordered_map<int64_t, int> seen;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!bm->seqs.count(parents[i])) return PA_ERR_NOT_FOUND;
+    if (bm->seqs.count(children[i]) || !seen.emplace(children[i], 1).second) return PA_ERR_EXISTS;
+  }
+  std::unordered_map<int64_t, int> gone;
+  for (int32_t j = 0; j < m; ++j) {
+    if (!bm->seqs.count(retire[j])) return PA_ERR_NOT_FOUND;
+    if (!gone.emplace(retire[j], 1).second) return PA_ERR_INVALID;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int rc = pa_bm_fork(bm, parents[i], children[i]);
+    if (rc != PA_OK) return rc;  // cannot happen after the checks
+  }
+  for (int32_t j = 0; j < m; ++j) {
+    const int rc = pa_bm_free_seq(bm, retire[j]);
+    if (rc != PA_OK) return rc;
+  }
+  return PA_OK;
+}
+
 int pa_bm_free_seq(pa_bm* bm, int64_t seq) {
   if (!bm) return PA_ERR_INVALID;
   auto it = bm->seqs.find(seq);

@@ -90,6 +90,14 @@ class PagedKVEngine:
     def fork(self, parent, child):
         self.bm.fork(parent, child)
 
+    def free(self, seq):
+        """Release a finished sequence's blocks (shared ones stay with their holders)."""
+        self.bm.free_seq(seq)
+
+    def select(self, pairs, retire):
+        """Beam-search selection: fork each (parent, child), then free ``retire``."""
+        self.bm.select(pairs, retire)
+
     def extend(self, seqs, k, v):
         """Append one token per entry of ``seqs`` (in order; repeats allowed) with K/V rows
         k[i], v[i]: copies first, then the writes."""

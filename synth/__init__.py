@@ -37,7 +37,7 @@ except Exception:  # pragma: no cover
 
 __all__ = [
     "DTYPES", "Workload", "make_workload", "make_custom", "to_storage", "CONFIG_NAMES",
-    "SWEEP_BLOCK_SIZES", "cache_draws", "to_torch", "make_fork_tree",
+    "SWEEP_BLOCK_SIZES", "cache_draws", "to_torch", "make_fork_tree", "make_beam_search",
 ]
 
 # storage dtype name -> (numpy storage dtype, bytes per element)
@@ -151,6 +151,10 @@ class Workload:
       ("fork", parent, child) child shares all of parent's blocks
       ("extend", seq, n)      append n tokens to seq, one at a time
       ("step", [seqs])        append one token to each listed seq, then decode them
+      ("free", seq)           release seq's blocks (shared ones stay with their holders)
+      ("select", [(parent, child)], [retired])
+                              beam selection: each child forks its parent, then the
+                              retired sequences are freed
     The values of token t of sequence s are ``kv(s, t, t+1)``; the step token of
     each sequence is its last logical token.
     """
@@ -433,3 +437,67 @@ def make_fork_tree(seed: int, H: int, D: int, dtype: str, bs: int, roots: int = 
                     bs=bs, NB=NB, scale=1.0 / math.sqrt(D), free_order=free_order,
                     poison_block=poison, ctx=ctx, q=q, ops=ops, max_blocks_per_seq=maxb,
                     _segments=segs, notes="random fork tree")
+
+
+def make_beam_search(seed: int, H: int, D: int, dtype: str, bs: int, prompt: int = 600,
+                     width: int = 4, steps: int = 12) -> Workload:
+    """Beam search as a block tree (polomodov.tech "vLLM and PagedAttention" slide
+    14: candidates share prefixes like forked processes; comfyai.app 6.4.2).
+    A prompt of ``prompt`` tokens is forked into ``width`` beams; each of
+    ``steps`` rounds appends one token to every beam, then selects ``width`` new
+    beams, each a fork of a seeded random surviving parent (with repetition),
+    and retires the old beams.  A final step appends one more token to every
+    beam and decodes them.  Children of one parent share its partly filled last
+    block, so their next appends copy it on write."""
+    rt = _rng(seed, _STREAM_TREE)
+    segs, lens, ops = {}, {}, []
+    sub = [0]
+
+    def new_tokens(seq, n):
+        k = _normal(_rng(seed, _STREAM_K, sub[0]), (n, H, D), dtype)
+        v = _normal(_rng(seed, _STREAM_V, sub[0]), (n, H, D), dtype)
+        sub[0] += 1
+        t = lens[seq]
+        segs[seq].append((t, t + n, k, v))
+        lens[seq] = t + n
+
+    def fork(parent, child):
+        segs[child] = list(segs[parent])
+        lens[child] = lens[parent]
+
+    segs[0], lens[0] = [], 0
+    new_tokens(0, prompt)
+    ops.append(("add", 0, prompt))
+    beams = list(range(1, width + 1))
+    for b in beams:
+        fork(0, b)
+    ops.append(("select", [(0, b) for b in beams], [0]))
+    nxt = width + 1
+    for _ in range(steps):
+        for b in beams:
+            new_tokens(b, 1)
+            ops.append(("extend", b, 1))
+        parents = [beams[int(i)] for i in rt.integers(0, width, size=width)]
+        children = list(range(nxt, nxt + width))
+        nxt += width
+        for p, c in zip(parents, children):
+            fork(p, c)
+        ops.append(("select", list(zip(parents, children)), list(beams)))
+        beams = children   # retired beams keep their segments (the script replays them)
+    rs = _rng(seed, _STREAM_STEP)
+    step_k = _normal(rs, (width, H, D), dtype)
+    step_v = _normal(rs, (width, H, D), dtype)
+    for i, b in enumerate(beams):
+        t = lens[b]
+        segs[b].append((t, t + 1, step_k[i:i + 1], step_v[i:i + 1]))
+        lens[b] = t + 1
+    ops.append(("step", beams))
+    ctx = np.array([lens[b] for b in beams], dtype=np.int64)
+    NB = (width + 1) * (-(-int(ctx.max()) // bs) + 2) + 8
+    poison, free_order = _placement(seed, NB)
+    q = _normal(_rng(seed, _STREAM_Q), (width, H, D), dtype)
+    return Workload(cfg=seed, name=f"beam-search-{seed}-{dtype}-bs{bs}-w{width}", H=H, D=D,
+                    dtype=dtype, bs=bs, NB=NB, scale=1.0 / math.sqrt(D), free_order=free_order,
+                    poison_block=poison, ctx=ctx, q=q, ops=ops,
+                    max_blocks_per_seq=int(math.ceil(int(ctx.max()) / bs)), _segments=segs,
+                    notes="beam search block tree")

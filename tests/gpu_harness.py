@@ -68,6 +68,10 @@ def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True):
             eng.add_sequence(seq, to_dev(k, wl.dtype), to_dev(v, wl.dtype))
         elif op[0] == "fork":
             eng.fork(op[1], op[2])
+        elif op[0] == "free":
+            eng.free(op[1])
+        elif op[0] == "select":
+            eng.select(op[1], op[2])
         elif op[0] == "extend":
             _, seq, n = op
             t = eng.bm.seq_len(seq)

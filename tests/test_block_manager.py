@@ -131,6 +131,8 @@ def test_workload_scripts_match_model():
              ((1, {}), (2, {}), (4, {}), (4, {"cow": True}), (5, {"bs": 8, "S": 40}))]
     cases += [synth.make_fork_tree(seed, 1, 8, "f32", bs, forks=12, max_prompt=200,
                                    max_extend=50) for seed, bs in ((510, 8), (511, 16))]
+    cases += [synth.make_beam_search(seed, 1, 8, "f32", bs, prompt=p, width=w, steps=15)
+              for seed, bs, p, w in ((512, 8, 37, 4), (513, 16, 300, 8))]
     for wl in cases:
         bm, model = _bm(wl.NB, wl.bs, wl.free_order), oracle.BlockPoolModel(wl.NB, wl.bs, wl.free_order)
         for op in wl.ops:
@@ -141,6 +143,16 @@ def test_workload_scripts_match_model():
             elif op[0] == "fork":
                 model.fork(op[1], op[2])
                 bm.fork(op[1], op[2])
+            elif op[0] == "free":
+                model.free_seq(op[1])
+                bm.free_seq(op[1])
+            elif op[0] == "select":
+                for p, c in op[1]:
+                    model.fork(p, c)
+                for r in op[2]:
+                    model.free_seq(r)
+                bm.select(op[1], op[2])
+                _same_state(bm, model)
             elif op[0] == "extend":
                 want = [model.append_slot(op[1]) for _ in range(op[2])]
                 slots, cows = bm.append_slots([op[1]] * op[2])
@@ -204,3 +216,30 @@ def test_errors():
     with pytest.raises(pk.PAError) as e:
         bm.block_tables([1], 1, -1)
     assert e.value.status == -8
+
+
+def test_select_checks_before_changing():
+    """A beam selection with any bad argument changes nothing; a good one forks, then
+    frees (blocks held only by retired beams go back to the free list in order)."""
+    import paged_kv_cache_write_amd as pk
+    bm, model = _bm(16, 4), oracle.BlockPoolModel(16, 4)
+    for x in (bm, model):
+        x.add_seq(1, 6)
+        x.add_seq(2, 3)
+    before = (bm.free_list(), bm.refcounts())
+    for pairs, retire, status in (([(9, 5)], [], -6),           # unknown parent
+                                  ([(1, 2)], [], -7),           # child exists
+                                  ([(1, 5), (2, 5)], [], -7),   # child twice
+                                  ([(1, 5)], [9], -6),          # unknown retired
+                                  ([(1, 5)], [2, 2], -1)):      # retired twice
+        with pytest.raises(pk.PAError) as e:
+            bm.select(pairs, retire)
+        assert e.value.status == status
+        assert (bm.free_list(), bm.refcounts()) == before
+    bm.select([(1, 5), (1, 6), (2, 7)], [1, 2])
+    for p, c in ((1, 5), (1, 6), (2, 7)):
+        model.fork(p, c)
+    model.free_seq(1)
+    model.free_seq(2)
+    _same_state(bm, model)
+    assert bm.seq_len(5) == 6 and bm.refcount(bm.block_table(5)[0]) == 2

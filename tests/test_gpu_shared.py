@@ -34,6 +34,18 @@ def test_fork_tree(dtype, bs, D):
     assert info["num_group_items"] > 0
 
 
+@pytest.mark.parametrize("dtype,bs,width", [("f16", 16, 4), ("bf16", 8, 8), ("f32", 32, 4)])
+def test_beam_search(dtype, bs, width):
+    """Beam search as a block tree: 20 rounds of appends and selections (repeated
+    parents, retired beams freed, children copying their parent's shared last
+    block on write), then a decode of every beam; the 600-token prompt is shared
+    by all beams, so the decode uses group items."""
+    wl = synth.make_beam_search(560 + bs, 4, 128, dtype, bs, prompt=600, width=width, steps=20)
+    g, r, _ = check_workload(wl, cast_bound=True)
+    assert r["all_cows"].shape[0] > 0
+    assert g["engine"].last_step["num_group_items"] > 0
+
+
 def test_fork_tree_forced_short_partitions():
     """Group items of 256 tokens next to single items of 64: the workspace stride
     and partition indices of both kinds interleave in one row."""

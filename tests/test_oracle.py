@@ -224,14 +224,19 @@ def test_decode_equals_unpaged_attention(cfg):
             assert np.array_equal(r["out"][s, h], want)
 
 
-@pytest.mark.parametrize("seed,bs", [(500, 16), (501, 8), (502, 32)])
-def test_fork_tree_decode_equals_unpaged_attention(seed, bs):
+@pytest.mark.parametrize("kind,seed,bs", [("tree", 500, 16), ("tree", 501, 8), ("tree", 502, 32),
+                                          ("beam", 503, 8), ("beam", 504, 16)])
+def test_fork_tree_decode_equals_unpaged_attention(kind, seed, bs):
     """Random fork trees (forks of forks, parents extended after forking, copy on
-    write of half-full shared blocks): each decode row equals attention over the
-    sequence's logical K/V as drawn, so the script's sharing never leaks one
-    branch's tokens into another."""
-    wl = synth.make_fork_tree(seed, 2, 16, "f32", bs, roots=2, forks=8, max_prompt=120,
-                              max_extend=40)
+    write of half-full shared blocks) and beam searches (selection with repeats,
+    retired beams freed): each decode row equals attention over the sequence's
+    logical K/V as drawn, so the script's sharing never leaks one branch's tokens
+    into another."""
+    if kind == "tree":
+        wl = synth.make_fork_tree(seed, 2, 16, "f32", bs, roots=2, forks=8, max_prompt=120,
+                                  max_extend=40)
+    else:
+        wl = synth.make_beam_search(seed, 2, 16, "f32", bs, prompt=45, width=4, steps=9)
     r = oracle.run_workload(wl)
     step = [op for op in wl.ops if op[0] == "step"][-1][1]
     assert r["all_cows"].shape[0] > 0
