@@ -42,17 +42,26 @@ bool pop_free(pa_bm* bm, int32_t* out) {
   return true;
 }
 
+// What one append did, for undoing it: 0 in place, 1 a new block, 2 a copy.
+struct Undo {
+  int64_t seq;
+  int kind;
+  int32_t src, dst;
+};
+
 int append_one(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
-               int32_t* cow_dst) {
+               int32_t* cow_dst, Undo* undo = nullptr) {
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PA_ERR_NOT_FOUND;
   SeqState& st = it->second;
   const int64_t t = st.len;
   int copied = 0;
+  if (undo) *undo = Undo{seq, 0, -1, -1};
   if (t % bm->bs == 0) {
     int32_t b;
     if (!pop_free(bm, &b)) return PA_ERR_NO_BLOCKS;
     st.table.push_back(b);
+    if (undo) *undo = Undo{seq, 1, -1, b};
   } else {
     int32_t last = st.table.back();
     if (bm->ref[last] > 1) {
@@ -62,12 +71,32 @@ int append_one(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
       st.table.back() = b;
       if (cow_src) *cow_src = last;
       if (cow_dst) *cow_dst = b;
+      if (undo) *undo = Undo{seq, 2, last, b};
       copied = 1;
     }
   }
   if (slot) *slot = int64_t(st.table[t / bm->bs]) * bm->bs + t % bm->bs;
   st.len = t + 1;
   return copied;
+}
+
+// Undo appends in reverse order: lengths, tables, refcounts and the free list
+// (popped blocks go back to its front) are exactly as before them.
+void undo_appends(pa_bm* bm, const std::vector<Undo>& log) {
+  for (auto u = log.rbegin(); u != log.rend(); ++u) {
+    SeqState& st = bm->seqs.find(u->seq)->second;
+    st.len -= 1;
+    if (u->kind == 1) {
+      st.table.pop_back();
+      bm->ref[u->dst] = 0;
+      bm->free_list.push_front(u->dst);
+    } else if (u->kind == 2) {
+      st.table.back() = u->src;
+      bm->ref[u->src] += 1;
+      bm->ref[u->dst] = 0;
+      bm->free_list.push_front(u->dst);
+    }
+  }
 }
 
 void export_row(const SeqState& st, int32_t* row, int32_t width, int32_t pad) {
@@ -155,21 +184,25 @@ int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n,
   if (!bm || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)))
     return PA_ERR_INVALID;
   int32_t ncow = 0;
+  std::vector<Undo> log;
+  log.reserve(size_t(n));
   for (int32_t i = 0; i < n; ++i) {
     int32_t src = -1, dst = -1;
-    int rc = append_one(bm, seqs[i], &slots[i], &src, &dst);
-    if (rc < 0) {
-      if (num_cow) *num_cow = ncow;
+    Undo u;
+    int rc = append_one(bm, seqs[i], &slots[i], &src, &dst, &u);
+    if (rc < 0) {  // all or nothing: the appends before this one are undone
+      undo_appends(bm, log);
       return rc;
     }
+    log.push_back(u);
     if (rc == 1) {
       cow_pairs[2 * ncow] = src;
       cow_pairs[2 * ncow + 1] = dst;
       ++ncow;
     }
-    if (num_done) *num_done = i + 1;
   }
   if (num_cow) *num_cow = ncow;
+  if (num_done) *num_done = n;
   return PA_OK;
 }
 

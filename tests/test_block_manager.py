@@ -3,6 +3,7 @@
 No GPU: the block manager never touches device memory.  Tables, slots,
 copy-on-write pairs, refcounts and the free list must match bit for bit.
 """
+import copy
 import numpy as np
 import pytest
 
@@ -102,6 +103,7 @@ def test_random_ops_match_model():
                 batch = [live[int(i)] for i in rng.integers(0, len(live), size=int(rng.integers(1, 6)))]
                 snapshot_ok = True
                 want_slots, want_cows = [], []
+                saved = copy.deepcopy(model)
                 try:
                     for s in batch:
                         slot, cow = model.append_slot(s)
@@ -115,9 +117,10 @@ def test_random_ops_match_model():
                     assert slots.tolist() == want_slots
                     assert [tuple(c) for c in cows.tolist()] == want_cows
                 else:
-                    with pytest.raises(pk.PAError):
+                    with pytest.raises(pk.PAError) as e:
                         bm.append_slots(batch)
-                    # the failed batch did its first appends; the model did too
+                    assert e.value.status == -4
+                    model = saved        # all or nothing: the batch changed nothing
             else:
                 s = live.pop(int(rng.integers(len(live))))
                 model.free_seq(s)
@@ -243,3 +246,25 @@ def test_select_checks_before_changing():
     model.free_seq(2)
     _same_state(bm, model)
     assert bm.seq_len(5) == 6 and bm.refcount(bm.block_table(5)[0]) == 2
+
+def test_failed_batch_changes_nothing():
+    """A batch of appends that runs out of blocks part way (after a new block and a
+    copy on write) is undone: lengths, tables, refcounts and the free list's order
+    are as before, and the same batch succeeds once a sequence is freed."""
+    import paged_kv_cache_write_amd as pk
+    bm = _bm(5, 4, [4, 3, 2, 1, 0])
+    bm.add_seq(1, 4)          # one full block: the next append takes a new block
+    bm.add_seq(2, 2)
+    bm.fork(2, 3)             # 2 and 3 share a partly filled block: copy on write
+    bm.add_seq(4, 5)          # two blocks; 1 block left free
+    state = (bm.free_list(), bm.refcounts(), [bm.block_table(s) for s in (1, 2, 3, 4)],
+             [bm.seq_len(s) for s in (1, 2, 3, 4)])
+    assert len(state[0]) == 1
+    with pytest.raises(pk.PAError) as e:
+        bm.append_slots([1, 2, 4])        # 1 takes the last free block, 2 would copy
+    assert e.value.status == -4
+    assert (bm.free_list(), bm.refcounts(), [bm.block_table(s) for s in (1, 2, 3, 4)],
+            [bm.seq_len(s) for s in (1, 2, 3, 4)]) == state
+    bm.free_seq(4)
+    slots, cows = bm.append_slots([1, 2, 3])
+    assert cows.shape == (1, 2) and bm.seq_len(1) == 5
