@@ -445,6 +445,27 @@ def main():
         sec["copy_blocks_us"] = round(ct * 1e6, 2)
         sec["copy_blocks_gbps"] = round(npairs * 2 * 2 * wl.H * wl.bs * wl.D * elem / ct / 1e9, 2)
         sec["copy_pairs"] = int(npairs)
+    # swapping (preemption): blocks to a pinned host pool and back over the host link
+    nswap = 64
+    hk = torch.empty((nswap,) + tuple(eng.k_cache.shape[1:]), dtype=eng.k_cache.dtype,
+                     pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    used = np.resize(tables[:, 0], nswap).astype(np.int32)
+    out_pairs = torch.from_numpy(np.stack([used, np.arange(nswap, dtype=np.int32)], 1)).to(dev)
+    back = free[:nswap] if len(free) >= nswap else None
+    pk.copy_blocks_between(eng.k_cache, eng.v_cache, hk, hv, out_pairs)
+    so = per_call(lambda: pk.copy_blocks_between(eng.k_cache, eng.v_cache, hk, hv, out_pairs), n=5)
+    blk = 2 * wl.H * wl.bs * wl.D * elem
+    sec["swap_out_us"] = round(so * 1e6, 2)
+    sec["swap_out_gbps"] = round(nswap * blk / so / 1e9, 2)
+    if back is not None:
+        in_pairs = torch.from_numpy(np.stack([np.arange(nswap, dtype=np.int32),
+                                              np.array(back, dtype=np.int32)], 1)).to(dev)
+        si = per_call(lambda: pk.copy_blocks_between(hk, hv, eng.k_cache, eng.v_cache, in_pairs),
+                      n=5)
+        sec["swap_in_us"] = round(si * 1e6, 2)
+        sec["swap_in_gbps"] = round(nswap * blk / si / 1e9, 2)
+    sec["swap_blocks"] = nswap
     res["secondary"] = sec
 
     if args.contiguous:

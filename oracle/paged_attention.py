@@ -197,6 +197,16 @@ class BlockPoolModel:
       slide 13).  slot = table[t // bs] * bs + t % bs.
     * free_seq: every block of the sequence loses one reference; blocks that
       reach zero go back to the free list in logical order.
+    * Preemption by swapping (slide 15: the newest request is evicted as a
+      whole, its blocks go to host memory and come back later): a second,
+      host pool with its own FIFO free list.  swap_out(seqs) requires that the
+      group holds its blocks alone (each block's refcount equals the group's
+      references to it); walking the group's tables in order, each distinct
+      block is given the next host block, keeps its refcount there, and goes
+      back to the device free list.  swap_in is the same move in the other
+      direction.  Both change nothing when the other pool is short of blocks.
+    * blocks_needed(seqs): how many device blocks append_slot over seqs would
+      take, without taking them.
     """
 
     class NoBlocks(Exception):
@@ -209,6 +219,10 @@ class BlockPoolModel:
         self.ref = [0] * self.NB
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
+        self.host_free: deque = deque()
+        self.host_ref: list[int] = []
+        self.swapped: dict[int, list[int]] = {}   # seq -> host block table
+        self.swapped_lens: dict[int, int] = {}
 
     def _pop(self):
         if not self.free:
@@ -253,11 +267,79 @@ class BlockPoolModel:
         return [table[t // self.bs] * self.bs + t % self.bs for t in range(t0, t1)]
 
     def free_seq(self, seq):
+        if seq in self.swapped:
+            for b in self.swapped.pop(seq):
+                self.host_ref[b] -= 1
+                if self.host_ref[b] == 0:
+                    self.host_free.append(b)
+            del self.swapped_lens[seq]
+            return
         for b in self.tables.pop(seq):
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
         del self.lens[seq]
+
+    def set_host_pool(self, n, free_order=None):
+        assert not self.swapped
+        order = range(int(n)) if free_order is None else [int(b) for b in free_order]
+        self.host_free = deque(order)
+        self.host_ref = [0] * int(n)
+
+    @staticmethod
+    def _move(seqs, tables, lens, ref, free, to_tables, to_lens, to_ref, to_free):
+        """Move the group's tables to the other pool; returns [(src, dst)] pairs."""
+        assert len(set(seqs)) == len(seqs)
+        count = {}
+        order = []
+        for s in seqs:
+            for b in tables[s]:
+                if b not in count:
+                    count[b] = 0
+                    order.append(b)
+                count[b] += 1
+        if any(count[b] != ref[b] for b in order):
+            raise ValueError("the group shares blocks with a sequence outside it")
+        if len(order) > len(to_free):
+            raise BlockPoolModel.NoBlocks()
+        new = {}
+        for b in order:
+            nb = to_free.popleft()
+            to_ref[nb] = ref[b]
+            ref[b] = 0
+            free.append(b)
+            new[b] = nb
+        for s in seqs:
+            to_tables[s] = [new[b] for b in tables.pop(s)]
+            to_lens[s] = lens.pop(s)
+        return [(b, new[b]) for b in order]
+
+    def swap_out(self, seqs):
+        return self._move(list(seqs), self.tables, self.lens, self.ref, self.free,
+                          self.swapped, self.swapped_lens, self.host_ref, self.host_free)
+
+    def swap_in(self, seqs):
+        return self._move(list(seqs), self.swapped, self.swapped_lens, self.host_ref,
+                          self.host_free, self.tables, self.lens, self.ref, self.free)
+
+    def blocks_needed(self, seqs):
+        """Device blocks append_slot over seqs would take: the append rules replayed
+        on copies of the lengths and refcounts (None = the last block is private
+        after a new block or a copy)."""
+        ref, lens = list(self.ref), dict(self.lens)
+        last = {s: (t[-1] if t else None) for s, t in self.tables.items()}
+        taken = 0
+        for s in seqs:
+            t = lens[s]
+            if t % self.bs == 0:
+                taken += 1
+                last[s] = None
+            elif last[s] is not None and ref[last[s]] > 1:
+                taken += 1
+                ref[last[s]] -= 1
+                last[s] = None
+            lens[s] = t + 1
+        return taken
 
     def table_array(self, seqs, width, pad):
         out = np.full((len(seqs), width), pad, dtype=np.int32)
@@ -317,6 +399,21 @@ def run_workload(wl, decode=True, decode_seqs=None, fill=None):
             bm.fork(op[1], op[2])
         elif kind == "free":
             bm.free_seq(op[1])
+        elif kind == "host_pool":
+            bm.set_host_pool(op[1])
+            host_shape = (op[1],) + k_cache.shape[1:]
+            poison = 0 if fill is not None else (0x7FC0 if wl.dtype == "bf16" else np.nan)
+            k_host = np.full(host_shape, poison, dtype=k_cache.dtype)
+            v_host = k_host.copy()
+        elif kind == "swap_out":
+            # preemption: the group's blocks are copied to the host pool, exactly
+            for dev_b, host_b in bm.swap_out(op[1]):
+                k_host[host_b] = k_cache[dev_b]
+                v_host[host_b] = v_cache[dev_b]
+        elif kind == "swap_in":
+            for host_b, dev_b in bm.swap_in(op[1]):
+                k_cache[dev_b] = k_host[host_b]
+                v_cache[dev_b] = v_host[host_b]
         elif kind == "select":
             # beam selection: every (parent, child) fork, then the retired frees
             for parent, child in op[1]:

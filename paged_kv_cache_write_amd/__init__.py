@@ -17,7 +17,7 @@ __all__ = [
     "lib", "PAError", "cache_write", "copy_blocks", "decode", "decode_partitions",
     "decode_reduce", "decode_plan", "decode_workspace_size", "decode_schedule",
     "decode_scheduled", "decode_schedule_shared", "decode_scheduled_shared", "stream_read",
-    "decode_contiguous",
+    "decode_contiguous", "copy_blocks_between",
     "BlockManager",
     "DTYPE_CODES", "LIB_PATH",
 ]
@@ -61,6 +61,16 @@ _SIGNATURES = {
     "pa_bm_step": (_c.c_int, [_vp, _vp, _i32, _vp, _vp, _pi32, _vp, _i32, _i32, _vp]),
     "pa_bm_free_seq": (_c.c_int, [_vp, _i64]),
     "pa_bm_select": (_c.c_int, [_vp, _vp, _vp, _i32, _vp, _i32]),
+    "pa_bm_set_host_pool": (_c.c_int, [_vp, _i64, _vp, _i64]),
+    "pa_bm_swap_out": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _pi32]),
+    "pa_bm_swap_in": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _pi32]),
+    "pa_bm_is_swapped": (_c.c_int, [_vp, _i64]),
+    "pa_bm_num_free_host": (_i64, [_vp]),
+    "pa_bm_host_free_list": (_i64, [_vp, _vp, _i64]),
+    "pa_bm_host_refcount": (_i32, [_vp, _i32]),
+    "pa_bm_blocks_needed": (_i64, [_vp, _vp, _i32]),
+    "pa_copy_blocks_between": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          _vp]),
     "pa_bm_slots": (_c.c_int, [_vp, _i64, _i64, _i64, _vp]),
     "pa_bm_block_table": (_c.c_int, [_vp, _i64, _vp, _i32, _pi32]),
     "pa_bm_block_tables": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp]),
@@ -192,6 +202,30 @@ def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
         _dev(block_pairs, "block_pairs", torch.int32), n, NB, H, D, bs, _dt(k_cache),
         _stream(stream, k_cache.device))
     _check(rc, "pa_copy_blocks")
+
+
+def copy_blocks_between(src_k, src_v, dst_k, dst_v, block_pairs, stream=None):
+    """dst[pairs[i,1]] = src[pairs[i,0]] for K and V between two pools of blocks
+    [NB, H, bs, D] (device memory or pinned host memory): swapping."""
+    torch = _torch()
+    _, H, bs, D = src_k.shape
+    n = int(block_pairs.shape[0])
+    for t in (src_v, dst_k, dst_v):
+        if tuple(t.shape[1:]) != (H, bs, D) or t.dtype != src_k.dtype:
+            raise ValueError("pools must share [H, bs, D] and dtype")
+    if not all(t.is_contiguous() for t in (src_k, src_v, dst_k, dst_v)):
+        raise ValueError("pools must be contiguous")
+    if n == 0:
+        return
+    if tuple(block_pairs.shape) != (n, 2) or block_pairs.dtype != torch.int32:
+        raise ValueError("block_pairs must be int32 [n, 2]")
+    if not (block_pairs.is_cuda or block_pairs.is_pinned()):
+        raise ValueError("block_pairs must be device or pinned host memory")
+    dev = src_k.device if src_k.is_cuda else dst_k.device
+    rc = lib().pa_copy_blocks_between(src_k.data_ptr(), src_v.data_ptr(), dst_k.data_ptr(),
+                                      dst_v.data_ptr(), block_pairs.data_ptr(), n, H, D, bs,
+                                      _dt(src_k), _stream(stream, dev))
+    _check(rc, "pa_copy_blocks_between")
 
 
 def decode_plan(num_seqs, num_heads, head_dim, block_size, max_context_len, dtype_code,
@@ -513,3 +547,62 @@ class BlockManager:
 
     def refcounts(self) -> list:
         return [self.refcount(b) for b in range(self.num_blocks)]
+
+    # ------------------------------------------------ preemption by swapping
+    def set_host_pool(self, num_host_blocks: int, free_order=None):
+        self.num_host_blocks = int(num_host_blocks)
+        if free_order is None:
+            rc = lib().pa_bm_set_host_pool(self._h, num_host_blocks, None, 0)
+        else:
+            fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            rc = lib().pa_bm_set_host_pool(self._h, num_host_blocks, _ptr(fo), fo.size)
+        _check(rc, "pa_bm_set_host_pool")
+
+    def _move(self, fn, seqs):
+        arr = np.ascontiguousarray(seqs, dtype=np.int64)
+        cap = 0
+        while True:
+            pairs = np.empty((max(cap, 1), 2), dtype=np.int32)
+            n = _c.c_int32()
+            rc = getattr(lib(), fn)(self._h, _ptr(arr), arr.size, _ptr(pairs), cap, _c.byref(n))
+            if rc == -8 and n.value > cap:      # PA_ERR_CAPACITY: retry with room
+                cap = n.value
+                continue
+            _check(rc, fn)
+            return pairs[:n.value].copy()
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """Move seqs (a group holding its blocks alone) to host blocks; returns the
+        (device block, host block) pairs to copy."""
+        return self._move("pa_bm_swap_out", seqs)
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """Move swapped-out seqs back to device blocks; returns (host block, device
+        block) pairs to copy."""
+        return self._move("pa_bm_swap_in", seqs)
+
+    def is_swapped(self, seq: int) -> bool:
+        rc = lib().pa_bm_is_swapped(self._h, seq)
+        _check(min(rc, 0), "pa_bm_is_swapped")
+        return rc == 1
+
+    @property
+    def num_free_host(self) -> int:
+        return int(lib().pa_bm_num_free_host(self._h))
+
+    def host_free_list(self) -> list:
+        n = int(lib().pa_bm_host_free_list(self._h, None, 0))
+        out = np.empty(n, dtype=np.int32)
+        lib().pa_bm_host_free_list(self._h, _ptr(out), n)
+        return out.tolist()
+
+    def host_refcounts(self) -> list:
+        return [int(lib().pa_bm_host_refcount(self._h, b))
+                for b in range(getattr(self, "num_host_blocks", 0))]
+
+    def blocks_needed(self, seqs) -> int:
+        """Device blocks the next append of each of seqs would take (no change)."""
+        arr = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = int(lib().pa_bm_blocks_needed(self._h, _ptr(arr) if arr.size else None, arr.size))
+        _check(min(n, 0), "pa_bm_blocks_needed")
+        return n

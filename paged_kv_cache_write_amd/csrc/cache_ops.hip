@@ -38,16 +38,18 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   *reinterpret_cast<u32x4*>(v_cache + dst) = *reinterpret_cast<const u32x4*>(v + src);
 }
 
-// blockIdx.y = pair; blocks of blockIdx.x stride over the tile's 16-byte vectors.
+// blockIdx.y = pair; blocks of blockIdx.x stride over the block's 16-byte
+// vectors.  Source and destination pools may be the same (copy on write) or
+// different (swapping between the device pool and a host pool).
 __global__ __launch_bounds__(kCwThreads) void copy_blocks_kernel(
-    char* __restrict__ k_cache, char* __restrict__ v_cache, const int32_t* __restrict__ pairs,
-    int64_t tile_vecs) {
+    const char* src_k, const char* src_v, char* dst_k, char* dst_v,
+    const int32_t* __restrict__ pairs, int64_t tile_vecs) {
   const int pair = blockIdx.y;
   const int64_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
-  const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache) + src * tile_vecs;
-  const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache) + src * tile_vecs;
-  u32x4* kd = reinterpret_cast<u32x4*>(k_cache) + dst * tile_vecs;
-  u32x4* vd = reinterpret_cast<u32x4*>(v_cache) + dst * tile_vecs;
+  const u32x4* ks = reinterpret_cast<const u32x4*>(src_k) + src * tile_vecs;
+  const u32x4* vs = reinterpret_cast<const u32x4*>(src_v) + src * tile_vecs;
+  u32x4* kd = reinterpret_cast<u32x4*>(dst_k) + dst * tile_vecs;
+  u32x4* vd = reinterpret_cast<u32x4*>(dst_v) + dst * tile_vecs;
   for (int64_t i = int64_t(blockIdx.x) * kCwThreads + threadIdx.x; i < tile_vecs;
        i += int64_t(gridDim.x) * kCwThreads) {
     const u32x4 a = ks[i];
@@ -159,7 +161,33 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int
   (void)hipGetLastError();
   hipLaunchKernelGGL(pa::copy_blocks_kernel, dim3(unsigned(gx), unsigned(num_pairs)),
                      dim3(pa::kCwThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const char*>(k_cache), static_cast<const char*>(v_cache),
                      static_cast<char*>(k_cache), static_cast<char*>(v_cache), block_pairs,
+                     tile_vecs);
+  return pa::launch_status();
+}
+
+int pa_copy_blocks_between(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                           const int32_t* block_pairs, int32_t num_pairs, int32_t num_heads,
+                           int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+  int rc = pa::check_shape(head_dim, block_size, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_pairs < 0 || num_heads <= 0) return PA_ERR_INVALID;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > 65535) return PA_ERR_UNSUPPORTED;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs) return PA_ERR_INVALID;
+  if (!pa::aligned16(src_k) || !pa::aligned16(src_v) || !pa::aligned16(dst_k) ||
+      !pa::aligned16(dst_v))
+    return PA_ERR_INVALID;
+  const int64_t tile_vecs =
+      int64_t(num_heads) * block_size * head_dim * pa::elem_bytes(dtype) / 16;
+  int64_t gx = (tile_vecs + pa::kCwThreads - 1) / pa::kCwThreads;
+  if (gx > 64) gx = 64;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(pa::copy_blocks_kernel, dim3(unsigned(gx), unsigned(num_pairs)),
+                     dim3(pa::kCwThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const char*>(src_k), static_cast<const char*>(src_v),
+                     static_cast<char*>(dst_k), static_cast<char*>(dst_v), block_pairs,
                      tile_vecs);
   return pa::launch_status();
 }

@@ -90,6 +90,35 @@ class PagedKVEngine:
     def fork(self, parent, child):
         self.bm.fork(parent, child)
 
+    def set_host_pool(self, num_host_blocks, free_order=None):
+        """Pinned host pool of num_host_blocks blocks for preempted requests."""
+        torch = self.torch
+        shape = (int(num_host_blocks), self.H, self.bs, self.D)
+        self.k_host = torch.empty(shape, dtype=self.dtype, pin_memory=True)
+        self.v_host = torch.empty(shape, dtype=self.dtype, pin_memory=True)
+        self.bm.set_host_pool(num_host_blocks, free_order)
+
+    def swap_out(self, seqs):
+        """Preempt a request (a group holding its blocks alone): its blocks are copied
+        to the host pool on the current stream and the device blocks are freed.
+        Returns the (device, host) block pairs."""
+        from . import copy_blocks_between
+        pairs = self.bm.swap_out(seqs)
+        if pairs.size:
+            p = self.torch.from_numpy(pairs).to(self.device)
+            copy_blocks_between(self.k_cache, self.v_cache, self.k_host, self.v_host, p)
+        return pairs
+
+    def swap_in(self, seqs):
+        """Bring a preempted request back into (possibly other) device blocks.
+        Returns the (host, device) block pairs."""
+        from . import copy_blocks_between
+        pairs = self.bm.swap_in(seqs)
+        if pairs.size:
+            p = self.torch.from_numpy(pairs).to(self.device)
+            copy_blocks_between(self.k_host, self.v_host, self.k_cache, self.v_cache, p)
+        return pairs
+
     def free(self, seq):
         """Release a finished sequence's blocks (shared ones stay with their holders)."""
         self.bm.free_seq(seq)

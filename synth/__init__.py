@@ -38,6 +38,7 @@ except Exception:  # pragma: no cover
 __all__ = [
     "DTYPES", "Workload", "make_workload", "make_custom", "to_storage", "CONFIG_NAMES",
     "SWEEP_BLOCK_SIZES", "cache_draws", "to_torch", "make_fork_tree", "make_beam_search",
+    "make_preemption",
 ]
 
 # storage dtype name -> (numpy storage dtype, bytes per element)
@@ -155,6 +156,9 @@ class Workload:
       ("select", [(parent, child)], [retired])
                               beam selection: each child forks its parent, then the
                               retired sequences are freed
+      ("host_pool", n)        a host pool of n blocks for preempted requests
+      ("swap_out", [seqs])    preempt a request (its sequences) to the host pool
+      ("swap_in", [seqs])     bring it back
     The values of token t of sequence s are ``kv(s, t, t+1)``; the step token of
     each sequence is its last logical token.
     """
@@ -501,3 +505,87 @@ def make_beam_search(seed: int, H: int, D: int, dtype: str, bs: int, prompt: int
                     poison_block=poison, ctx=ctx, q=q, ops=ops,
                     max_blocks_per_seq=int(math.ceil(int(ctx.max()) / bs)), _segments=segs,
                     notes="beam search block tree")
+
+
+def make_preemption(seed: int, H: int, D: int, dtype: str, bs: int, rounds_before: int = 20,
+                    rounds_out: int = 40) -> Workload:
+    """Preemption by swapping (polomodov.tech "vLLM and PagedAttention" slide 15:
+    when the pool runs short the scheduler evicts the newest request as a
+    whole; its blocks go to host memory and come back when there is room).
+    Four requests in arrival order: a long single sequence (id 0), a group of 3
+    parallel samples of one prompt (comfyai.app 6.4.3), a single sequence and,
+    newest, a group of 2 samples.  After ``rounds_before`` rounds of one
+    appended token per sequence the pool is nearly full (it has the blocks in
+    use then plus 2) and the newest group is swapped out; the others run
+    ``rounds_out`` more rounds, taking the blocks the group gave back; request
+    0 finishes (freed); the group is swapped in, to other physical blocks, and
+    a final step decodes the remaining sequences."""
+    rp = _rng(seed, _STREAM_TREE)
+    prompts = [40 * bs] + [int(x) for x in rp.integers(bs + 1, 12 * bs, size=3)]
+    groups = [[0], [1, 2, 3], [4], [5, 6]]
+    segs, lens, ops = {}, {}, []
+    sub = [0]
+
+    def new_tokens(seq, n):
+        k = _normal(_rng(seed, _STREAM_K, sub[0]), (n, H, D), dtype)
+        v = _normal(_rng(seed, _STREAM_V, sub[0]), (n, H, D), dtype)
+        sub[0] += 1
+        t = lens[seq]
+        segs[seq].append((t, t + n, k, v))
+        lens[seq] = t + n
+
+    def blocks(gs):
+        """Blocks in use by groups gs: a group's full prompt blocks once (its
+        members copy the partly filled prompt block on their first append)."""
+        n = 0
+        for g in gs:
+            members = groups[g]
+            full = prompts[g] // bs if len(members) > 1 else 0
+            n += full + sum(-(-(lens[m] - full * bs) // bs) for m in members)
+        return n
+
+    for g, members in enumerate(groups):
+        lead = members[0]
+        segs[lead], lens[lead] = [], 0
+        new_tokens(lead, prompts[g])
+        ops.append(("add", lead, prompts[g]))
+        for m in members[1:]:
+            segs[m], lens[m] = list(segs[lead]), lens[lead]
+            ops.append(("fork", lead, m))
+
+    def rounds(seqs, n):
+        for _ in range(n):
+            for s_ in seqs:
+                new_tokens(s_, 1)
+                ops.append(("extend", s_, 1))
+
+    rounds([m for g in groups for m in g], rounds_before)
+    at_swap = blocks(range(4))
+    group_blocks = blocks([3])
+    newest = groups[-1]
+    ops.append(("host_pool", group_blocks + 2))
+    ops.append(("swap_out", list(newest)))
+    rounds([m for g in groups[:3] for m in g], rounds_out)
+    # the pool: nearly full when the group goes out (2 spare blocks), large
+    # enough for the others' growth (which then takes the group's blocks)
+    NB = max(at_swap + 2, blocks([0, 1, 2])) + 1        # + the poison block
+    ops.append(("free", 0))
+    assert NB - 1 - blocks([1, 2]) >= group_blocks, "the swap-in must fit"
+    ops.append(("swap_in", list(newest)))
+    final = [m for g in groups[1:] for m in g]
+    rs = _rng(seed, _STREAM_STEP)
+    step_k = _normal(rs, (len(final), H, D), dtype)
+    step_v = _normal(rs, (len(final), H, D), dtype)
+    for i, s_ in enumerate(final):
+        t = lens[s_]
+        segs[s_].append((t, t + 1, step_k[i:i + 1], step_v[i:i + 1]))
+        lens[s_] = t + 1
+    ops.append(("step", final))
+    ctx = np.array([lens[s_] for s_ in final], dtype=np.int64)
+    poison, free_order = _placement(seed, NB)
+    q = _normal(_rng(seed, _STREAM_Q), (len(final), H, D), dtype)
+    return Workload(cfg=seed, name=f"preemption-{seed}-{dtype}-bs{bs}", H=H, D=D, dtype=dtype,
+                    bs=bs, NB=NB, scale=1.0 / math.sqrt(D), free_order=free_order,
+                    poison_block=poison, ctx=ctx, q=q, ops=ops,
+                    max_blocks_per_seq=int(math.ceil(int(ctx.max()) / bs)), _segments=segs,
+                    notes="newest request swapped out and back in")

@@ -72,6 +72,12 @@ def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True):
             eng.free(op[1])
         elif op[0] == "select":
             eng.select(op[1], op[2])
+        elif op[0] == "host_pool":
+            eng.set_host_pool(op[1])
+        elif op[0] == "swap_out":
+            eng.swap_out(op[1])
+        elif op[0] == "swap_in":
+            eng.swap_in(op[1])
         elif op[0] == "extend":
             _, seq, n = op
             t = eng.bm.seq_len(seq)

@@ -20,7 +20,7 @@ def _same_state(bm, model):
     assert bm.num_free == len(model.free)
     assert bm.free_list() == list(model.free)
     assert bm.refcounts() == model.ref
-    assert bm.num_seqs == len(model.tables)
+    assert bm.num_seqs == len(model.tables) + len(model.swapped)
     for s, tab in model.tables.items():
         assert bm.block_table(s) == tab
         assert bm.seq_len(s) == model.lens[s]
@@ -136,6 +136,7 @@ def test_workload_scripts_match_model():
                                    max_extend=50) for seed, bs in ((510, 8), (511, 16))]
     cases += [synth.make_beam_search(seed, 1, 8, "f32", bs, prompt=p, width=w, steps=15)
               for seed, bs, p, w in ((512, 8, 37, 4), (513, 16, 300, 8))]
+    cases += [synth.make_preemption(seed, 1, 8, "f32", bs) for seed, bs in ((514, 8), (515, 16))]
     for wl in cases:
         bm, model = _bm(wl.NB, wl.bs, wl.free_order), oracle.BlockPoolModel(wl.NB, wl.bs, wl.free_order)
         for op in wl.ops:
@@ -155,6 +156,14 @@ def test_workload_scripts_match_model():
                 for r in op[2]:
                     model.free_seq(r)
                 bm.select(op[1], op[2])
+                _same_state(bm, model)
+            elif op[0] == "host_pool":
+                model.set_host_pool(op[1])
+                bm.set_host_pool(op[1])
+            elif op[0] in ("swap_out", "swap_in"):
+                want = getattr(model, op[0])(op[1])
+                got = getattr(bm, op[0])(op[1])
+                assert [tuple(p) for p in got.tolist()] == want
                 _same_state(bm, model)
             elif op[0] == "extend":
                 want = [model.append_slot(op[1]) for _ in range(op[2])]
@@ -268,3 +277,80 @@ def test_failed_batch_changes_nothing():
     bm.free_seq(4)
     slots, cows = bm.append_slots([1, 2, 3])
     assert cows.shape == (1, 2) and bm.seq_len(1) == 5
+
+
+def _same_host_state(bm, model):
+    assert bm.host_free_list() == list(model.host_free)
+    assert bm.host_refcounts() == model.host_ref
+    for s, t in model.swapped.items():
+        assert bm.is_swapped(s) and bm.block_table(s) == t
+
+
+@pytest.mark.parametrize("seed,bs", [(516, 8), (517, 16), (518, 32)])
+def test_preemption_swap_round_trip(seed, bs):
+    """The newest request is swapped out as a group, the others reuse its device
+    blocks, and it comes back into other blocks; both managers agree throughout."""
+    wl = synth.make_preemption(seed, 1, 8, "f32", bs)
+    bm, model = _bm(wl.NB, wl.bs, wl.free_order), oracle.BlockPoolModel(wl.NB, wl.bs, wl.free_order)
+    out_blocks, reused = None, False
+    for op in wl.ops:
+        if op[0] == "add":
+            model.add_seq(op[1], op[2]); bm.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            model.fork(op[1], op[2]); bm.fork(op[1], op[2])
+        elif op[0] == "extend":
+            model.append_slot(op[1]); bm.append_slot(op[1])
+            if out_blocks and set(model.tables[op[1]]) & out_blocks:
+                reused = True
+        elif op[0] == "free":
+            model.free_seq(op[1]); bm.free_seq(op[1])
+        elif op[0] == "host_pool":
+            model.set_host_pool(op[1]); bm.set_host_pool(op[1])
+        elif op[0] == "swap_out":
+            pairs = bm.swap_out(op[1])
+            assert [tuple(p) for p in pairs.tolist()] == model.swap_out(op[1])
+            out_blocks = {int(p[0]) for p in pairs}
+            with pytest.raises(Exception):
+                bm.append_slot(op[1][0])            # a swapped-out sequence cannot grow
+        elif op[0] == "swap_in":
+            pairs = bm.swap_in(op[1])
+            assert [tuple(p) for p in pairs.tolist()] == model.swap_in(op[1])
+        elif op[0] == "step":
+            for s in op[1]:
+                model.append_slot(s); bm.append_slot(s)
+        _same_state(bm, model)
+        _same_host_state(bm, model)
+    assert reused, "the other requests should take the blocks the preempted group gave back"
+
+
+def test_swap_checks_before_changing():
+    """Swapping part of a group, unknown or repeated sequences, a short pool or a
+    short pairs buffer change nothing; blocks_needed matches the model's count."""
+    import paged_kv_cache_write_amd as pk
+    bm, model = _bm(10, 4), oracle.BlockPoolModel(10, 4)
+    for x in (bm, model):
+        x.add_seq(1, 6)
+        x.fork(1, 2)
+        x.add_seq(3, 9)
+        x.set_host_pool(2)
+    before = (bm.free_list(), bm.refcounts(), bm.host_free_list())
+    for seqs, status in (([1], -1), ([9], -6), ([1, 1, 2], -1), ([3], -4)):
+        with pytest.raises(pk.PAError) as e:
+            bm.swap_out(seqs)
+        assert e.value.status == status
+        assert (bm.free_list(), bm.refcounts(), bm.host_free_list()) == before
+    with pytest.raises(pk.PAError):
+        bm.swap_in([1])                               # not swapped out
+    for seqs in ([1, 2, 3, 1], [3, 3, 3, 3], [2, 1], [3]):
+        assert bm.blocks_needed(seqs) == model.blocks_needed(seqs)
+    assert bm.blocks_needed([1, 2]) == 1              # the first writer copies, the last writes in place
+    assert [tuple(p) for p in bm.swap_out([2, 1]).tolist()] == model.swap_out([2, 1])
+    with pytest.raises(pk.PAError) as e:
+        bm.fork(2, 4)                                 # swapped out: no fork
+    assert e.value.status == -6
+    bm.free_seq(2)                                    # frees host references
+    model.free_seq(2)
+    _same_host_state(bm, model)
+    assert [tuple(p) for p in bm.swap_in([1]).tolist()] == model.swap_in([1])
+    _same_state(bm, model)
+    _same_host_state(bm, model)

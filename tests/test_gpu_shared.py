@@ -46,6 +46,15 @@ def test_beam_search(dtype, bs, width):
     assert g["engine"].last_step["num_group_items"] > 0
 
 
+@pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 8), ("f32", 32)])
+def test_preemption_swap(dtype, bs):
+    """The newest request (a group of 2 samples) is swapped out to the pinned host
+    pool, the others reuse its device blocks, it is swapped back into other
+    blocks: pools bit-exact with the oracle and every sequence decodes correctly."""
+    wl = synth.make_preemption(930 + bs, 4, 128, dtype, bs)
+    check_workload(wl, cast_bound=True)
+
+
 def test_fork_tree_forced_short_partitions():
     """Group items of 256 tokens next to single items of 64: the workspace stride
     and partition indices of both kinds interleave in one row."""

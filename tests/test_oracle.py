@@ -225,7 +225,8 @@ def test_decode_equals_unpaged_attention(cfg):
 
 
 @pytest.mark.parametrize("kind,seed,bs", [("tree", 500, 16), ("tree", 501, 8), ("tree", 502, 32),
-                                          ("beam", 503, 8), ("beam", 504, 16)])
+                                          ("beam", 503, 8), ("beam", 504, 16),
+                                          ("preempt", 505, 8), ("preempt", 506, 16)])
 def test_fork_tree_decode_equals_unpaged_attention(kind, seed, bs):
     """Random fork trees (forks of forks, parents extended after forking, copy on
     write of half-full shared blocks) and beam searches (selection with repeats,
@@ -235,11 +236,13 @@ def test_fork_tree_decode_equals_unpaged_attention(kind, seed, bs):
     if kind == "tree":
         wl = synth.make_fork_tree(seed, 2, 16, "f32", bs, roots=2, forks=8, max_prompt=120,
                                   max_extend=40)
-    else:
+    elif kind == "beam":
         wl = synth.make_beam_search(seed, 2, 16, "f32", bs, prompt=45, width=4, steps=9)
+    else:   # swapped out to the host pool and back in to other blocks
+        wl = synth.make_preemption(seed, 2, 16, "f32", bs, rounds_before=6, rounds_out=12)
     r = oracle.run_workload(wl)
     step = [op for op in wl.ops if op[0] == "step"][-1][1]
-    assert r["all_cows"].shape[0] > 0
+    assert r["all_cows"].shape[0] > 0 or kind == "preempt"
     for row, s in enumerate(step):
         L = int(r["ctx"][row])
         k, v = wl.kv(s, 0, L)
