@@ -64,7 +64,7 @@ def step_bytes(ctx, H, D, elem, bs, ncow):
 
 def build_state(wl, dtype, partition_tokens=0, extra_blocks=64):
     """Run the workload's cache-building ops (prefill, forks, extends) on the GPU.
-    Returns the engine and the step's sequence list."""
+    Returns the engine and the step's sequence list (None without a step)."""
     import torch
     from paged_kv_cache_write_amd.engine import PagedKVEngine
     from synth import to_torch as to_dev
@@ -72,12 +72,13 @@ def build_state(wl, dtype, partition_tokens=0, extra_blocks=64):
     for op in wl.ops:
         if op[0] == "step":
             step_seqs = np.array(op[1], dtype=np.int64)
+    n_seqs = len(step_seqs) if step_seqs is not None else int(wl.S)
     # growth blocks for the timed steps go after the workload's pool, so the
     # workload's own placement is unchanged
-    NB = wl.NB + len(step_seqs) * extra_blocks
+    NB = wl.NB + n_seqs * extra_blocks
     free_order = np.concatenate([wl.free_order, np.arange(wl.NB, NB, dtype=np.int32)])
     eng = PagedKVEngine(NB, wl.H, wl.D, wl.bs, dtype, wl.max_blocks_per_seq + extra_blocks,
-                        len(step_seqs), free_order=free_order, pad_block=wl.poison_block,
+                        n_seqs, free_order=free_order, pad_block=wl.poison_block,
                         fill=0.0, partition_tokens=partition_tokens)
     for op in wl.ops:
         if op[0] == "add":
@@ -193,6 +194,35 @@ def contiguous_compare(eng, seqs, q, wl, torch, pk, per_call):
     return res
 
 
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix cores, published
+
+
+def prefill_measure(torch, pk, per_call, dtype, seqs=8, prompt=1024, H=40, D=128, bs=16):
+    """Paged prefill attention of `seqs` whole prompts of `prompt` tokens: causal
+    flops 4*D*H per (query, key <= query), 20 back-to-back calls."""
+    import synth
+    wl, qn, cu_q = synth.make_prefill(901, H, D, dtype, bs, [0] * seqs, [prompt] * seqs)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    eng, _ = build_state(wl, tdt, 0, extra_blocks=1)
+    tables, ctx = eng.bm.block_tables(np.arange(seqs), eng.maxB, wl.poison_block)
+    from synth import to_torch as to_dev
+    q = to_dev(qn, dtype)
+    dt_, dc = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+    cu = torch.from_numpy(cu_q).cuda()
+    out = torch.empty_like(q)
+    run = lambda: pk.prefill(q, eng.k_cache, eng.v_cache, dt_, cu, dc, wl.scale, prompt, out=out)
+    run()
+    t = per_call(run)
+    pairs = seqs * prompt * (prompt + 1) // 2
+    flops = 4.0 * D * H * pairs
+    return {"workload": f"{seqs} prompts x {prompt} tokens, {H} heads, head_dim {D}, {dtype}, "
+                        f"bs {bs}", "us": round(t * 1e6, 2),
+            "tflops": round(flops / t / 1e12, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
+            "frac": round(flops / t / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "flops_counted": "4*D*H per causal (query, key) pair",
+            "timing": "20 back-to-back calls between one pair of events"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +242,9 @@ def main():
     ap.add_argument("--contiguous", action="store_true",
                     help="also time the decode over the same K/V gathered into a contiguous "
                          "[S, L, H, D] layout (pa_decode_contiguous) next to the paged decode")
+    ap.add_argument("--prefill", action="store_true",
+                    help="also time the paged prefill attention (8 prompts of 1024 tokens at "
+                         "the 13B-layer shape) against the matrix cores' peak")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run 3 plain elementwise copies (neg) of this many MiB: a "
                          "known-size reference for the HBM traffic counters")
@@ -470,6 +503,9 @@ def main():
 
     if args.contiguous:
         res["contiguous"] = contiguous_compare(eng, seqs, q, wl, torch, pk, per_call)
+    if args.prefill:
+        res["prefill"] = prefill_measure(torch, pk, per_call,
+                                         "f16" if wl.dtype == "f32" else wl.dtype)
 
     if not args.no_cpu_baseline:
         t = time.perf_counter()

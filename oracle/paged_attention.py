@@ -42,6 +42,7 @@ __all__ = [
     "kv_bytes_per_token", "useful_kv_fraction", "run_workload",
     "attention_brute_force",
     "oracle_decode_contiguous",
+    "oracle_prefill",
 ]
 
 
@@ -164,6 +165,31 @@ def oracle_decode_contiguous(q, k, v, context_lens, scale, dtype, layout="SLHD")
             kh = ks[:, h, :] if layout == "SLHD" else ks[h]
             vh = vs[:, h, :] if layout == "SLHD" else vs[h]
             out[s, h] = attention_one(qf[s, h], kh, vh, scale)[0]
+    return out
+
+
+def oracle_prefill(q, k_cache, v_cache, block_tables, cu_q, context_lens, scale, dtype):
+    """Causal prefill attention over the paged cache (brentwoodlivery "5.3.18",
+    the prefill/decode cards; comfyai.app 6.4.3: the prompt's K/V are written
+    into blocks first): with q_len = cu_q[s+1] - cu_q[s], query row cu_q[s] + i
+    sits at position p = context_lens[s] - q_len + i and attends to the
+    sequence's tokens 0..p, gathered from its blocks.  Returns float64 [T, H, D]."""
+    T, H, D = q.shape
+    out = np.zeros((T, H, D))
+    qf = widen(q, dtype)
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        q_len = int(cu_q[s + 1]) - int(cu_q[s])
+        if q_len == 0:
+            continue
+        K = widen(oracle_gather(k_cache, block_tables[s], L), dtype)
+        V = widen(oracle_gather(v_cache, block_tables[s], L), dtype)
+        for i in range(q_len):
+            pos = L - q_len + i
+            row = int(cu_q[s]) + i
+            for h in range(H):
+                out[row, h] = attention_one(qf[row, h], K[:pos + 1, h, :], V[:pos + 1, h, :],
+                                            scale)[0]
     return out
 
 
@@ -449,10 +475,12 @@ def run_workload(wl, decode=True, decode_seqs=None, fill=None):
         else:
             raise ValueError(kind)
     width = wl.max_blocks_per_seq
+    if step_seqs is None:   # no decode step: every resident sequence, by id
+        step_seqs = sorted(bm.tables)
     tables = bm.table_array(step_seqs, width, wl.poison_block)
     ctx = np.array([bm.lens[s] for s in step_seqs], dtype=np.int64)
     res = dict(k_cache=k_cache, v_cache=v_cache, tables=tables, ctx=ctx,
-               step_slots=np.array(step_slots, dtype=np.int64),
+               step_slots=np.array(step_slots if step_slots is not None else [], dtype=np.int64),
                step_cows=np.array(step_cows, dtype=np.int64).reshape(-1, 2),
                all_cows=np.array(all_cows, dtype=np.int64).reshape(-1, 2),
                refcounts=np.array(bm.ref, dtype=np.int64), model=bm)

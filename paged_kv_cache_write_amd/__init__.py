@@ -17,7 +17,7 @@ __all__ = [
     "lib", "PAError", "cache_write", "copy_blocks", "decode", "decode_partitions",
     "decode_reduce", "decode_plan", "decode_workspace_size", "decode_schedule",
     "decode_scheduled", "decode_schedule_shared", "decode_scheduled_shared", "stream_read",
-    "decode_contiguous", "copy_blocks_between",
+    "decode_contiguous", "copy_blocks_between", "prefill",
     "BlockManager",
     "DTYPE_CODES", "LIB_PATH",
 ]
@@ -69,6 +69,8 @@ _SIGNATURES = {
     "pa_bm_host_free_list": (_i64, [_vp, _vp, _i64]),
     "pa_bm_host_refcount": (_i32, [_vp, _i32]),
     "pa_bm_blocks_needed": (_i64, [_vp, _vp, _i32]),
+    "pa_prefill": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i64,
+                              _f32, _i32, _i32, _vp, _vp]),
     "pa_copy_blocks_between": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                           _vp]),
     "pa_bm_slots": (_c.c_int, [_vp, _i64, _i64, _i64, _vp]),
@@ -202,6 +204,31 @@ def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
         _dev(block_pairs, "block_pairs", torch.int32), n, NB, H, D, bs, _dt(k_cache),
         _stream(stream, k_cache.device))
     _check(rc, "pa_copy_blocks")
+
+
+def prefill(q, k_cache, v_cache, block_tables, cu_q, context_lens, scale, max_q_len, out=None,
+            stream=None):
+    """pa_prefill: causal attention of the packed new tokens ``q`` [T, H, D] over the
+    paged cache; ``cu_q`` int32 [S+1] query offsets, ``context_lens`` int32 [S]
+    (new tokens included, already written)."""
+    torch = _torch()
+    T, H, D = q.shape
+    NB, Hc, bs, Dc = k_cache.shape
+    S = int(context_lens.shape[0])
+    if (Hc, Dc) != (H, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or cu_q.shape != (S + 1,):
+        raise ValueError("block_tables must be [S, maxB] and cu_q [S + 1]")
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib().pa_prefill(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(cu_q, "cu_q", torch.int32), _dev(context_lens, "context_lens", torch.int32), S, H,
+        D, bs, NB, float(scale), int(max_q_len), _dt(q), _dev(out, "out"),
+        _stream(stream, q.device))
+    _check(rc, "pa_prefill")
+    return out
 
 
 def copy_blocks_between(src_k, src_v, dst_k, dst_v, block_pairs, stream=None):

@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["decode.hip", "cache_ops.hip", "measure.hip", "block_manager.cpp", "capi.cpp",
-           "engine.cpp"]
+SOURCES = ["decode.hip", "prefill.hip", "cache_ops.hip", "measure.hip", "block_manager.cpp",
+           "capi.cpp", "engine.cpp"]
 ARCH = "gfx950"
 
 

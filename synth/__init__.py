@@ -38,7 +38,7 @@ except Exception:  # pragma: no cover
 __all__ = [
     "DTYPES", "Workload", "make_workload", "make_custom", "to_storage", "CONFIG_NAMES",
     "SWEEP_BLOCK_SIZES", "cache_draws", "to_torch", "make_fork_tree", "make_beam_search",
-    "make_preemption",
+    "make_preemption", "make_prefill",
 ]
 
 # storage dtype name -> (numpy storage dtype, bytes per element)
@@ -589,3 +589,36 @@ def make_preemption(seed: int, H: int, D: int, dtype: str, bs: int, rounds_befor
                     poison_block=poison, ctx=ctx, q=q, ops=ops,
                     max_blocks_per_seq=int(math.ceil(int(ctx.max()) / bs)), _segments=segs,
                     notes="newest request swapped out and back in")
+
+
+def make_prefill(seed: int, H: int, D: int, dtype: str, bs: int, prefix_lens, q_lens):
+    """Chunked prefill (brentwoodlivery "5.3.18", the prefill/decode cards;
+    comfyai.app 6.4.3): sequence s already holds prefix_lens[s] cached tokens
+    (written by an "add"), then a chunk of q_lens[s] new tokens is written
+    through the slot mapping (an "extend") and attends causally over the whole
+    cache.  Returns (workload, q [sum q_lens, H, D], cu_q int32 [S + 1]); the
+    workload has no decode step, its ctx is prefix + chunk."""
+    prefix_lens = [int(x) for x in prefix_lens]
+    q_lens = [int(x) for x in q_lens]
+    S = len(q_lens)
+    segs, ops = {}, []
+    for s_ in range(S):
+        n = prefix_lens[s_] + q_lens[s_]
+        k = _normal(_rng(seed, _STREAM_K, s_), (n, H, D), dtype)
+        v = _normal(_rng(seed, _STREAM_V, s_), (n, H, D), dtype)
+        segs[s_] = [(0, n, k, v)]
+        ops.append(("add", s_, prefix_lens[s_]))
+    for s_ in range(S):
+        if q_lens[s_]:
+            ops.append(("extend", s_, q_lens[s_]))
+    ctx = np.array([p + q for p, q in zip(prefix_lens, q_lens)], dtype=np.int64)
+    NB = int(sum(-(-int(c) // bs) for c in ctx)) + 8
+    poison, free_order = _placement(seed, NB)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q = _normal(_rng(seed, _STREAM_Q), (int(cu_q[-1]), H, D), dtype)
+    wl = Workload(cfg=seed, name=f"prefill-{seed}-{dtype}-bs{bs}", H=H, D=D, dtype=dtype, bs=bs,
+                  NB=NB, scale=1.0 / math.sqrt(D), free_order=free_order, poison_block=poison,
+                  ctx=ctx, q=np.zeros((S, H, D), dtype=DTYPES[dtype][0]), ops=ops,
+                  max_blocks_per_seq=max(1, int(math.ceil(int(ctx.max()) / bs))),
+                  _segments=segs, notes="chunked prefill: cached prefix + new chunk")
+    return wl, q, cu_q

@@ -284,6 +284,53 @@ def test_contiguous_decode_closed_forms():
     np.testing.assert_allclose(a[2], v[2].astype(np.float64).mean(axis=0), rtol=0, atol=1e-15)
 
 
+def _prefill_oracle(wl, q, cu_q):
+    r = oracle.run_workload(wl, decode=False)
+    return r, oracle.oracle_prefill(q, r["k_cache"], r["v_cache"], r["tables"], cu_q, r["ctx"],
+                                    wl.scale, wl.dtype)
+
+
+def test_prefill_equals_per_position_attention():
+    """Each prefill row equals attention of that query over the logical K/V as
+    drawn, up to and including its own position (bit-identical), for a chunk
+    after a cached prefix, a whole prompt, and a one-token chunk."""
+    wl, q, cu_q = synth.make_prefill(600, 2, 16, "f32", 4, [5, 0, 9], [7, 6, 1])
+    r, out = _prefill_oracle(wl, q, cu_q)
+    for s in range(3):
+        L, ql = int(r["ctx"][s]), int(cu_q[s + 1] - cu_q[s])
+        k, v = wl.kv(s, 0, L)
+        for i in range(ql):
+            pos, row = L - ql + i, int(cu_q[s]) + i
+            for h in range(wl.H):
+                logits = wl.scale * (k[:pos + 1, h].astype(np.float64) @ q[row, h].astype(np.float64))
+                e = np.exp(logits - logits.max())
+                want = (e / e.sum()) @ v[:pos + 1, h].astype(np.float64)
+                assert np.array_equal(out[row, h], want)
+
+
+def test_prefill_closed_forms_and_causality():
+    """Position 0 attends to itself only (out = V_0 exactly); the last row of a
+    chunk equals the decode of that position (bit-identical); changing K/V after
+    a query's position leaves its row unchanged."""
+    wl, q, cu_q = synth.make_prefill(601, 2, 8, "f32", 4, [0, 3], [5, 4])
+    r, out = _prefill_oracle(wl, q, cu_q)
+    k0, v0 = wl.kv(0, 0, 1)
+    assert np.array_equal(out[0], v0[0].astype(np.float64))
+    dec = oracle.oracle_decode(q[cu_q[1:] - 1], r["k_cache"], r["v_cache"], r["tables"],
+                               r["ctx"], wl.scale, wl.dtype)
+    assert np.array_equal(out[cu_q[1:] - 1], dec)
+    # causality: poison every cached slot after sequence 1's first query position
+    kc, vc = r["k_cache"].copy(), r["v_cache"].copy()
+    pos = int(r["ctx"][1]) - 4
+    for t in range(pos + 1, int(r["ctx"][1])):
+        b, o = r["tables"][1][t // wl.bs], t % wl.bs
+        kc[b, :, o] = 1e3
+        vc[b, :, o] = -1e3
+    out2 = oracle.oracle_prefill(q, kc, vc, r["tables"], cu_q, r["ctx"], wl.scale, wl.dtype)
+    assert np.array_equal(out2[cu_q[1]], out[cu_q[1]])
+    assert not np.array_equal(out2[cu_q[1] + 1], out[cu_q[1] + 1])
+
+
 def test_cache_write_places_every_token():
     """After the script, every token t of every sequence sits at
     pool[table[t//bs], :, t%bs, :], and nothing else was written."""
