@@ -10,21 +10,25 @@
 // Earlier tokens (a cached prefix or earlier chunks) and the new ones are
 // read the same way.
 //
-// How (MI355X design): with 16 queries of one sequence against each key
-// tile, q.K and P.V are dense products for the matrix cores.  One wave owns
-// (sequence, head, 16 consecutive queries) and streams keys 0 .. last query's
-// position in steps of 32 (two 16-token tiles):
+// How (MI355X design): with many queries of one sequence against each key
+// tile, q.K and P.V are dense products for the matrix cores.  A workgroup of
+// 4 waves owns (sequence, head, 128 consecutive queries), 32 per wave in two
+// column sets of 16 (each K or V operand read from LDS feeds both), and
+// streams keys 0 .. its last query's position in steps of 32: the step's K
+// and V rows are loaded once for the workgroup (coalesced 16-byte loads,
+// block ids read per row from the table) into LDS, double-buffered so the
+// next step's loads are in flight during this one, and each wave computes
 //   S^T[t][q] = sum_d K[t][d] Q[q][d]        (v_mfma_f32_16x16x32, A = K rows)
 //   O^T[d][q] += sum_t V^T[d][t] P^T[t][q]   (P^T is S^T's layout; the d axis
 //                                             of this product is permuted so V
-//                                             comes from plain row loads)
+//                                             comes from plain row reads)
 // with the online softmax per query column, the causal mask (key t > query
-// position -> weight 0) on the steps that reach the tile's own positions, and
+// position -> weight 0) on the steps that reach the wave's own positions, and
 // P split into storage-type hi + lo parts so the weights keep float32-like
-// precision.  Block ids come from wave-uniform (scalar) table loads, so
-// contexts of any length stream without a table window; addresses past the
-// last key are clamped to it (never an unwritten slot or a table entry past
-// the sequence) and masked.
+// precision.  A wave skips the steps after its last query.  Rows past the
+// workgroup's last key are clamped to it (never an unwritten slot or a table
+// entry past the sequence) and masked.  LDS rows are padded by 16 bytes so the
+// 16 rows of one operand read start on different banks.
 #include <type_traits>
 
 #include "launch_common.hpp"
@@ -51,40 +55,80 @@ struct PrefillParams {
   float qk_scale;  // scale * log2(e)
 };
 
-template <class DT, int D>
-__global__ __launch_bounds__(kWave, 2) void prefill_mfma_kernel(PrefillParams P) {
+constexpr int kPfWaves = 4;                 // waves per workgroup
+constexpr int kPfKeys = 32;                 // keys per step
+
+// LDS layout of one step's K (or V): key rows of D elements; the 16-byte
+// chunk c of row r is stored at chunk c ^ (r mod chunks-per-row), so the 16
+// lanes of every operand read (16 rows of one chunk, or 16 chunks of one row)
+// and of the cooperative stores touch 16 different chunks: no bank conflicts.
+template <int D>
+struct PfLds {
+  static constexpr int kRow = D * 2;
+  static constexpr int kChunksPerRow = kRow / 16;
+  static constexpr int kMat = kPfKeys * kRow;  // one K (or V) step
+  static __device__ __forceinline__ int at(int row, int chunk) {
+    return row * kRow + ((chunk ^ (row & (kChunksPerRow - 1))) << 4);
+  }
+};
+
+template <class DT, int D, int NS>
+__global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfma_kernel(
+    PrefillParams P) {
   using T = typename DT::T;
+  using L = PfLds<D>;
   constexpr int NK = D / 32;
   constexpr int NJ = D / 16;
+  constexpr int kWaveQueries = 16 * NS;             // queries per wave (NS sets of 16)
+  constexpr int kWgQueries = kWaveQueries * kPfWaves;
   constexpr uint32_t kRowBytes = uint32_t(D) * sizeof(T);
   constexpr int kLog2Row = __builtin_ctz(kRowBytes);
+  constexpr int kChunks = kPfKeys * (D / 8);             // 16-byte chunks of one step's K
+  constexpr int kPerThread = kChunks / (kPfWaves * kWave);  // of K, and as many of V
   using VRow = typename std::conditional<NJ == 8, u32x4, u32x2>::type;
   static_assert(sizeof(T) == 2 && (NJ == 8 || NJ == 4), "16-bit storage, D 64 or 128");
+  static_assert(kPerThread >= 1 && kChunks % (kPfWaves * kWave) == 0, "load split");
+  __shared__ __align__(16) char lds[2][2][L::kMat];  // [buffer][K, V]
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = wave_uniform(tid / kWave);
+  const int lane = tid & (kWave - 1);
   const int qt = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int H = P.H;
   const int q_begin = P.cu_q[s];
   const int q_len = P.cu_q[s + 1] - q_begin;
-  const int q0 = qt * 16;
-  if (q0 >= q_len) return;
-  const int nq = min(16, q_len - q0);
+  const int q0 = qt * kWgQueries;
+  if (q0 >= q_len) return;  // whole workgroup: no barrier is skipped by part of it
   const int ctx = P.context_lens[s];
-  const int pos0 = ctx - q_len + q0;  // position of the tile's first query
-  const int kv_end = pos0 + nq;       // keys [0, kv_end)
-  if (pos0 < 0) return;               // inconsistent lengths: nothing is read
+  const int pos0 = ctx - q_len + q0;
+  if (pos0 < 0) return;  // inconsistent lengths: nothing is read
+  const int nq_wg = min(kWgQueries, q_len - q0);
+  const int kv_end = pos0 + nq_wg;  // keys [0, kv_end) for the workgroup
+  const int last = kv_end - 1;
   const int qi = lane & 15;
   const int g = lane >> 4;
-  const bool has_q = qi < nq;
-  const int my_pos = pos0 + qi;
-  const size_t qrow = (size_t(q_begin + q0 + (has_q ? qi : 0)) * H + h);
-
-  u32x4 qv[NK];
+  // set k of this wave: queries q0 + wave * kWaveQueries + 16 k + (0..15)
+  const int wq0 = wave * kWaveQueries;
+  const int nq_w = max(0, min(kWaveQueries, nq_wg - wq0));
+  const int wpos0 = pos0 + wq0;
+  const int w_end = nq_w > 0 ? wpos0 + nq_w : 0;  // keys this wave needs
+  bool has_q[NS];
+  int my_pos[NS];
+  size_t qrow[NS];
+  u32x4 qv[NS][NK];
 #pragma unroll
-  for (int j = 0; j < NK; ++j)
-    qv[j] = has_q ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(P.q) +
-                                                    qrow * kRowBytes + (32 * j + 8 * g) * sizeof(T))
-                  : u32x4{0, 0, 0, 0};
+  for (int k = 0; k < NS; ++k) {
+    has_q[k] = 16 * k + qi < nq_w;
+    my_pos[k] = wpos0 + 16 * k + qi;
+    qrow[k] = size_t(q_begin + q0 + wq0 + 16 * k + (has_q[k] ? qi : 0)) * H + h;
+#pragma unroll
+    for (int j = 0; j < NK; ++j)
+      qv[k][j] = has_q[k]
+                     ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(P.q) +
+                                                       qrow[k] * kRowBytes +
+                                                       (32 * j + 8 * g) * sizeof(T))
+                     : u32x4{0, 0, 0, 0};
+  }
 
   const int log2_bs = P.log2_bs;
   const int bs_mask = (1 << log2_bs) - 1;
@@ -92,80 +136,116 @@ __global__ __launch_bounds__(kWave, 2) void prefill_mfma_kernel(PrefillParams P)
   const int32_t* trow = P.block_tables + size_t(s) * P.maxB;
   const char* kc = reinterpret_cast<const char*>(P.k_cache);
   const char* vc = reinterpret_cast<const char*>(P.v_cache);
-  const int last = kv_end - 1;
-  // Byte offset of token row tt + r (r < 16) of the sequence, clamped to the
-  // last key; a 16-token tile spans at most two blocks.
-  auto row_off = [&](int tt, int r) -> size_t {
-    const int lo = __builtin_amdgcn_readfirstlane(min(tt, last) >> log2_bs);
-    const int hi = __builtin_amdgcn_readfirstlane(min(tt + 15, last) >> log2_bs);
-    const int b_lo = trow[lo];
-    const int b_hi = trow[hi];
-    const int t = min(tt + r, last);
-    const int b = (t >> log2_bs) == lo ? b_lo : b_hi;
-    return (size_t(uint32_t(b) * uint32_t(H) + uint32_t(h)) << log2_tile) +
-           size_t(t & bs_mask) * kRowBytes;
+
+  // Cooperative load of one step: thread tid moves chunks tid, tid + 256, ...
+  // of K and of V (row = chunk / (D/8), 16-byte column = chunk % (D/8));
+  // rows past the last key are clamped to it.  A wave's rows of one chunk
+  // group are 64 / (D/8) consecutive rows aligned to that count (<= 8 <= bs),
+  // so they lie in one block: its id is a wave-uniform (scalar) table load.
+  constexpr int kRowsPerGroup = kPfWaves * kWave / (D / 8);  // rows per chunk group
+  struct Ids { int b[kPerThread]; };
+  auto load_ids = [&](int base, Ids& ids) {
+#pragma unroll
+    for (int c = 0; c < kPerThread; ++c) {
+      const int r0 = c * kRowsPerGroup + wave * (kWave / (D / 8));  // first row of the wave
+      const int t = wave_uniform(min(base + r0, last));
+      ids.b[c] = trow[t >> log2_bs];
+    }
+  };
+  struct Regs { u32x4 k[kPerThread], v[kPerThread]; };
+  auto load_step = [&](int base, const Ids& ids, Regs& g_) {
+#pragma unroll
+    for (int c = 0; c < kPerThread; ++c) {
+      const int chunk = tid + c * kPfWaves * kWave;
+      const int r = chunk / (D / 8), col = chunk % (D / 8);
+      const int t = min(base + r, last);
+      const int r0 = c * kRowsPerGroup + wave * (kWave / (D / 8));
+      // a clamped row may fall in the last key's block rather than the group's
+      const int t0 = min(base + r0, last);
+      const int b = (t >> log2_bs) == (t0 >> log2_bs) ? ids.b[c] : trow[t >> log2_bs];
+      const size_t off = (size_t(uint32_t(b) * uint32_t(H) + uint32_t(h)) << log2_tile) +
+                         size_t(t & bs_mask) * kRowBytes + size_t(col) * 16;
+      g_.k[c] = *reinterpret_cast<const u32x4*>(kc + off);
+      g_.v[c] = *reinterpret_cast<const u32x4*>(vc + off);
+    }
+  };
+  auto store_step = [&](int buf, const Regs& g_) {
+#pragma unroll
+    for (int c = 0; c < kPerThread; ++c) {
+      const int chunk = tid + c * kPfWaves * kWave;
+      const int r = chunk / (D / 8), col = chunk % (D / 8);
+      *reinterpret_cast<u32x4*>(&lds[buf][0][L::at(r, col)]) = g_.k[c];
+      *reinterpret_cast<u32x4*>(&lds[buf][1][L::at(r, col)]) = g_.v[c];
+    }
   };
 
-  float m = kPfNegBig, l = 0.f;
-  f32x4 o[NJ];
+  float m[NS], l[NS];
+  f32x4 o[NS][NJ];
 #pragma unroll
-  for (int jd = 0; jd < NJ; ++jd) o[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < NS; ++k) {
+    m[k] = kPfNegBig;
+    l[k] = 0.f;
+#pragma unroll
+    for (int jd = 0; jd < NJ; ++jd) o[k][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const float qk_scale = P.qk_scale;
 
-  for (int base = 0; base < kv_end; base += 32) {
-    u32x4 kr[2][NK];
+  auto compute = [&](int buf, int base) {
+    const char* lk = lds[buf][0];
+    const char* lv = lds[buf][1];
+    // one K operand read from LDS serves the NS query sets
+    f32x4 sc[NS][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) sc[k][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const u32x4 kr = *reinterpret_cast<const u32x4*>(lk + L::at(16 * a + qi, 4 * j + g));
+#pragma unroll
+        for (int k = 0; k < NS; ++k) sc[k][a] = mma16x16x32(DT{}, kr, qv[k][j], sc[k][a]);
+      }
+    }
+    u32x4 phi[NS], plo[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      float x[8];
+      const bool masked = base + kPfKeys > wpos0 + 16 * k;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = base + 16 * (e >> 2) + 4 * g + (e & 3);
+        x[e] = sc[k][e >> 2][e & 3] * qk_scale;
+        if (masked && t > my_pos[k]) x[e] = -__builtin_inff();
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mn = fmaxf(m[k], mx);
+      const float alpha = fast_exp2(m[k] - mn);
+      m[k] = mn;
+      l[k] *= alpha;
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) {
+        const float p0 = fast_exp2(x[2 * p2] - mn), p1 = fast_exp2(x[2 * p2 + 1] - mn);
+        l[k] += p0 + p1;
+        uint32_t hw, lw;
+        split_pair(DT{}, p0, p1, hw, lw);
+        phi[k][p2] = hw;
+        plo[k][p2] = lw;
+      }
+#pragma unroll
+      for (int jd = 0; jd < NJ; ++jd) o[k][jd] *= alpha;
+    }
     VRow vr[8];
+    // lane qi's NJ elements of a row: chunk qi (D = 128) or half of chunk qi / 2
+    constexpr int kLanesPerChunk = 16 / (NJ * 2);
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int tt = base + 16 * a;
-      const char* kp = kc + row_off(tt, qi) + 8 * g * sizeof(T);
-#pragma unroll
-      for (int j = 0; j < NK; ++j)
-        kr[a][j] = *reinterpret_cast<const u32x4*>(kp + 32 * j * sizeof(T));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vr[4 * a + i] = *reinterpret_cast<const VRow*>(vc + row_off(tt, 4 * g + i) +
-                                                       qi * NJ * sizeof(T));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 sc[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      sc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < NK; ++j) sc[a] = mma16x16x32(DT{}, kr[a][j], qv[j], sc[a]);
-    }
-    // x[e]: key base + 16 (e / 4) + 4 g + e % 4, query qi; keys after the
-    // query's position (and past the last key) get weight 0
-    float x[8];
-    const bool masked = base + 32 > pos0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = base + 16 * (e >> 2) + 4 * g + (e & 3);
-      x[e] = sc[e >> 2][e & 3] * qk_scale;
-      if (masked && t > my_pos) x[e] = -__builtin_inff();
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    l *= alpha;
-    u32x4 phi, plo;
-#pragma unroll
-    for (int p2 = 0; p2 < 4; ++p2) {
-      const float p0 = fast_exp2(x[2 * p2] - mn), p1 = fast_exp2(x[2 * p2 + 1] - mn);
-      l += p0 + p1;
-      uint32_t hw, lw;
-      split_pair(DT{}, p0, p1, hw, lw);
-      phi[p2] = hw;
-      plo[p2] = lw;
-    }
-#pragma unroll
-    for (int jd = 0; jd < NJ; ++jd) o[jd] *= alpha;
+    for (int e = 0; e < 8; ++e)
+      vr[e] = *reinterpret_cast<const VRow*>(
+          lv + L::at(16 * (e >> 2) + 4 * g + (e & 3), qi / kLanesPerChunk) +
+          (qi % kLanesPerChunk) * NJ * 2);
 #pragma unroll
     for (int jd = 0; jd < NJ; ++jd) {
       const uint32_t sel = (jd & 1) ? 0x07060302u : 0x05040100u;
@@ -174,30 +254,73 @@ __global__ __launch_bounds__(kWave, 2) void prefill_mfma_kernel(PrefillParams P)
       for (int p2 = 0; p2 < 4; ++p2)
         va[p2] = __builtin_amdgcn_perm(uint32_t(vr[2 * p2 + 1][jd >> 1]),
                                        uint32_t(vr[2 * p2][jd >> 1]), sel);
-      o[jd] = mma16x16x32(DT{}, va, phi, o[jd]);
-      o[jd] = mma16x16x32(DT{}, va, plo, o[jd]);
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        o[k][jd] = mma16x16x32(DT{}, va, phi[k], o[k][jd]);
+        o[k][jd] = mma16x16x32(DT{}, va, plo[k], o[k][jd]);
+      }
     }
+  };
+
+  // Steps: LDS double buffer, and global loads two steps ahead in
+  // registers (steps c + 1 and c + 2 in flight while step c is computed);
+  // one barrier per step makes the next buffer's writes visible and keeps a
+  // buffer from being overwritten while another wave still reads it.  Loads
+  // are issued unconditionally (steps past the end read the clamped last row
+  // again): a load issued on one path only would make the compiler wait for
+  // every load where the paths join.
+  const int nsteps = (kv_end + kPfKeys - 1) / kPfKeys;
+  Ids ida, idb;
+  Regs ra, rb;
+  load_ids(0, ida);
+  load_step(0, ida, ra);
+  load_ids(kPfKeys, idb);
+  load_step(kPfKeys, idb, rb);
+  store_step(0, ra);
+  __syncthreads();
+  for (int c = 0; c < nsteps; ++c) {
+    // registers: rb holds step c + 1 (in flight); ra is free for step c + 2
+    load_ids((c + 2) * kPfKeys, ida);
+    load_step((c + 2) * kPfKeys, ida, ra);
+    const int base = c * kPfKeys;
+    if (base < w_end) compute(c & 1, base);  // wave-uniform: keys this wave needs
+    if (c + 1 < nsteps) store_step((c + 1) & 1, rb);
+    __syncthreads();
+    Regs t = rb;  // the step loaded two steps ahead becomes the next one
+    rb = ra;
+    ra = t;
   }
 
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
-  if (!has_q) return;
-  const float inv = 1.0f / l;  // l >= 1: the running max key contributes 2^0
-  T* out = reinterpret_cast<T*>(P.out) + qrow * D;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    VRow w;
+  for (int k = 0; k < NS; ++k) {
+    float lk = l[k];
+    lk += __shfl_xor(lk, 16, kWave);
+    lk += __shfl_xor(lk, 32, kWave);
+    if (!has_q[k]) continue;
+    const float inv = 1.0f / lk;  // l >= 1: the running max key contributes 2^0
+    T* out = reinterpret_cast<T*>(P.out) + qrow[k] * D;
 #pragma unroll
-    for (int p2 = 0; p2 < NJ / 2; ++p2)
-      w[p2] = pack_store(DT{}, o[2 * p2][r] * inv, o[2 * p2 + 1][r] * inv);
-    *reinterpret_cast<VRow*>(out + NJ * (4 * g + r)) = w;
+    for (int r = 0; r < 4; ++r) {
+      VRow w;
+#pragma unroll
+      for (int p2 = 0; p2 < NJ / 2; ++p2)
+        w[p2] = pack_store(DT{}, o[k][2 * p2][r] * inv, o[k][2 * p2 + 1][r] * inv);
+      *reinterpret_cast<VRow*>(out + NJ * (4 * g + r)) = w;
+    }
   }
 }
 
+#ifndef PA_PREFILL_SETS
+#define PA_PREFILL_SETS 2
+#endif
+constexpr int kPfSets = PA_PREFILL_SETS;  // 16-query sets per wave
+
 template <class DT, int D>
 void launch_prefill(const PrefillParams& p, int S, int max_q_len, hipStream_t st) {
-  const dim3 grid(unsigned((max_q_len + 15) / 16), unsigned(p.H), unsigned(S));
-  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D>), grid, dim3(kWave), 0, st, p);
+  constexpr int q_per_wg = 16 * kPfSets * kPfWaves;
+  const dim3 grid(unsigned((max_q_len + q_per_wg - 1) / q_per_wg), unsigned(p.H), unsigned(S));
+  hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, kPfSets>), grid, dim3(kPfWaves * kWave), 0, st,
+                     p);
 }
 
 }  // namespace
