@@ -149,14 +149,23 @@ __device__ __forceinline__ void split_pair(BF16, float x0, float x1, uint32_t& h
                              0x07060302u);
 }
 
-// Two float32 values rounded (nearest even) to the storage type, packed.
+// Two float32 values rounded (nearest even) to the storage type, packed
+// (one v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t round_pair(F16, float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), h2));
+}
+__device__ __forceinline__ uint32_t round_pair(BF16, float a, float b) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), b2));
+}
 __device__ __forceinline__ uint32_t pack_store(F16, float a, float b) {
-  return uint32_t(__builtin_bit_cast(uint16_t, (_Float16)a)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)b)) << 16);
+  return round_pair(F16{}, a, b);
 }
 __device__ __forceinline__ uint32_t pack_store(BF16, float a, float b) {
-  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)a)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)b)) << 16);
+  return round_pair(BF16{}, a, b);
 }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

@@ -40,6 +40,7 @@ namespace {
 
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfNegBig = -1.0e30f;  // running-max start: finite
+constexpr float kPfSlack = 8.0f;       // lazy rescale threshold, log2 units
 
 struct PrefillParams {
   const void* q;       // [T, H, D] queries of all sequences, packed
@@ -93,7 +94,8 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
   const int tid = threadIdx.x;
   const int wave = wave_uniform(tid / kWave);
   const int lane = tid & (kWave - 1);
-  const int qt = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // grid (heads, sequences, query tiles), the last (longest) tiles dispatched first
+  const int h = blockIdx.x, s = blockIdx.y, qt = gridDim.z - 1 - blockIdx.z;
   const int H = P.H;
   const int q_begin = P.cu_q[s];
   const int q_len = P.cu_q[s + 1] - q_begin;
@@ -138,18 +140,24 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
   const char* vc = reinterpret_cast<const char*>(P.v_cache);
 
   // Cooperative load of one step: thread tid moves chunks tid, tid + 256, ...
-  // of K and of V (row = chunk / (D/8), 16-byte column = chunk % (D/8));
-  // rows past the last key are clamped to it.  A wave's rows of one chunk
-  // group are 64 / (D/8) consecutive rows aligned to that count (<= 8 <= bs),
-  // so they lie in one block: its id is a wave-uniform (scalar) table load.
+  // of K and of V (row = chunk / (D/8), 16-byte column = chunk % (D/8)).  A
+  // wave's rows of one chunk group are 64 / (D/8) consecutive rows aligned to
+  // that count (<= 8 <= bs), so they lie in one block: its id is one scalar
+  // load from the table, read through the constant address space (the table
+  // is not written here).  A group that starts past the last key reads the
+  // last key's block instead; rows past the last key are read from their
+  // group's block (allocated memory, any content), their K scores are masked
+  // and their V rows are stored to LDS as zeros.
   constexpr int kRowsPerGroup = kPfWaves * kWave / (D / 8);  // rows per chunk group
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
+  ConstI32* trow_c = (ConstI32*)trow;
   struct Ids { int b[kPerThread]; };
   auto load_ids = [&](int base, Ids& ids) {
 #pragma unroll
     for (int c = 0; c < kPerThread; ++c) {
       const int r0 = c * kRowsPerGroup + wave * (kWave / (D / 8));  // first row of the wave
       const int t = wave_uniform(min(base + r0, last));
-      ids.b[c] = trow[t >> log2_bs];
+      ids.b[c] = trow_c[t >> log2_bs];
     }
   };
   struct Regs { u32x4 k[kPerThread], v[kPerThread]; };
@@ -158,24 +166,21 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
     for (int c = 0; c < kPerThread; ++c) {
       const int chunk = tid + c * kPfWaves * kWave;
       const int r = chunk / (D / 8), col = chunk % (D / 8);
-      const int t = min(base + r, last);
-      const int r0 = c * kRowsPerGroup + wave * (kWave / (D / 8));
-      // a clamped row may fall in the last key's block rather than the group's
-      const int t0 = min(base + r0, last);
-      const int b = (t >> log2_bs) == (t0 >> log2_bs) ? ids.b[c] : trow[t >> log2_bs];
-      const size_t off = (size_t(uint32_t(b) * uint32_t(H) + uint32_t(h)) << log2_tile) +
-                         size_t(t & bs_mask) * kRowBytes + size_t(col) * 16;
+      const size_t off = (size_t(uint32_t(ids.b[c]) * uint32_t(H) + uint32_t(h)) << log2_tile) +
+                         size_t((base + r) & bs_mask) * kRowBytes + size_t(col) * 16;
       g_.k[c] = *reinterpret_cast<const u32x4*>(kc + off);
       g_.v[c] = *reinterpret_cast<const u32x4*>(vc + off);
     }
   };
-  auto store_step = [&](int buf, const Regs& g_) {
+  auto store_step = [&](int buf, int base, const Regs& g_) {
 #pragma unroll
     for (int c = 0; c < kPerThread; ++c) {
       const int chunk = tid + c * kPfWaves * kWave;
       const int r = chunk / (D / 8), col = chunk % (D / 8);
+      const bool live = base + r <= last;
       *reinterpret_cast<u32x4*>(&lds[buf][0][L::at(r, col)]) = g_.k[c];
-      *reinterpret_cast<u32x4*>(&lds[buf][1][L::at(r, col)]) = g_.v[c];
+      *reinterpret_cast<u32x4*>(&lds[buf][1][L::at(r, col)]) =
+          live ? g_.v[c] : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -189,6 +194,9 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
     for (int jd = 0; jd < NJ; ++jd) o[k][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float qk_scale = P.qk_scale;
+  // float16 weights are rounded once (relative error <= 2^-11, weights <= 2^8);
+  // bfloat16 weights keep a low part so that they stay close to float32.
+  constexpr bool kSplitP = !std::is_same<DT, F16>::value;
 
   auto compute = [&](int buf, int base) {
     const char* lk = lds[buf][0];
@@ -209,34 +217,46 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
     u32x4 phi[NS], plo[NS];
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      float x[8];
-      const bool masked = base + kPfKeys > wpos0 + 16 * k;
+      float x[8];  // raw scores q.k of keys base + 16 (e / 4) + 4 g + e % 4
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = base + 16 * (e >> 2) + 4 * g + (e & 3);
-        x[e] = sc[k][e >> 2][e & 3] * qk_scale;
-        if (masked && t > my_pos[k]) x[e] = -__builtin_inff();
+      for (int e = 0; e < 8; ++e) x[e] = sc[k][e >> 2][e & 3];
+      if (base + kPfKeys > wpos0 + 16 * k) {  // wave-uniform: a step on this set's diagonal
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (base + 16 * (e >> 2) + 4 * g + (e & 3) > my_pos[k]) x[e] = -__builtin_inff();
       }
       float mx = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mn = fmaxf(m[k], mx);
-      const float alpha = fast_exp2(m[k] - mn);
-      m[k] = mn;
-      l[k] *= alpha;
+      // The running reference m moves only when a column's maximum passes it by
+      // more than kPfSlack (log2 units): weights stay <= 2^kPfSlack, and the
+      // rescale of O and l is skipped on most steps.  o / l does not depend on m.
+      const float ms = mx * qk_scale;
+      if (__builtin_amdgcn_ballot_w64(ms > m[k] + kPfSlack) != 0) {
+        const float mn = fmaxf(m[k], ms);
+        const float alpha = fast_exp2(m[k] - mn);
+        m[k] = mn;
+        l[k] *= alpha;
+#pragma unroll
+        for (int jd = 0; jd < NJ; ++jd) o[k][jd] *= alpha;
+      }
+      const float neg_m = -m[k];
 #pragma unroll
       for (int p2 = 0; p2 < 4; ++p2) {
-        const float p0 = fast_exp2(x[2 * p2] - mn), p1 = fast_exp2(x[2 * p2 + 1] - mn);
+        const float p0 = fast_exp2(fmaf(x[2 * p2], qk_scale, neg_m));
+        const float p1 = fast_exp2(fmaf(x[2 * p2 + 1], qk_scale, neg_m));
         l[k] += p0 + p1;
-        uint32_t hw, lw;
-        split_pair(DT{}, p0, p1, hw, lw);
-        phi[k][p2] = hw;
-        plo[k][p2] = lw;
+        if constexpr (kSplitP) {
+          uint32_t hw, lw;
+          split_pair(DT{}, p0, p1, hw, lw);
+          phi[k][p2] = hw;
+          plo[k][p2] = lw;
+        } else {
+          phi[k][p2] = round_pair(DT{}, p0, p1);
+        }
       }
-#pragma unroll
-      for (int jd = 0; jd < NJ; ++jd) o[k][jd] *= alpha;
     }
     VRow vr[8];
     // lane qi's NJ elements of a row: chunk qi (D = 128) or half of chunk qi / 2
@@ -257,7 +277,7 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         o[k][jd] = mma16x16x32(DT{}, va, phi[k], o[k][jd]);
-        o[k][jd] = mma16x16x32(DT{}, va, plo[k], o[k][jd]);
+        if constexpr (kSplitP) o[k][jd] = mma16x16x32(DT{}, va, plo[k], o[k][jd]);
       }
     }
   };
@@ -265,10 +285,12 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
   // Steps: LDS double buffer, and global loads two steps ahead in
   // registers (steps c + 1 and c + 2 in flight while step c is computed);
   // one barrier per step makes the next buffer's writes visible and keeps a
-  // buffer from being overwritten while another wave still reads it.  Loads
-  // are issued unconditionally (steps past the end read the clamped last row
-  // again): a load issued on one path only would make the compiler wait for
-  // every load where the paths join.
+  // buffer from being overwritten while another wave still reads it.  The
+  // loop is unrolled by two so that the two register sets keep fixed roles
+  // (no copies that would wait for the loads in flight), block ids are read
+  // one step before their loads, and loads are issued unconditionally (steps
+  // past the end read in-bounds rows again): a load issued on one path only
+  // would make the compiler wait for every load where the paths join.
   const int nsteps = (kv_end + kPfKeys - 1) / kPfKeys;
   Ids ida, idb;
   Regs ra, rb;
@@ -276,19 +298,22 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
   load_step(0, ida, ra);
   load_ids(kPfKeys, idb);
   load_step(kPfKeys, idb, rb);
-  store_step(0, ra);
+  load_ids(2 * kPfKeys, ida);
+  store_step(0, 0, ra);
   __syncthreads();
-  for (int c = 0; c < nsteps; ++c) {
-    // registers: rb holds step c + 1 (in flight); ra is free for step c + 2
-    load_ids((c + 2) * kPfKeys, ida);
+  for (int c = 0; c < nsteps; c += 2) {
+    // step c: ra free, rb holds step c + 1, ida step c + 2's ids
     load_step((c + 2) * kPfKeys, ida, ra);
-    const int base = c * kPfKeys;
-    if (base < w_end) compute(c & 1, base);  // wave-uniform: keys this wave needs
-    if (c + 1 < nsteps) store_step((c + 1) & 1, rb);
+    load_ids((c + 3) * kPfKeys, idb);
+    if (c * kPfKeys < w_end) compute(0, c * kPfKeys);  // wave-uniform: keys this wave needs
+    if (c + 1 < nsteps) store_step(1, (c + 1) * kPfKeys, rb);
     __syncthreads();
-    Regs t = rb;  // the step loaded two steps ahead becomes the next one
-    rb = ra;
-    ra = t;
+    // step c + 1: rb free, ra holds step c + 2, idb step c + 3's ids
+    load_step((c + 3) * kPfKeys, idb, rb);
+    load_ids((c + 4) * kPfKeys, ida);
+    if (c + 1 < nsteps && (c + 1) * kPfKeys < w_end) compute(1, (c + 1) * kPfKeys);
+    if (c + 2 < nsteps) store_step(0, (c + 2) * kPfKeys, ra);
+    __syncthreads();
   }
 
 #pragma unroll
@@ -318,7 +343,7 @@ constexpr int kPfSets = PA_PREFILL_SETS;  // 16-query sets per wave
 template <class DT, int D>
 void launch_prefill(const PrefillParams& p, int S, int max_q_len, hipStream_t st) {
   constexpr int q_per_wg = 16 * kPfSets * kPfWaves;
-  const dim3 grid(unsigned((max_q_len + q_per_wg - 1) / q_per_wg), unsigned(p.H), unsigned(S));
+  const dim3 grid(unsigned(p.H), unsigned(S), unsigned((max_q_len + q_per_wg - 1) / q_per_wg));
   hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, kPfSets>), grid, dim3(kPfWaves * kWave), 0, st,
                      p);
 }
