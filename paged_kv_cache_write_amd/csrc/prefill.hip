@@ -59,19 +59,58 @@ struct PrefillParams {
 constexpr int kPfWaves = 4;                 // waves per workgroup
 constexpr int kPfKeys = 32;                 // keys per step
 
-// LDS layout of one step's K (or V): key rows of D elements; the 16-byte
-// chunk c of row r is stored at chunk c ^ (r mod chunks-per-row), so the 16
-// lanes of every operand read (16 rows of one chunk, or 16 chunks of one row)
-// and of the cooperative stores touch 16 different chunks: no bank conflicts.
+// LDS layout of one step.  K: key rows of D elements; the 16-byte chunk c
+// of row r sits at chunk c ^ f(r), f(r) = (r >> (1 for D = 64)) mod
+// chunks-per-row, so the 16 lanes of every K operand read (16 rows of one
+// chunk) and of the cooperative stores (consecutive chunks of a row) fall on
+// different banks.  V: key rows padded by 32 bytes, no swizzle: the
+// transposed reads that build V^T operands then sit at constant offsets from
+// a per-lane base, and the 32 lanes of each half of such a read (8 rows x 32
+// bytes) cover the 64 banks once.
 template <int D>
 struct PfLds {
   static constexpr int kRow = D * 2;
   static constexpr int kChunksPerRow = kRow / 16;
-  static constexpr int kMat = kPfKeys * kRow;  // one K (or V) step
+  static constexpr int kShift = D == 64 ? 1 : 0;
+  static constexpr int kMat = kPfKeys * kRow;  // one K step
+  static constexpr int kVRow = kRow + 32;
+  static constexpr int kVMat = kPfKeys * kVRow;  // one V step
   static __device__ __forceinline__ int at(int row, int chunk) {
-    return row * kRow + ((chunk ^ (row & (kChunksPerRow - 1))) << 4);
+    return row * kRow + ((chunk ^ ((row >> kShift) & (kChunksPerRow - 1))) << 4);
   }
 };
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4a + b receives element b of the 4-element vectors read by lanes a, a + 4,
+// a + 8 and a + 12 of the group.  When lane s of the group reads row s / 4,
+// columns 4 (s % 4) .. + 3 of a row-major tile, lane i thus receives column i
+// of rows 0..3: four keys of one head-dimension column.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 LdsS4;
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LdsS4*)((__attribute__((address_space(3))) const char*)p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA operand of 16 x 32 ones (the sums of P^T's columns)
+__device__ __forceinline__ u32x4 ones_operand(F16) {
+  return u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+}
+__device__ __forceinline__ u32x4 ones_operand(BF16) {
+  return u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+}
+
+// Maximum over the 4 rows of 16 lanes (v_permlane16_swap / v_permlane32_swap:
+// the rows that pair up in each swap exchange values).
+__device__ __forceinline__ float max_over_rows(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(bits_as<float>(a[0]), bits_as<float>(a[1]));
+  const uint32_t w = __builtin_bit_cast(uint32_t, v);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(bits_as<float>(b[0]), bits_as<float>(b[1]));
+}
 
 template <class DT, int D, int NS>
 __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfma_kernel(
@@ -86,10 +125,10 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
   constexpr int kLog2Row = __builtin_ctz(kRowBytes);
   constexpr int kChunks = kPfKeys * (D / 8);             // 16-byte chunks of one step's K
   constexpr int kPerThread = kChunks / (kPfWaves * kWave);  // of K, and as many of V
-  using VRow = typename std::conditional<NJ == 8, u32x4, u32x2>::type;
   static_assert(sizeof(T) == 2 && (NJ == 8 || NJ == 4), "16-bit storage, D 64 or 128");
   static_assert(kPerThread >= 1 && kChunks % (kPfWaves * kWave) == 0, "load split");
-  __shared__ __align__(16) char lds[2][2][L::kMat];  // [buffer][K, V]
+  __shared__ __align__(16) char lds_k[2][L::kMat];   // [buffer]
+  __shared__ __align__(16) char lds_v[2][L::kVMat];
 
   const int tid = threadIdx.x;
   const int wave = wave_uniform(tid / kWave);
@@ -178,18 +217,19 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
       const int chunk = tid + c * kPfWaves * kWave;
       const int r = chunk / (D / 8), col = chunk % (D / 8);
       const bool live = base + r <= last;
-      *reinterpret_cast<u32x4*>(&lds[buf][0][L::at(r, col)]) = g_.k[c];
-      *reinterpret_cast<u32x4*>(&lds[buf][1][L::at(r, col)]) =
+      *reinterpret_cast<u32x4*>(&lds_k[buf][L::at(r, col)]) = g_.k[c];
+      *reinterpret_cast<u32x4*>(&lds_v[buf][r * L::kVRow + col * 16]) =
           live ? g_.v[c] : u32x4{0, 0, 0, 0};
     }
   };
 
-  float m[NS], l[NS];
+  float m[NS];
   f32x4 o[NS][NJ];
+  f32x4 ol[NS];  // row sums of the weights, from the matrix cores (a V^T tile of ones)
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     m[k] = kPfNegBig;
-    l[k] = 0.f;
+    ol[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jd = 0; jd < NJ; ++jd) o[k][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -197,10 +237,13 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
   // float16 weights are rounded once (relative error <= 2^-11, weights <= 2^8);
   // bfloat16 weights keep a low part so that they stay close to float32.
   constexpr bool kSplitP = !std::is_same<DT, F16>::value;
+  // this lane's part of the transposed V reads: row 4 g + qi / 4, 4 columns
+  // from 4 (qi % 4); the other key half is 16 rows further
+  const int v_lane = (4 * g + (qi >> 2)) * L::kVRow + 8 * (qi & 3);
 
   auto compute = [&](int buf, int base) {
-    const char* lk = lds[buf][0];
-    const char* lv = lds[buf][1];
+    const char* lk = lds_k[buf];
+    const char* lv = lds_v[buf] + v_lane;
     // one K operand read from LDS serves the NS query sets
     f32x4 sc[NS][2];
 #pragma unroll
@@ -228,8 +271,7 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
       float mx = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = max_over_rows(mx);
       // The running reference m moves only when a column's maximum passes it by
       // more than kPfSlack (log2 units): weights stay <= 2^kPfSlack, and the
       // rescale of O and l is skipped on most steps.  o / l does not depend on m.
@@ -238,7 +280,7 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
         const float mn = fmaxf(m[k], ms);
         const float alpha = fast_exp2(m[k] - mn);
         m[k] = mn;
-        l[k] *= alpha;
+        ol[k][0] *= alpha;  // only element 0 is read
 #pragma unroll
         for (int jd = 0; jd < NJ; ++jd) o[k][jd] *= alpha;
       }
@@ -247,7 +289,6 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
       for (int p2 = 0; p2 < 4; ++p2) {
         const float p0 = fast_exp2(fmaf(x[2 * p2], qk_scale, neg_m));
         const float p1 = fast_exp2(fmaf(x[2 * p2 + 1], qk_scale, neg_m));
-        l[k] += p0 + p1;
         if constexpr (kSplitP) {
           uint32_t hw, lw;
           split_pair(DT{}, p0, p1, hw, lw);
@@ -258,22 +299,20 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
         }
       }
     }
-    VRow vr[8];
-    // lane qi's NJ elements of a row: chunk qi (D = 128) or half of chunk qi / 2
-    constexpr int kLanesPerChunk = 16 / (NJ * 2);
+    // O^T += V^T P^T: the V^T operand of head-dimension tile jd (rows d =
+    // 16 jd + 0..15, k-slots = this lane group's keys 4 g + 0..3 and
+    // 16 + 4 g + 0..3, matching P^T's slots) is two transposed reads.
+    const u32x4 ones = ones_operand(DT{});
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      vr[e] = *reinterpret_cast<const VRow*>(
-          lv + L::at(16 * (e >> 2) + 4 * g + (e & 3), qi / kLanesPerChunk) +
-          (qi % kLanesPerChunk) * NJ * 2);
+    for (int k = 0; k < NS; ++k) {
+      ol[k] = mma16x16x32(DT{}, ones, phi[k], ol[k]);
+      if constexpr (kSplitP) ol[k] = mma16x16x32(DT{}, ones, plo[k], ol[k]);
+    }
 #pragma unroll
     for (int jd = 0; jd < NJ; ++jd) {
-      const uint32_t sel = (jd & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 va;
-#pragma unroll
-      for (int p2 = 0; p2 < 4; ++p2)
-        va[p2] = __builtin_amdgcn_perm(uint32_t(vr[2 * p2 + 1][jd >> 1]),
-                                       uint32_t(vr[2 * p2][jd >> 1]), sel);
+      const u32x2 v0 = lds_read_tr16(lv + 32 * jd);
+      const u32x2 v1 = lds_read_tr16(lv + 16 * L::kVRow + 32 * jd);
+      const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         o[k][jd] = mma16x16x32(DT{}, va, phi[k], o[k][jd]);
@@ -318,19 +357,14 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
 
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    float lk = l[k];
-    lk += __shfl_xor(lk, 16, kWave);
-    lk += __shfl_xor(lk, 32, kWave);
     if (!has_q[k]) continue;
-    const float inv = 1.0f / lk;  // l >= 1: the running max key contributes 2^0
-    T* out = reinterpret_cast<T*>(P.out) + qrow[k] * D;
+    const float inv = 1.0f / ol[k][0];  // >= 1: the reference key's weight is 2^0 or more
+    T* out = reinterpret_cast<T*>(P.out) + qrow[k] * D + 4 * g;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      VRow w;
-#pragma unroll
-      for (int p2 = 0; p2 < NJ / 2; ++p2)
-        w[p2] = pack_store(DT{}, o[k][2 * p2][r] * inv, o[k][2 * p2 + 1][r] * inv);
-      *reinterpret_cast<VRow*>(out + NJ * (4 * g + r)) = w;
+    for (int jd = 0; jd < NJ; ++jd) {
+      const u32x2 w = {pack_store(DT{}, o[k][jd][0] * inv, o[k][jd][1] * inv),
+                       pack_store(DT{}, o[k][jd][2] * inv, o[k][jd][3] * inv)};
+      *reinterpret_cast<u32x2*>(out + 16 * jd) = w;  // d = 16 jd + 4 g + 0..3
     }
   }
 }
