@@ -14,21 +14,21 @@
 // tile, q.K and P.V are dense products for the matrix cores.  A workgroup of
 // 4 waves owns (sequence, head, 128 consecutive queries), 32 per wave in two
 // column sets of 16 (each K or V operand read from LDS feeds both), and
-// streams keys 0 .. its last query's position in steps of 32: the step's K
-// and V rows are loaded once for the workgroup (coalesced 16-byte loads,
-// block ids read per row from the table) into LDS, double-buffered so the
-// next step's loads are in flight during this one, and each wave computes
+// streams keys 0 .. its last query's position in steps of 64: the step's K
+// and V rows are loaded once for the workgroup (coalesced 16-byte loads; the
+// block id of each wave's group of rows is one scalar table load) into
+// registers while the previous step is computed, then stored into one of two
+// LDS buffers.  Each wave computes
 //   S^T[t][q] = sum_d K[t][d] Q[q][d]        (v_mfma_f32_16x16x32, A = K rows)
-//   O^T[d][q] += sum_t V^T[d][t] P^T[t][q]   (P^T is S^T's layout; the d axis
-//                                             of this product is permuted so V
-//                                             comes from plain row reads)
-// with the online softmax per query column, the causal mask (key t > query
-// position -> weight 0) on the steps that reach the wave's own positions, and
-// P split into storage-type hi + lo parts so the weights keep float32-like
-// precision.  A wave skips the steps after its last query.  Rows past the
-// workgroup's last key are clamped to it (never an unwritten slot or a table
-// entry past the sequence) and masked.  LDS rows are padded by 16 bytes so the
-// 16 rows of one operand read start on different banks.
+//   O^T[d][q] += sum_t V^T[d][t] P^T[t][q]   (P^T is S^T's layout; V^T comes
+//                                             from transposed LDS reads)
+// with the online softmax per query column (base 2, lazy rescale), the causal
+// mask (key t > query position -> weight 0) only on the steps that cross the
+// wave's own positions, and l = sum P from one more product against ones.
+// Float16 weights are rounded once; bfloat16 weights keep a hi + lo pair.  A
+// wave skips the steps after its last query.  Rows past the workgroup's last
+// key are read from their group's block (allocated memory), their scores are
+// masked and their V rows are stored as zeros.
 #include <type_traits>
 
 #include "launch_common.hpp"
@@ -51,13 +51,16 @@ struct PrefillParams {
   const int32_t* context_lens;  // [S] tokens in the cache, the new ones included
   void* out;                    // [T, H, D]
   int H;
+  int S;
+  int num_tiles;  // query tiles per sequence (of the longest chunk)
   int maxB;
   int log2_bs;
   float qk_scale;  // scale * log2(e)
 };
 
 constexpr int kPfWaves = 4;                 // waves per workgroup
-constexpr int kPfKeys = 32;                 // keys per step
+constexpr int kPfKeys = 64;                 // keys per step
+constexpr int kPfTiles = kPfKeys / 16;      // 16-key tiles of S^T per step
 
 // LDS layout of one step.  K: key rows of D elements; the 16-byte chunk c
 // of row r sits at chunk c ^ f(r), f(r) = (r >> (1 for D = 64)) mod
@@ -113,7 +116,7 @@ __device__ __forceinline__ float max_over_rows(float v) {
 }
 
 template <class DT, int D, int NS>
-__global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfma_kernel(
+__global__ __launch_bounds__(kPfWaves * kWave, 2) void prefill_mfma_kernel(
     PrefillParams P) {
   using T = typename DT::T;
   using L = PfLds<D>;
@@ -133,8 +136,16 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
   const int tid = threadIdx.x;
   const int wave = wave_uniform(tid / kWave);
   const int lane = tid & (kWave - 1);
-  // grid (heads, sequences, query tiles), the last (longest) tiles dispatched first
-  const int h = blockIdx.x, s = blockIdx.y, qt = gridDim.z - 1 - blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i mod 8).
+  // All query tiles of one (sequence, head) go to one XCD, whose L2 then
+  // holds the keys they share; over the grid the last (longest, under the
+  // causal mask) tiles go first, so that the short ones fill the end.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int groups_per_xcd = (P.S * P.H + 7) / 8;
+  const int grp = xcd + 8 * (slot % groups_per_xcd);
+  const int qt = P.num_tiles - 1 - slot / groups_per_xcd;
+  if (grp >= P.S * P.H) return;
+  const int h = grp % P.H, s = grp / P.H;
   const int H = P.H;
   const int q_begin = P.cu_q[s];
   const int q_len = P.cu_q[s + 1] - q_begin;
@@ -245,9 +256,9 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
     const char* lk = lds_k[buf];
     const char* lv = lds_v[buf] + v_lane;
     // one K operand read from LDS serves the NS query sets
-    f32x4 sc[NS][2];
+    f32x4 sc[NS][kPfTiles];  // S^T tile a: keys 16 a + 4 g + r, query qi
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < kPfTiles; ++a) {
 #pragma unroll
       for (int k = 0; k < NS; ++k) sc[k][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -257,20 +268,23 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
         for (int k = 0; k < NS; ++k) sc[k][a] = mma16x16x32(DT{}, kr, qv[k][j], sc[k][a]);
       }
     }
-    u32x4 phi[NS], plo[NS];
+    // P^T per 32-key chunk b (one MFMA k-extent): k-slot 8 g + 4 a' + r holds
+    // key 32 b + 16 a' + 4 g + r
+    constexpr int NB = kPfKeys / 32;
+    u32x4 phi[NS][NB], plo[NS][NB];
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      float x[8];  // raw scores q.k of keys base + 16 (e / 4) + 4 g + e % 4
+      float x[4 * kPfTiles];  // raw scores q.k of keys base + 16 (e / 4) + 4 g + e % 4
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = sc[k][e >> 2][e & 3];
+      for (int e = 0; e < 4 * kPfTiles; ++e) x[e] = sc[k][e >> 2][e & 3];
       if (base + kPfKeys > wpos0 + 16 * k) {  // wave-uniform: a step on this set's diagonal
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 4 * kPfTiles; ++e)
           if (base + 16 * (e >> 2) + 4 * g + (e & 3) > my_pos[k]) x[e] = -__builtin_inff();
       }
       float mx = x[0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+      for (int e = 1; e < 4 * kPfTiles; ++e) mx = fmaxf(mx, x[e]);
       mx = max_over_rows(mx);
       // The running reference m moves only when a column's maximum passes it by
       // more than kPfSlack (log2 units): weights stay <= 2^kPfSlack, and the
@@ -286,72 +300,76 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
       }
       const float neg_m = -m[k];
 #pragma unroll
-      for (int p2 = 0; p2 < 4; ++p2) {
-        const float p0 = fast_exp2(fmaf(x[2 * p2], qk_scale, neg_m));
-        const float p1 = fast_exp2(fmaf(x[2 * p2 + 1], qk_scale, neg_m));
-        if constexpr (kSplitP) {
-          uint32_t hw, lw;
-          split_pair(DT{}, p0, p1, hw, lw);
-          phi[k][p2] = hw;
-          plo[k][p2] = lw;
-        } else {
-          phi[k][p2] = round_pair(DT{}, p0, p1);
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const float p0 = fast_exp2(fmaf(x[8 * b + 2 * p2], qk_scale, neg_m));
+          const float p1 = fast_exp2(fmaf(x[8 * b + 2 * p2 + 1], qk_scale, neg_m));
+          if constexpr (kSplitP) {
+            uint32_t hw, lw;
+            split_pair(DT{}, p0, p1, hw, lw);
+            phi[k][b][p2] = hw;
+            plo[k][b][p2] = lw;
+          } else {
+            phi[k][b][p2] = round_pair(DT{}, p0, p1);
+          }
         }
-      }
     }
     // O^T += V^T P^T: the V^T operand of head-dimension tile jd (rows d =
     // 16 jd + 0..15, k-slots = this lane group's keys 4 g + 0..3 and
-    // 16 + 4 g + 0..3, matching P^T's slots) is two transposed reads.
+    // 16 + 4 g + 0..3 of chunk b, matching P^T's slots) is two transposed
+    // reads.
     const u32x4 ones = ones_operand(DT{});
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      ol[k] = mma16x16x32(DT{}, ones, phi[k], ol[k]);
-      if constexpr (kSplitP) ol[k] = mma16x16x32(DT{}, ones, plo[k], ol[k]);
-    }
-#pragma unroll
-    for (int jd = 0; jd < NJ; ++jd) {
-      const u32x2 v0 = lds_read_tr16(lv + 32 * jd);
-      const u32x2 v1 = lds_read_tr16(lv + 16 * L::kVRow + 32 * jd);
-      const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+    for (int b = 0; b < NB; ++b) {
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
-        o[k][jd] = mma16x16x32(DT{}, va, phi[k], o[k][jd]);
-        if constexpr (kSplitP) o[k][jd] = mma16x16x32(DT{}, va, plo[k], o[k][jd]);
+        ol[k] = mma16x16x32(DT{}, ones, phi[k][b], ol[k]);
+        if constexpr (kSplitP) ol[k] = mma16x16x32(DT{}, ones, plo[k][b], ol[k]);
+      }
+#pragma unroll
+      for (int jd = 0; jd < NJ; ++jd) {
+        const u32x2 v0 = lds_read_tr16(lv + 32 * b * L::kVRow + 32 * jd);
+        const u32x2 v1 = lds_read_tr16(lv + (32 * b + 16) * L::kVRow + 32 * jd);
+        const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+          o[k][jd] = mma16x16x32(DT{}, va, phi[k][b], o[k][jd]);
+          if constexpr (kSplitP) o[k][jd] = mma16x16x32(DT{}, va, plo[k][b], o[k][jd]);
+        }
       }
     }
   };
 
-  // Steps: LDS double buffer, and global loads two steps ahead in
-  // registers (steps c + 1 and c + 2 in flight while step c is computed);
-  // one barrier per step makes the next buffer's writes visible and keeps a
-  // buffer from being overwritten while another wave still reads it.  The
-  // loop is unrolled by two so that the two register sets keep fixed roles
-  // (no copies that would wait for the loads in flight), block ids are read
-  // one step before their loads, and loads are issued unconditionally (steps
-  // past the end read in-bounds rows again): a load issued on one path only
-  // would make the compiler wait for every load where the paths join.
+  // Steps: LDS double buffer; the next step's rows are loaded into registers
+  // while this step is computed, then stored into the other buffer.  One
+  // barrier per step makes the stores visible and keeps a buffer from being
+  // overwritten while another wave still reads it.  Unrolled by two so that
+  // buffers are fixed per position; block ids are read one step before their
+  // loads; loads are issued unconditionally (steps past the end read in-bounds
+  // rows again): a load issued on one path only would make the compiler wait
+  // for every load where the paths join.
   const int nsteps = (kv_end + kPfKeys - 1) / kPfKeys;
   Ids ida, idb;
-  Regs ra, rb;
+  Regs r;
   load_ids(0, ida);
-  load_step(0, ida, ra);
+  load_step(0, ida, r);
   load_ids(kPfKeys, idb);
-  load_step(kPfKeys, idb, rb);
+  store_step(0, 0, r);
   load_ids(2 * kPfKeys, ida);
-  store_step(0, 0, ra);
   __syncthreads();
   for (int c = 0; c < nsteps; c += 2) {
-    // step c: ra free, rb holds step c + 1, ida step c + 2's ids
-    load_step((c + 2) * kPfKeys, ida, ra);
-    load_ids((c + 3) * kPfKeys, idb);
+    // step c (buffer 0): idb holds step c + 1's ids, ida step c + 2's
+    load_step((c + 1) * kPfKeys, idb, r);
     if (c * kPfKeys < w_end) compute(0, c * kPfKeys);  // wave-uniform: keys this wave needs
-    if (c + 1 < nsteps) store_step(1, (c + 1) * kPfKeys, rb);
+    if (c + 1 < nsteps) store_step(1, (c + 1) * kPfKeys, r);
+    load_ids((c + 3) * kPfKeys, idb);
     __syncthreads();
-    // step c + 1: rb free, ra holds step c + 2, idb step c + 3's ids
-    load_step((c + 3) * kPfKeys, idb, rb);
-    load_ids((c + 4) * kPfKeys, ida);
+    // step c + 1 (buffer 1)
+    load_step((c + 2) * kPfKeys, ida, r);
     if (c + 1 < nsteps && (c + 1) * kPfKeys < w_end) compute(1, (c + 1) * kPfKeys);
-    if (c + 2 < nsteps) store_step(0, (c + 2) * kPfKeys, ra);
+    if (c + 2 < nsteps) store_step(0, (c + 2) * kPfKeys, r);
+    load_ids((c + 4) * kPfKeys, ida);
     __syncthreads();
   }
 
@@ -369,15 +387,14 @@ __global__ __launch_bounds__(kPfWaves * kWave, NS == 1 ? 3 : 2) void prefill_mfm
   }
 }
 
-#ifndef PA_PREFILL_SETS
-#define PA_PREFILL_SETS 2
-#endif
-constexpr int kPfSets = PA_PREFILL_SETS;  // 16-query sets per wave
+constexpr int kPfSets = 2;  // 16-query sets per wave
+constexpr int kPfWgQueries = 16 * kPfSets * kPfWaves;  // queries per workgroup
 
 template <class DT, int D>
 void launch_prefill(const PrefillParams& p, int S, int max_q_len, hipStream_t st) {
-  constexpr int q_per_wg = 16 * kPfSets * kPfWaves;
-  const dim3 grid(unsigned(p.H), unsigned(S), unsigned((max_q_len + q_per_wg - 1) / q_per_wg));
+  // 8 XCDs x (sequence, head) groups per XCD x query tiles; see the kernel
+  const int64_t groups_per_xcd = (int64_t(S) * p.H + 7) / 8;
+  const dim3 grid(unsigned(8 * groups_per_xcd * p.num_tiles));
   hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, kPfSets>), grid, dim3(kPfWaves * kWave), 0, st,
                      p);
 }
@@ -415,6 +432,11 @@ int pa_prefill(const void* q, const void* k_cache, const void* v_cache,
   p.context_lens = context_lens;
   p.out = out;
   p.H = num_heads;
+  p.S = num_seqs;
+  p.num_tiles = (max_q_len + pa::kPfWgQueries - 1) / pa::kPfWgQueries;
+  // the 1-D grid's work-items (256 per workgroup) must stay below 2^32
+  if (int64_t(p.num_tiles) * ((int64_t(num_seqs) * num_heads + 7) / 8) * 8 * 256 > 0xFFFFFFFFll)
+    return PA_ERR_UNSUPPORTED;
   p.maxB = max_blocks_per_seq;
   p.log2_bs = pa::log2_exact(block_size);
   p.qk_scale = scale * pa::kPfLog2e;

@@ -63,6 +63,8 @@ class PagedKVEngine:
                                 self._dev.data_ptr(), ctypes.byref(h))
         _check(rc, "pa_engine_create")
         self._e = h
+        # kept on the instance: at interpreter exit module globals may be gone
+        self._destroy = L.pa_engine_destroy
         ws = int(L.pa_engine_workspace_bytes(self._e, self.partition_tokens))
         # zero-filled once: the decode's per-row counters start at zero and
         # every completed decode leaves them at zero
@@ -73,8 +75,9 @@ class PagedKVEngine:
 
     def __del__(self):
         e = getattr(self, "_e", None)
-        if e is not None:
-            lib().pa_engine_destroy(e)
+        destroy = getattr(self, "_destroy", None)
+        if e is not None and destroy is not None:
+            destroy(e)
             self._e = None
 
     # ------------------------------------------------------ cache building
