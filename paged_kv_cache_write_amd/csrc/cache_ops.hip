@@ -60,36 +60,57 @@ __global__ __launch_bounds__(kCwThreads) void copy_blocks_kernel(
 }
 
 // Engine step prologue.  Workgroups [0, copy_wgs) copy the staging bytes
-// from pinned host memory (read over the host link) to device memory; each
-// workgroup after them writes one new token: one lane reads the token's slot
-// from host memory, the workgroup then moves the token's H rows of K and V.
+// from pinned host memory (read over the host link) to device memory, each
+// lane kPrologueVecs 16-byte vectors whose loads are all issued before the
+// first store (one host round trip, not one per vector); each workgroup
+// after them writes one new token: one lane reads the token's slot from host
+// memory, the workgroup then moves the token's H rows of K and V.
+constexpr int kPrologueVecs = 4;
+
 __global__ __launch_bounds__(kCwThreads) void step_prologue_kernel(
     const u32x4* __restrict__ host_src, u32x4* __restrict__ dev_dst, int64_t copy_vecs,
     int copy_wgs, const int64_t* __restrict__ host_slots, const char* __restrict__ k,
     const char* __restrict__ v, char* __restrict__ k_cache, char* __restrict__ v_cache, int H,
     int vecs_per_row, int row_bytes, int log2_bs) {
   if (int(blockIdx.x) < copy_wgs) {
-    for (int64_t i = int64_t(blockIdx.x) * kCwThreads + threadIdx.x; i < copy_vecs;
-         i += int64_t(copy_wgs) * kCwThreads)
-      dev_dst[i] = host_src[i];
+    const int64_t i0 = int64_t(blockIdx.x) * kCwThreads * kPrologueVecs + threadIdx.x;
+    u32x4 x[kPrologueVecs];
+#pragma unroll
+    for (int j = 0; j < kPrologueVecs; ++j)  // clamped: every lane loads, in bounds
+      x[j] = host_src[min(i0 + int64_t(j) * kCwThreads, copy_vecs - 1)];
+#pragma unroll
+    for (int j = 0; j < kPrologueVecs; ++j)
+      if (i0 + int64_t(j) * kCwThreads < copy_vecs) dev_dst[i0 + int64_t(j) * kCwThreads] = x[j];
     return;
   }
+  // Every lane reads the slot (one host request per wave) while its K/V
+  // loads from device memory are already in flight: the two round trips
+  // overlap, and no barrier is needed.
   const int64_t n = int64_t(blockIdx.x) - copy_wgs;
-  __shared__ int64_t s_slot;
-  if (threadIdx.x == 0) s_slot = host_slots[n];
-  __syncthreads();
-  const int64_t slot = s_slot;
-  if (slot < 0) return;
-  const int64_t blk = slot >> log2_bs;
-  const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
+  const int64_t slot = host_slots[n];
   const int total = H * vecs_per_row;
-  for (int i = threadIdx.x; i < total; i += kCwThreads) {
-    const int h = i / vecs_per_row;
-    const int col = i - h * vecs_per_row;
-    const int64_t dst = ((((blk * H + h) << log2_bs) + off) * row_bytes) + int64_t(col) * 16;
-    const int64_t src = (n * total + i) * 16;
-    *reinterpret_cast<u32x4*>(k_cache + dst) = *reinterpret_cast<const u32x4*>(k + src);
-    *reinterpret_cast<u32x4*>(v_cache + dst) = *reinterpret_cast<const u32x4*>(v + src);
+  for (int base = 0; base < total; base += kCwThreads * kPrologueVecs) {
+    u32x4 kx[kPrologueVecs], vx[kPrologueVecs];
+#pragma unroll
+    for (int j = 0; j < kPrologueVecs; ++j) {  // clamped: every lane loads, in bounds
+      const int i = min(base + j * kCwThreads + int(threadIdx.x), total - 1);
+      const int64_t src = (n * total + i) * 16;
+      kx[j] = *reinterpret_cast<const u32x4*>(k + src);
+      vx[j] = *reinterpret_cast<const u32x4*>(v + src);
+    }
+    if (slot < 0) return;  // a padding token
+    const int64_t blk = slot >> log2_bs;
+    const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
+#pragma unroll
+    for (int j = 0; j < kPrologueVecs; ++j) {
+      const int i = base + j * kCwThreads + int(threadIdx.x);
+      if (i >= total) break;
+      const int h = i / vecs_per_row;
+      const int col = i - h * vecs_per_row;
+      const int64_t dst = ((((blk * H + h) << log2_bs) + off) * row_bytes) + int64_t(col) * 16;
+      *reinterpret_cast<u32x4*>(k_cache + dst) = kx[j];
+      *reinterpret_cast<u32x4*>(v_cache + dst) = vx[j];
+    }
   }
 }
 
@@ -103,8 +124,11 @@ int launch_step_prologue(const void* host_src, void* dev_dst, size_t copy_bytes,
     return PA_ERR_INVALID;
   if (n > 0 && (!k || !v || !aligned16(k) || !aligned16(v) || !host_slots)) return PA_ERR_INVALID;
   const int64_t copy_vecs = int64_t(copy_bytes / 16);
-  int copy_wgs = int((copy_vecs + kCwThreads * 4 - 1) / (kCwThreads * 4));
-  if (copy_wgs < 1) copy_wgs = 1;
+  const int64_t per_wg = int64_t(kCwThreads) * kPrologueVecs;
+  const int64_t copy_wgs64 = (copy_vecs + per_wg - 1) / per_wg;
+  if (copy_wgs64 + n > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int copy_wgs = int(copy_wgs64);  // 0 when nothing is staged
+  if (copy_wgs + n == 0) return PA_OK;
   const int row_bytes = head_dim * elem_bytes(dtype);
   (void)hipGetLastError();
   hipLaunchKernelGGL(step_prologue_kernel, dim3(unsigned(copy_wgs + n)), dim3(kCwThreads), 0,
