@@ -18,12 +18,21 @@ __all__ = [
     "decode_reduce", "decode_plan", "decode_workspace_size", "decode_schedule",
     "decode_scheduled", "decode_schedule_shared", "decode_scheduled_shared", "stream_read",
     "decode_contiguous", "copy_blocks_between", "prefill",
+    "debug_status", "use_debug_library", "PA_DEBUG_TABLE", "PA_DEBUG_SLOT", "PA_DEBUG_PAIR",
     "BlockManager",
     "DTYPE_CODES", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# the same library built with PA_DEBUG (device checks of slots, block ids, copy pairs)
+LIB_DEBUG_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa_debug.so")
 _LIB = None
+_LIB_DEBUG = None
+_USE_DEBUG = False
+
+PA_DEBUG_TABLE = 1
+PA_DEBUG_SLOT = 2
+PA_DEBUG_PAIR = 4
 
 PA_OK = 0
 PA_ERR_NO_BLOCKS = -4
@@ -37,6 +46,8 @@ _DECODE_ARGS = [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i64, _f3
 _SIGNATURES = {
     "pa_status_string": (_c.c_char_p, [_c.c_int]),
     "pa_version": (_c.c_int, []),
+    "pa_debug_status": (_c.c_int, [_vp]),
+    "pa_debug_enabled": (_c.c_int, []),
     "pa_cache_write": (_c.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (_c.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode": (_c.c_int, _DECODE_ARGS),
@@ -71,8 +82,8 @@ _SIGNATURES = {
     "pa_bm_blocks_needed": (_i64, [_vp, _vp, _i32]),
     "pa_prefill": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i64,
                               _f32, _i32, _i32, _vp, _vp]),
-    "pa_copy_blocks_between": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                          _vp]),
+    "pa_copy_blocks_between": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i32, _i32,
+                                          _i32, _i32, _vp]),
     "pa_bm_slots": (_c.c_int, [_vp, _i64, _i64, _i64, _vp]),
     "pa_bm_block_table": (_c.c_int, [_vp, _i64, _vp, _i32, _pi32]),
     "pa_bm_block_tables": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp]),
@@ -111,21 +122,48 @@ class PAError(RuntimeError):
         super().__init__(f"{where}: {msg} ({status})")
 
 
+def _load(path):
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_kv_cache_write_amd.build`")
+    import torch  # noqa: F401  (loads torch's libamdhip64 first)
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib():
-    """Load libpa.so (after torch, so that both use torch's HIP runtime)."""
-    global _LIB
+    """Load libpa.so (after torch, so that both use torch's HIP runtime), or
+    libpa_debug.so while use_debug_library(True) is in effect."""
+    global _LIB, _LIB_DEBUG
+    if _USE_DEBUG:
+        if _LIB_DEBUG is None:
+            _LIB_DEBUG = _load(LIB_DEBUG_PATH)
+        return _LIB_DEBUG
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_write_amd.build`")
-        import torch  # noqa: F401  (loads torch's libamdhip64 first)
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _LIB = handle
+        _LIB = _load(LIB_PATH)
     return _LIB
+
+
+def use_debug_library(on: bool = True) -> bool:
+    """Route the following calls to libpa_debug.so (on) or libpa.so (off);
+    returns the previous setting.  Objects keep the library they were made
+    with (a BlockManager holds its handle's library)."""
+    global _USE_DEBUG
+    prev, _USE_DEBUG = _USE_DEBUG, bool(on)
+    return prev
+
+
+def debug_status(stream=None) -> int:
+    """pa_debug_status: wait for the stream, return and clear the device error
+    bits (PA_DEBUG_* ; always 0 from the release library)."""
+    rc = lib().pa_debug_status(_stream(stream, None))
+    if rc < 0:
+        raise PAError(rc, "pa_debug_status")
+    return rc
 
 
 def _check(status: int, where: str):
@@ -250,7 +288,8 @@ def copy_blocks_between(src_k, src_v, dst_k, dst_v, block_pairs, stream=None):
         raise ValueError("block_pairs must be device or pinned host memory")
     dev = src_k.device if src_k.is_cuda else dst_k.device
     rc = lib().pa_copy_blocks_between(src_k.data_ptr(), src_v.data_ptr(), dst_k.data_ptr(),
-                                      dst_v.data_ptr(), block_pairs.data_ptr(), n, H, D, bs,
+                                      dst_v.data_ptr(), block_pairs.data_ptr(), n,
+                                      int(src_k.shape[0]), int(dst_k.shape[0]), H, D, bs,
                                       _dt(src_k), _stream(stream, dev))
     _check(rc, "pa_copy_blocks_between")
 
@@ -459,31 +498,33 @@ class BlockManager:
 
     def __init__(self, num_blocks: int, block_size: int, free_order=None):
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self._lib = lib()  # the library that owns the handle
         h = _vp()
         if free_order is None:
-            rc = lib().pa_bm_create(num_blocks, block_size, None, 0, _c.byref(h))
+            rc = self._lib.pa_bm_create(num_blocks, block_size, None, 0, _c.byref(h))
         else:
             fo = np.ascontiguousarray(free_order, dtype=np.int32)
-            rc = lib().pa_bm_create(num_blocks, block_size, _ptr(fo), fo.size, _c.byref(h))
+            rc = self._lib.pa_bm_create(num_blocks, block_size, _ptr(fo), fo.size, _c.byref(h))
         _check(rc, "pa_bm_create")
         self._h = h
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and _LIB is not None:
-            _LIB.pa_bm_destroy(h)
+        L = getattr(self, "_lib", None)
+        if h is not None and L is not None:
+            L.pa_bm_destroy(h)
             self._h = None
 
     def add_seq(self, seq: int, num_tokens: int):
-        _check(lib().pa_bm_add_seq(self._h, seq, num_tokens), "pa_bm_add_seq")
+        _check(self._lib.pa_bm_add_seq(self._h, seq, num_tokens), "pa_bm_add_seq")
 
     def fork(self, parent: int, child: int):
-        _check(lib().pa_bm_fork(self._h, parent, child), "pa_bm_fork")
+        _check(self._lib.pa_bm_fork(self._h, parent, child), "pa_bm_fork")
 
     def append_slot(self, seq: int):
         """Returns (slot, cow) with cow None or (src, dst)."""
         slot, src, dst = _c.c_int64(), _c.c_int32(), _c.c_int32()
-        rc = lib().pa_bm_append_slot(self._h, seq, _c.byref(slot), _c.byref(src), _c.byref(dst))
+        rc = self._lib.pa_bm_append_slot(self._h, seq, _c.byref(slot), _c.byref(src), _c.byref(dst))
         if rc < 0:
             _check(rc, "pa_bm_append_slot")
         return slot.value, ((src.value, dst.value) if rc == 1 else None)
@@ -495,7 +536,7 @@ class BlockManager:
         slots = np.empty(n, dtype=np.int64)
         cows = np.empty(2 * max(n, 1), dtype=np.int32)
         ncow, done = _c.c_int32(), _c.c_int32()
-        rc = lib().pa_bm_append_slots(self._h, _ptr(seqs), n, _ptr(slots), _ptr(cows),
+        rc = self._lib.pa_bm_append_slots(self._h, _ptr(seqs), n, _ptr(slots), _ptr(cows),
                                       _c.byref(ncow), _c.byref(done))
         _check(rc, "pa_bm_append_slots")
         return slots, cows[:2 * ncow.value].reshape(-1, 2).copy()
@@ -504,14 +545,14 @@ class BlockManager:
                   tables: np.ndarray, pad: int, context_lens: np.ndarray) -> int:
         """pa_bm_step into caller arrays (views of pinned memory); returns the CoW count."""
         ncow = _c.c_int32()
-        rc = lib().pa_bm_step(self._h, _ptr(seqs), seqs.size, _ptr(slots), _ptr(cows),
+        rc = self._lib.pa_bm_step(self._h, _ptr(seqs), seqs.size, _ptr(slots), _ptr(cows),
                               _c.byref(ncow), _ptr(tables), tables.shape[1], pad,
                               _ptr(context_lens))
         _check(rc, "pa_bm_step")
         return ncow.value
 
     def free_seq(self, seq: int):
-        _check(lib().pa_bm_free_seq(self._h, seq), "pa_bm_free_seq")
+        _check(self._lib.pa_bm_free_seq(self._h, seq), "pa_bm_free_seq")
 
     def select(self, pairs, retire):
         """Beam selection: fork child from parent for each (parent, child), then free
@@ -519,22 +560,22 @@ class BlockManager:
         pr = np.ascontiguousarray([p for p, _ in pairs], dtype=np.int64)
         ch = np.ascontiguousarray([c for _, c in pairs], dtype=np.int64)
         rt = np.ascontiguousarray(list(retire), dtype=np.int64)
-        _check(lib().pa_bm_select(self._h, _ptr(pr) if pr.size else None,
+        _check(self._lib.pa_bm_select(self._h, _ptr(pr) if pr.size else None,
                                   _ptr(ch) if ch.size else None, int(pr.size),
                                   _ptr(rt) if rt.size else None, int(rt.size)), "pa_bm_select")
 
     def slots(self, seq: int, start: int, n: int) -> np.ndarray:
         out = np.empty(n, dtype=np.int64)
-        _check(lib().pa_bm_slots(self._h, seq, start, n, _ptr(out)), "pa_bm_slots")
+        _check(self._lib.pa_bm_slots(self._h, seq, start, n, _ptr(out)), "pa_bm_slots")
         return out
 
     def block_table(self, seq: int) -> list:
         n = _c.c_int32()
-        rc = lib().pa_bm_block_table(self._h, seq, None, 0, _c.byref(n))
+        rc = self._lib.pa_bm_block_table(self._h, seq, None, 0, _c.byref(n))
         if rc not in (PA_OK, -8):
             _check(rc, "pa_bm_block_table")
         out = np.empty(n.value, dtype=np.int32)
-        _check(lib().pa_bm_block_table(self._h, seq, _ptr(out), n.value, _c.byref(n)),
+        _check(self._lib.pa_bm_block_table(self._h, seq, _ptr(out), n.value, _c.byref(n)),
                "pa_bm_block_table")
         return out.tolist()
 
@@ -542,34 +583,34 @@ class BlockManager:
         seqs = np.ascontiguousarray(seqs, dtype=np.int64)
         tables = np.empty((seqs.size, max_blocks), dtype=np.int32)
         ctx = np.empty(seqs.size, dtype=np.int32)
-        _check(lib().pa_bm_block_tables(self._h, _ptr(seqs), seqs.size, _ptr(tables), max_blocks,
+        _check(self._lib.pa_bm_block_tables(self._h, _ptr(seqs), seqs.size, _ptr(tables), max_blocks,
                                         pad, _ptr(ctx)), "pa_bm_block_tables")
         return tables, ctx
 
     def seq_len(self, seq: int) -> int:
-        n = lib().pa_bm_seq_len(self._h, seq)
+        n = self._lib.pa_bm_seq_len(self._h, seq)
         if n < 0:
             _check(int(n), "pa_bm_seq_len")
         return int(n)
 
     def refcount(self, block: int) -> int:
-        r = lib().pa_bm_refcount(self._h, block)
+        r = self._lib.pa_bm_refcount(self._h, block)
         if r < 0:
             _check(int(r), "pa_bm_refcount")
         return int(r)
 
     @property
     def num_free(self) -> int:
-        return int(lib().pa_bm_num_free(self._h))
+        return int(self._lib.pa_bm_num_free(self._h))
 
     @property
     def num_seqs(self) -> int:
-        return int(lib().pa_bm_num_seqs(self._h))
+        return int(self._lib.pa_bm_num_seqs(self._h))
 
     def free_list(self) -> list:
-        n = int(lib().pa_bm_free_list(self._h, None, 0))
+        n = int(self._lib.pa_bm_free_list(self._h, None, 0))
         out = np.empty(n, dtype=np.int32)
-        lib().pa_bm_free_list(self._h, _ptr(out), n)
+        self._lib.pa_bm_free_list(self._h, _ptr(out), n)
         return out.tolist()
 
     def refcounts(self) -> list:
@@ -579,10 +620,10 @@ class BlockManager:
     def set_host_pool(self, num_host_blocks: int, free_order=None):
         self.num_host_blocks = int(num_host_blocks)
         if free_order is None:
-            rc = lib().pa_bm_set_host_pool(self._h, num_host_blocks, None, 0)
+            rc = self._lib.pa_bm_set_host_pool(self._h, num_host_blocks, None, 0)
         else:
             fo = np.ascontiguousarray(free_order, dtype=np.int32)
-            rc = lib().pa_bm_set_host_pool(self._h, num_host_blocks, _ptr(fo), fo.size)
+            rc = self._lib.pa_bm_set_host_pool(self._h, num_host_blocks, _ptr(fo), fo.size)
         _check(rc, "pa_bm_set_host_pool")
 
     def _move(self, fn, seqs):
@@ -609,27 +650,27 @@ class BlockManager:
         return self._move("pa_bm_swap_in", seqs)
 
     def is_swapped(self, seq: int) -> bool:
-        rc = lib().pa_bm_is_swapped(self._h, seq)
+        rc = self._lib.pa_bm_is_swapped(self._h, seq)
         _check(min(rc, 0), "pa_bm_is_swapped")
         return rc == 1
 
     @property
     def num_free_host(self) -> int:
-        return int(lib().pa_bm_num_free_host(self._h))
+        return int(self._lib.pa_bm_num_free_host(self._h))
 
     def host_free_list(self) -> list:
-        n = int(lib().pa_bm_host_free_list(self._h, None, 0))
+        n = int(self._lib.pa_bm_host_free_list(self._h, None, 0))
         out = np.empty(n, dtype=np.int32)
-        lib().pa_bm_host_free_list(self._h, _ptr(out), n)
+        self._lib.pa_bm_host_free_list(self._h, _ptr(out), n)
         return out.tolist()
 
     def host_refcounts(self) -> list:
-        return [int(lib().pa_bm_host_refcount(self._h, b))
+        return [int(self._lib.pa_bm_host_refcount(self._h, b))
                 for b in range(getattr(self, "num_host_blocks", 0))]
 
     def blocks_needed(self, seqs) -> int:
         """Device blocks the next append of each of seqs would take (no change)."""
         arr = np.ascontiguousarray(seqs, dtype=np.int64)
-        n = int(lib().pa_bm_blocks_needed(self._h, _ptr(arr) if arr.size else None, arr.size))
+        n = int(self._lib.pa_bm_blocks_needed(self._h, _ptr(arr) if arr.size else None, arr.size))
         _check(min(n, 0), "pa_bm_blocks_needed")
         return n

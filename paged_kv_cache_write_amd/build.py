@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+# the same sources with PA_DEBUG: device checks of slots, block ids and copy pairs
+BUILD_DEBUG = os.path.join(ROOT, "_build_debug")
+LIB_DEBUG = os.path.join(PKG, "libpa_debug.so")
 
 SOURCES = ["decode.hip", "prefill.hip", "cache_ops.hip", "measure.hip", "block_manager.cpp",
            "capi.cpp", "engine.cpp"]
@@ -41,10 +44,10 @@ def _device_flags():
             "-packed-fp32-ops"]
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), "-c", path, "-o", obj] + _common()
+    obj = os.path.join(BUILD_DEBUG if debug else BUILD, src + ".o")
+    cmd = [hipcc(), "-c", path, "-o", obj] + _common() + (["-DPA_DEBUG"] if debug else [])
     if src.endswith(".hip"):
         cmd += ["-x", "hip"] + _device_flags()
     if verbose:
@@ -59,20 +62,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libpa.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def _build_one(verbose: bool, debug: bool) -> str:
+    os.makedirs(BUILD_DEBUG if debug else BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, debug), SOURCES))
+    lib = LIB_DEBUG if debug else LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libpa.so and libpa_debug.so; returns the
+    path of libpa.so."""
+    _build_one(verbose, debug=True)
+    return _build_one(verbose, debug=False)
 
 
 if __name__ == "__main__":

@@ -21,7 +21,7 @@ constexpr int kCwThreads = 256;
 __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
     const char* __restrict__ k, const char* __restrict__ v, const int64_t* __restrict__ slots,
     char* __restrict__ k_cache, char* __restrict__ v_cache, int64_t total_vecs, int H,
-    int vecs_per_row, int row_bytes, int log2_bs) {
+    int vecs_per_row, int row_bytes, int log2_bs, int64_t num_slots) {
   const int64_t g = int64_t(blockIdx.x) * kCwThreads + threadIdx.x;
   if (g >= total_vecs) return;
   const int64_t row = g / vecs_per_row;  // n * H + h
@@ -30,6 +30,7 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
   const int h = int(row - n * H);
   const int64_t slot = slots[n];
   if (slot < 0) return;
+  if (debug_bad(slot, num_slots, PA_DEBUG_SLOT)) return;
   const int64_t blk = slot >> log2_bs;
   const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
   const int64_t dst = ((((blk * H + h) << log2_bs) + off) * row_bytes) + int64_t(col) * 16;
@@ -43,9 +44,10 @@ __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
 // different (swapping between the device pool and a host pool).
 __global__ __launch_bounds__(kCwThreads) void copy_blocks_kernel(
     const char* src_k, const char* src_v, char* dst_k, char* dst_v,
-    const int32_t* __restrict__ pairs, int64_t tile_vecs) {
+    const int32_t* __restrict__ pairs, int64_t tile_vecs, int64_t src_blocks, int64_t dst_blocks) {
   const int pair = blockIdx.y;
   const int64_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if (debug_bad(src, src_blocks, PA_DEBUG_PAIR) | debug_bad(dst, dst_blocks, PA_DEBUG_PAIR)) return;
   const u32x4* ks = reinterpret_cast<const u32x4*>(src_k) + src * tile_vecs;
   const u32x4* vs = reinterpret_cast<const u32x4*>(src_v) + src * tile_vecs;
   u32x4* kd = reinterpret_cast<u32x4*>(dst_k) + dst * tile_vecs;
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kCwThreads) void step_prologue_kernel(
     const u32x4* __restrict__ host_src, u32x4* __restrict__ dev_dst, int64_t copy_vecs,
     int copy_wgs, const int64_t* __restrict__ host_slots, const char* __restrict__ k,
     const char* __restrict__ v, char* __restrict__ k_cache, char* __restrict__ v_cache, int H,
-    int vecs_per_row, int row_bytes, int log2_bs) {
+    int vecs_per_row, int row_bytes, int log2_bs, int64_t num_slots) {
   if (int(blockIdx.x) < copy_wgs) {
     const int64_t i0 = int64_t(blockIdx.x) * kCwThreads * kPrologueVecs + threadIdx.x;
     u32x4 x[kPrologueVecs];
@@ -99,6 +101,7 @@ __global__ __launch_bounds__(kCwThreads) void step_prologue_kernel(
       vx[j] = *reinterpret_cast<const u32x4*>(v + src);
     }
     if (slot < 0) return;  // a padding token
+    if (debug_bad(slot, num_slots, PA_DEBUG_SLOT)) return;
     const int64_t blk = slot >> log2_bs;
     const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
 #pragma unroll
@@ -116,8 +119,9 @@ __global__ __launch_bounds__(kCwThreads) void step_prologue_kernel(
 
 int launch_step_prologue(const void* host_src, void* dev_dst, size_t copy_bytes,
                          const int64_t* host_slots, const void* k, const void* v, int64_t n,
-                         void* k_cache, void* v_cache, int32_t num_heads, int32_t head_dim,
-                         int32_t block_size, int32_t dtype, hipStream_t stream) {
+                         void* k_cache, void* v_cache, int64_t num_blocks, int32_t num_heads,
+                         int32_t head_dim, int32_t block_size, int32_t dtype,
+                         hipStream_t stream) {
   int rc = check_shape(head_dim, block_size, dtype);
   if (rc != PA_OK) return rc;
   if (copy_bytes % 16 || !aligned16(host_src) || !aligned16(dev_dst) || n < 0 || n > 65535)
@@ -136,10 +140,14 @@ int launch_step_prologue(const void* host_src, void* dev_dst, size_t copy_bytes,
                      copy_vecs, copy_wgs, host_slots, static_cast<const char*>(k),
                      static_cast<const char*>(v), static_cast<char*>(k_cache),
                      static_cast<char*>(v_cache), num_heads, row_bytes / 16, row_bytes,
-                     log2_exact(block_size));
+                     log2_exact(block_size), num_blocks * block_size);
   return launch_status();
 }
 
+}  // namespace pa
+
+namespace pa {
+uint32_t debug_take_cache_ops() { return debug_take_word(); }
 }  // namespace pa
 
 extern "C" {
@@ -164,7 +172,7 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, in
                      reinterpret_cast<hipStream_t>(stream), static_cast<const char*>(k),
                      static_cast<const char*>(v), slot_mapping, static_cast<char*>(k_cache),
                      static_cast<char*>(v_cache), total, num_heads, vecs_per_row, row_bytes,
-                     pa::log2_exact(block_size));
+                     pa::log2_exact(block_size), num_blocks * block_size);
   return pa::launch_status();
 }
 
@@ -187,16 +195,18 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int
                      dim3(pa::kCwThreads), 0, reinterpret_cast<hipStream_t>(stream),
                      static_cast<const char*>(k_cache), static_cast<const char*>(v_cache),
                      static_cast<char*>(k_cache), static_cast<char*>(v_cache), block_pairs,
-                     tile_vecs);
+                     tile_vecs, num_blocks, num_blocks);
   return pa::launch_status();
 }
 
 int pa_copy_blocks_between(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
-                           const int32_t* block_pairs, int32_t num_pairs, int32_t num_heads,
-                           int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+                           const int32_t* block_pairs, int32_t num_pairs, int64_t src_blocks,
+                           int64_t dst_blocks, int32_t num_heads, int32_t head_dim,
+                           int32_t block_size, int32_t dtype, void* stream) {
   int rc = pa::check_shape(head_dim, block_size, dtype);
   if (rc != PA_OK) return rc;
-  if (num_pairs < 0 || num_heads <= 0) return PA_ERR_INVALID;
+  if (num_pairs < 0 || num_heads <= 0 || src_blocks <= 0 || dst_blocks <= 0)
+    return PA_ERR_INVALID;
   if (num_pairs == 0) return PA_OK;
   if (num_pairs > 65535) return PA_ERR_UNSUPPORTED;
   if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs) return PA_ERR_INVALID;
@@ -212,7 +222,7 @@ int pa_copy_blocks_between(const void* src_k, const void* src_v, void* dst_k, vo
                      dim3(pa::kCwThreads), 0, reinterpret_cast<hipStream_t>(stream),
                      static_cast<const char*>(src_k), static_cast<const char*>(src_v),
                      static_cast<char*>(dst_k), static_cast<char*>(dst_v), block_pairs,
-                     tile_vecs);
+                     tile_vecs, src_blocks, dst_blocks);
   return pa::launch_status();
 }
 

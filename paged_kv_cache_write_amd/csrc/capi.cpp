@@ -1,4 +1,7 @@
-// Status strings and version of the C ABI.
+// Status strings, version and debug status of the C ABI.
+#include <hip/hip_runtime_api.h>
+
+#include "internal.hpp"
 #include "pa.h"
 
 extern "C" {
@@ -19,5 +22,20 @@ const char* pa_status_string(int status) {
 }
 
 int pa_version(void) { return 100; }
+
+int pa_debug_status(void* stream) {
+  if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_HIP;
+  const uint32_t w = pa::debug_take_decode() | pa::debug_take_prefill() | pa::debug_take_cache_ops();
+  if (w == ~0u) return PA_ERR_HIP;  // a symbol copy failed
+  return int(w & (PA_DEBUG_TABLE | PA_DEBUG_SLOT | PA_DEBUG_PAIR));
+}
+
+int pa_debug_enabled(void) {
+#ifdef PA_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
 
 }  // extern "C"

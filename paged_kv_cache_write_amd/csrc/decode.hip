@@ -98,6 +98,7 @@ struct DecodeParams {
   // s * stride_s + t * stride_t + h * stride_h; max_tokens bounds t
   bool contig;
   int64_t stride_s, stride_t, stride_h, max_tokens;
+  int64_t num_blocks;  // pool size (checked against table entries in debug builds)
 };
 
 template <class DT, int D, int U>
@@ -453,8 +454,15 @@ __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h
   // its length: entries past the partition are loaded as integers but never
   // used as addresses.
   int tbl = 0;
-  if (lane < (P.window_tokens >> P.log2_bs) && blk0 + lane < P.maxB)
+  if (lane < (P.window_tokens >> P.log2_bs) && blk0 + lane < P.maxB) {
     tbl = P.block_tables[size_t(s) * P.maxB + blk0 + lane];
+#ifdef PA_DEBUG
+    // entries of blocks inside the context are addresses; the rest are never used
+    if (((blk0 + lane) << P.log2_bs) < P.context_lens[s] &&
+        debug_bad(tbl, P.num_blocks, PA_DEBUG_TABLE))
+      tbl = 0;
+#endif
+  }
   cx.kc = reinterpret_cast<const char*>(P.k_cache);
   cx.vc = reinterpret_cast<const char*>(P.v_cache);
   cx.log2_tile = kLog2Row + P.log2_bs;
@@ -711,8 +719,10 @@ __global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParam
   const int log2_tile = kLog2Row + log2_bs;
   const int blk0 = t0 >> log2_bs;
   int tbl = 0;
-  if (lane < (kSharedPartTokens >> log2_bs) && blk0 + lane < P.maxB)
+  if (lane < (kSharedPartTokens >> log2_bs) && blk0 + lane < P.maxB) {
     tbl = P.block_tables[size_t(mem[0]) * P.maxB + blk0 + lane];
+    if (debug_bad(tbl, P.num_blocks, PA_DEBUG_TABLE)) tbl = 0;  // every entry is used
+  }
 
   u32x4 qv[NK];
 #pragma unroll
@@ -1057,6 +1067,7 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.stride_t = cg.stride_t;
   p.stride_h = cg.stride_h;
   p.max_tokens = cg.max_tokens;
+  p.num_blocks = NB;
   if (shared && !p.counters) return PA_ERR_INVALID;  // groups need the one-launch merge
   if (shared && cg.on) return PA_ERR_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -1216,6 +1227,10 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
   return PA_OK;
 }
 
+}  // namespace pa
+
+namespace pa {
+uint32_t debug_take_decode() { return debug_take_word(); }
 }  // namespace pa
 
 extern "C" {

@@ -215,8 +215,8 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
   if (fused) {
     char* hd = e->host_dev + size_t(slot) * e->slot_bytes;
     rc = pa::launch_step_prologue(hd, d, used, reinterpret_cast<const int64_t*>(hd + off_slots),
-                                  k_new, v_new, n, e->k_cache, e->v_cache, e->H, e->D, e->bs,
-                                  e->dtype, st);
+                                  k_new, v_new, n, e->k_cache, e->v_cache, e->num_blocks, e->H,
+                                  e->D, e->bs, e->dtype, st);
     if (rc != PA_OK) return rc;
   } else if (hipMemcpyAsync(d, h, used, hipMemcpyHostToDevice, st) != hipSuccess) {
     return PA_ERR_HIP;

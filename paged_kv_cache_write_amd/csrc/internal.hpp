@@ -34,7 +34,15 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
 // read from the host staging `host_slots`.  Returns a pa_status.
 int launch_step_prologue(const void* host_src, void* dev_dst, size_t copy_bytes,
                          const int64_t* host_slots, const void* k, const void* v, int64_t n,
-                         void* k_cache, void* v_cache, int32_t num_heads, int32_t head_dim,
-                         int32_t block_size, int32_t dtype, hipStream_t stream);
+                         void* k_cache, void* v_cache, int64_t num_blocks, int32_t num_heads,
+                         int32_t head_dim, int32_t block_size, int32_t dtype,
+                         hipStream_t stream);
+
+// Device error words of the translation units with kernels (debug builds:
+// table entries, slots and copy pairs out of range; release builds: 0), each
+// read and cleared.  Synchronous.
+uint32_t debug_take_decode();
+uint32_t debug_take_prefill();
+uint32_t debug_take_cache_ops();
 
 }  // namespace pa

@@ -170,4 +170,28 @@ __device__ __forceinline__ uint32_t pack_store(BF16, float a, float b) {
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Debug builds (PA_DEBUG): a kernel checks every table entry, slot and copy
+// pair before it becomes an address.  A value outside [0, n) sets `bit` in
+// this translation unit's device error word (read and cleared by
+// pa_debug_status) and is reported as invalid, so the caller substitutes an
+// in-bounds block or skips the write.  Release builds check nothing.
+#ifdef PA_DEBUG
+static __device__ uint32_t pa_debug_word;
+__device__ __forceinline__ bool debug_bad(int64_t v, int64_t n, uint32_t bit) {
+  if (v >= 0 && v < n) return false;
+  atomicOr(&pa_debug_word, bit);
+  return true;
+}
+// The error word of this translation unit, then cleared (host; synchronous).
+static inline uint32_t debug_take_word() {
+  uint32_t w = 0, zero = 0;
+  if (hipMemcpyFromSymbol(&w, HIP_SYMBOL(pa_debug_word), sizeof(w)) != hipSuccess) return ~0u;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(pa_debug_word), &zero, sizeof(zero)) != hipSuccess) return ~0u;
+  return w;
+}
+#else
+__device__ __forceinline__ bool debug_bad(int64_t, int64_t, uint32_t) { return false; }
+static inline uint32_t debug_take_word() { return 0; }
+#endif
+
 }  // namespace pa

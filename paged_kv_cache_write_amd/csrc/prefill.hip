@@ -54,6 +54,7 @@ struct PrefillParams {
   int S;
   int num_tiles;  // query tiles per sequence (of the longest chunk)
   int maxB;
+  int64_t num_blocks;  // pool size (checked against table entries in debug builds)
   int log2_bs;
   float qk_scale;  // scale * log2(e)
 };
@@ -208,6 +209,7 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void prefill_mfma_kernel(
       const int r0 = c * kRowsPerGroup + wave * (kWave / (D / 8));  // first row of the wave
       const int t = wave_uniform(min(base + r0, last));
       ids.b[c] = trow_c[t >> log2_bs];
+      if (debug_bad(ids.b[c], P.num_blocks, PA_DEBUG_TABLE)) ids.b[c] = 0;  // t is in the context
     }
   };
   struct Regs { u32x4 k[kPerThread], v[kPerThread]; };
@@ -403,6 +405,10 @@ void launch_prefill(const PrefillParams& p, int S, int max_q_len, hipStream_t st
 
 }  // namespace pa
 
+namespace pa {
+uint32_t debug_take_prefill() { return debug_take_word(); }
+}  // namespace pa
+
 extern "C" {
 
 int pa_prefill(const void* q, const void* k_cache, const void* v_cache,
@@ -438,6 +444,7 @@ int pa_prefill(const void* q, const void* k_cache, const void* v_cache,
   if (int64_t(p.num_tiles) * ((int64_t(num_seqs) * num_heads + 7) / 8) * 8 * 256 > 0xFFFFFFFFll)
     return PA_ERR_UNSUPPORTED;
   p.maxB = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
   p.log2_bs = pa::log2_exact(block_size);
   p.qk_scale = scale * pa::kPfLog2e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

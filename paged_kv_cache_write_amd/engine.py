@@ -52,7 +52,7 @@ class PagedKVEngine:
             self.k_cache = torch.full(shape, fill, dtype=dtype, device=self.device)
             self.v_cache = torch.full(shape, fill, dtype=dtype, device=self.device)
         self.bm = BlockManager(self.NB, self.bs, free_order)
-        L = lib()
+        L = self._lib = lib()  # the library that owns the handle
         slot = int(L.pa_engine_staging_bytes(self.max_batch, self.maxB, self.bs))
         self._host = torch.empty(slot * self.RING, dtype=torch.uint8, pin_memory=True)
         self._dev = torch.empty(slot, dtype=torch.uint8, device=self.device)
@@ -159,7 +159,7 @@ class PagedKVEngine:
         if out is None:
             out = torch.empty_like(q)
         st = (torch.cuda.current_stream(self.device) if stream is None else stream).cuda_stream
-        rc = lib().pa_engine_step(self._e, _ptr(arr), S, q.data_ptr(), k_new.data_ptr(),
+        rc = self._lib.pa_engine_step(self._e, _ptr(arr), S, q.data_ptr(), k_new.data_ptr(),
                                   v_new.data_ptr(), float(scale), out.data_ptr(),
                                   self.workspace.data_ptr(), self.workspace.numel(),
                                   self.partition_tokens, st, ctypes.byref(self._info))
@@ -169,19 +169,20 @@ class PagedKVEngine:
 
     def set_sharing(self, enable: bool):
         """Shared-prefix groups in later steps (on by default)."""
-        _check(lib().pa_engine_set_sharing(self._e, 1 if enable else 0), "pa_engine_set_sharing")
+        _check(self._lib.pa_engine_set_sharing(self._e, 1 if enable else 0),
+               "pa_engine_set_sharing")
 
     def set_decode_events(self, start=None, end=None):
         """Record torch.cuda.Event ``start``/``end`` around the decode launch of the
         following steps (None = stop)."""
         if start is None or end is None:
-            _check(lib().pa_engine_set_decode_events(self._e, None, None), "set events")
+            _check(self._lib.pa_engine_set_decode_events(self._e, None, None), "set events")
             return
         stream = self.torch.cuda.current_stream(self.device)
         for ev in (start, end):
             if ev.cuda_event == 0:     # torch creates the HIP event on first record
                 ev.record(stream)
-        _check(lib().pa_engine_set_decode_events(self._e, start.cuda_event, end.cuda_event),
+        _check(self._lib.pa_engine_set_decode_events(self._e, start.cuda_event, end.cuda_event),
                "pa_engine_set_decode_events")
 
     @property
@@ -192,7 +193,7 @@ class PagedKVEngine:
         slots = np.empty(S, dtype=np.int64)
         ctx = np.empty(S, dtype=np.int32)
         cows = np.empty((max(info.num_cow, 1), 2), dtype=np.int32)
-        _check(lib().pa_engine_last_step(self._e, S, _ptr(slots), _ptr(ctx), _ptr(cows),
+        _check(self._lib.pa_engine_last_step(self._e, S, _ptr(slots), _ptr(ctx), _ptr(cows),
                                          info.num_cow), "pa_engine_last_step")
         return dict(ctx=ctx, slots=slots, cows=cows[:info.num_cow], num_cow=info.num_cow,
                     max_ctx=info.max_context_len, partition_tokens=info.partition_tokens,

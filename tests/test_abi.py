@@ -33,6 +33,22 @@ def test_library_exports_every_declared_symbol():
     assert lib.pa_version() >= 100
 
 
+def test_debug_library_exports_the_same_symbols():
+    """libpa_debug.so (PA_DEBUG: device checks of slots, block ids and copy pairs)
+    exports the same ABI and says it is the debug build; libpa.so says it is not."""
+    import paged_kv_cache_write_amd as pk
+    raw = ctypes.CDLL(pk.LIB_DEBUG_PATH)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, missing
+    assert pk.lib().pa_debug_enabled() == 0
+    prev = pk.use_debug_library(True)
+    try:
+        assert pk.lib().pa_debug_enabled() == 1
+    finally:
+        pk.use_debug_library(prev)
+    assert pk.lib().pa_debug_enabled() == 0
+
+
 def test_status_strings():
     import paged_kv_cache_write_amd as pk
     lib = pk.lib()
