@@ -322,7 +322,9 @@ int pa_bm_block_table(const pa_bm* bm, int64_t seq, int32_t* out, int32_t cap,
 int64_t pa_bm_seq_len(const pa_bm* bm, int64_t seq) {
   if (!bm) return PA_ERR_INVALID;
   auto it = bm->seqs.find(seq);
-  return it == bm->seqs.end() ? int64_t(PA_ERR_NOT_FOUND) : it->second.len;
+  if (it != bm->seqs.end()) return it->second.len;
+  it = bm->swapped.find(seq);  // a swapped-out sequence keeps its length
+  return it == bm->swapped.end() ? int64_t(PA_ERR_NOT_FOUND) : it->second.len;
 }
 
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {

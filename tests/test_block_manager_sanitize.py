@@ -1,0 +1,36 @@
+"""The host block manager under AddressSanitizer and UndefinedBehaviorSanitizer
+(CPU only): tests/bm_sanitize_driver.cpp runs a seeded random workload through
+every pa_bm_* call (successes and failures) and checks the pool's invariants
+after each operation; any memory error, leak or undefined behaviour aborts it."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+
+def test_block_manager_under_sanitizers(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "bm_sanitize")
+    src = [os.path.join(ROOT, "tests", "bm_sanitize_driver.cpp"),
+           os.path.join(ROOT, "paged_kv_cache_write_amd", "csrc", "block_manager.cpp")]
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"), *src, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    env.pop("LD_PRELOAD", None)
+    r = subprocess.run([exe, "6000"], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
+    assert r.stdout.startswith("ok 6000")
+    counts = dict(line.split() for line in r.stdout.splitlines()[1:])
+    for outcome in ("add", "add_full", "fork", "append", "append_cow", "append_full", "free",
+                    "free_swapped", "select", "swap_out", "swap_out_refused", "swap_in", "step",
+                    "step_full"):
+        assert int(counts.get(outcome, 0)) > 0, (outcome, counts)
