@@ -223,6 +223,22 @@ def prefill_measure(torch, pk, per_call, dtype, seqs=8, prompt=1024, H=40, D=128
             "timing": "20 back-to-back calls between one pair of events"}
 
 
+def block_manager_stats(eng, seqs, tables, wl):
+    """Memory figures of the pool after the timed steps: useful KV fraction
+    sum(ctx) / (sum(ceil(ctx/bs)) * bs) (the waste is only each sequence's
+    last block), physical blocks in use, and the saving of shared blocks
+    1 - distinct / sum(ceil(ctx/bs))."""
+    lens = np.array([eng.bm.seq_len(int(x)) for x in seqs], dtype=np.int64)
+    nblk = -(-lens // wl.bs)
+    ids = np.concatenate([tables[i, :n] for i, n in enumerate(nblk)]) if len(nblk) else []
+    distinct = int(np.unique(ids).size)
+    logical = int(nblk.sum())
+    return {"useful_kv_fraction": round(float(lens.sum()) / max(logical * wl.bs, 1), 4),
+            "blocks_in_use": distinct, "pool_blocks": int(eng.NB),
+            "logical_blocks": logical,
+            "sharing_saving": round(1.0 - distinct / max(logical, 1), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +354,7 @@ def main():
     uniq_bytes = [b - decode_bytes(c, wl.H, wl.D, elem, wl.bs)[1] +
                   unique_kv_bytes(tables, c, wl.H, wl.D, elem, wl.bs)
                   for b, c in zip(dec_bytes, ctxs2)]
+    bm_stats = block_manager_stats(eng, seqs, tables, wl)
     elapsed = t1 - t0
     ms_per_step = elapsed / args.steps * 1e3
     kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
@@ -500,6 +517,7 @@ def main():
         sec["swap_in_gbps"] = round(nswap * blk / si / 1e9, 2)
     sec["swap_blocks"] = nswap
     res["secondary"] = sec
+    res["block_manager"] = bm_stats
 
     if args.contiguous:
         res["contiguous"] = contiguous_compare(eng, seqs, q, wl, torch, pk, per_call)
