@@ -173,16 +173,21 @@ class PagedKVEngine:
                "pa_engine_set_sharing")
 
     def set_decode_events(self, start=None, end=None):
-        """Record torch.cuda.Event ``start``/``end`` around the decode launch of the
-        following steps (None = stop)."""
+        """Record ``start``/``end`` around the decode launch of the following steps
+        (None = stop): torch.cuda.Event objects, or raw hipEvent_t handles (int)."""
         if start is None or end is None:
             _check(self._lib.pa_engine_set_decode_events(self._e, None, None), "set events")
             return
         stream = self.torch.cuda.current_stream(self.device)
+        handles = []
         for ev in (start, end):
+            if isinstance(ev, int):
+                handles.append(ev)
+                continue
             if ev.cuda_event == 0:     # torch creates the HIP event on first record
                 ev.record(stream)
-        _check(self._lib.pa_engine_set_decode_events(self._e, start.cuda_event, end.cuda_event),
+            handles.append(ev.cuda_event)
+        _check(self._lib.pa_engine_set_decode_events(self._e, handles[0], handles[1]),
                "pa_engine_set_decode_events")
 
     @property
