@@ -99,6 +99,8 @@ struct DecodeParams {
   bool contig;
   int64_t stride_s, stride_t, stride_h, max_tokens;
   int64_t num_blocks;  // pool size (checked against table entries in debug builds)
+  int64_t ws_o_bytes;  // bytes of the ws_o region
+  int num_group_wgs;   // decode_shared_kernel: workgroups of the group items
 };
 
 template <class DT, int D, int U>
@@ -484,7 +486,7 @@ __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h
 // One wave per (sequence, head, partition): grid order from context_lens, or
 // a host-scheduled work list of single items.
 template <class DT, int D, int U, bool kContig = false>
-__global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
+__device__ __forceinline__ void wave_body(DecodeParams P, uint3 block) {
   using T = typename DT::T;
   using Sh = Shape<DT, D, U>;
   constexpr int kVec = DT::kVec;
@@ -497,16 +499,16 @@ __global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
   int hg, part, s, t0;
   const int32_t* it = nullptr;
   if (P.items != nullptr) {  // scheduled launch: x = item * head_groups + head group
-    const int item = blockIdx.x / ngroups;
-    hg = blockIdx.x - item * ngroups;
+    const int item = block.x / ngroups;
+    hg = block.x - item * ngroups;
     it = P.items + kItemInts * item;
     s = it[0];
     part = it[1];
     t0 = it[2];
   } else {
-    hg = blockIdx.x;
-    part = blockIdx.y;
-    s = blockIdx.z;
+    hg = block.x;
+    part = block.y;
+    s = block.z;
     t0 = part * P.part_tokens;
   }
   const int h = hg * kWaves + wave;
@@ -593,6 +595,11 @@ __global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
   const size_t rows[1] = {row_id};
   const int nps[1] = {nparts};
   finish<DT, D, U, 1>(P, rows, nps, 1, part, m, l, acc, lane);
+}
+
+template <class DT, int D, int U, bool kContig = false>
+__global__ __launch_bounds__(kThreads) void decode_wave_kernel(DecodeParams P) {
+  wave_body<DT, D, U, kContig>(P, uint3{blockIdx.x, blockIdx.y, blockIdx.z});
 }
 
 // One wave per (group of sequences sharing a prefix, head, shared partition):
@@ -684,7 +691,7 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeParams P) 
 // 32 tokens (two 16-token tiles); the next step's loads are in flight while
 // one is computed.
 template <class DT, int D>
-__global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParams P) {
+__device__ __forceinline__ void group_mfma_body(DecodeParams P, unsigned block_x) {
   using T = typename DT::T;
   constexpr int NK = D / 32;  // q.K products per tile (32 d each)
   constexpr int NJ = D / 16;  // P.V products per step (16 d each) = V elements per row load
@@ -695,8 +702,8 @@ __global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParam
 
   const int lane = threadIdx.x;
   const int H = P.H;
-  const int item = blockIdx.x / H;
-  const int h = blockIdx.x - item * H;
+  const int item = int(block_x) / H;
+  const int h = int(block_x) - item * H;
   const int32_t* it = P.group_items + kItemInts * item;
   const int moff = it[0];
   const int nq = min(int(it[1]), kGroupMfma);
@@ -857,24 +864,88 @@ __global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParam
       *reinterpret_cast<VRow*>(out + NJ * (4 * g + r)) = w;
     }
   }
-  // Partials: the schedule keeps every member's last partition in the
-  // single-item launch that follows on the same stream, so no group wave is
-  // the last of its row; the partials are plain stores, made visible to the
-  // next launch by the kernel boundary, and only the row counter is counted.
+  // Partials, in the merge's layout (element d at part_pos(d)) and with
+  // agent-scope stores, so that they are visible on every XCD while the
+  // single items of the same rows may still run (in the same launch order
+  // or concurrently on another stream).  For D = 128, lane (qi, g) holds
+  // d = 8 (4 g + r) + jd, i.e. positions 16 jd + 4 g + r: one 16-byte store
+  // per jd (64 contiguous bytes per member and store instruction); for D = 64
+  // the same lane's values pair into 8-byte stores.  Then each member's row
+  // is counted, and the wave that completes a row merges it.
   if (has_q && split) {
     const size_t pi = row_q * P.max_parts + part;
-    float* po = P.ws_o + pi * D;
+    if (P.ws_o_bytes < (int64_t(1) << 31)) {  // 32-bit buffer offsets
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(P.ws_o, 0, int(P.ws_o_bytes), 0x00020000);
+      const uint32_t base = uint32_t(pi * D * sizeof(float));
+      constexpr int kAgent = 0x10;  // sc1: agent-scope coherent store
+      if constexpr (D == 128) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+        for (int jd = 0; jd < NJ; ++jd) {
+          const u32x4 w = {float_bits(o[jd][0] * inv), float_bits(o[jd][1] * inv),
+                           float_bits(o[jd][2] * inv), float_bits(o[jd][3] * inv)};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rsrc, base + (16 * jd + 4 * g) * 4, 0, kAgent);
+        }
+      } else {
 #pragma unroll
-      for (int jd = 0; jd < NJ; ++jd) po[part_pos<DT, D>(NJ * (4 * g + r) + jd)] = o[jd][r] * inv;
+        for (int jd = 0; jd < NJ; ++jd)
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {  // (r, r + 2) are adjacent positions
+            const u32x2 w = {float_bits(o[jd][r] * inv), float_bits(o[jd][r + 2] * inv)};
+            const int pos = part_pos<DT, D>(NJ * (4 * g + r) + jd);
+            __builtin_amdgcn_raw_buffer_store_b64(w, rsrc, base + pos * 4, 0, kAgent);
+          }
+      }
+    } else {
+      float* po = P.ws_o + pi * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jd = 0; jd < NJ; ++jd)
+          __hip_atomic_store(po + part_pos<DT, D>(NJ * (4 * g + r) + jd), o[jd][r] * inv,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (g == 0) {
-      P.ws_ml[2 * pi] = m;
-      P.ws_ml[2 * pi + 1] = l;
-      if (P.counters)
-        __hip_atomic_fetch_add(P.counters + row_q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.ws_ml + 2 * pi, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.ws_ml + 2 * pi + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  if (!P.counters) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // all counters zero: this wave's stores are complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int last = 0;
+  if (g == 0 && has_q && split) {
+    const int prev = __hip_atomic_fetch_add(P.counters + row_q, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == nparts_q - 1 ? 1 : 0;
+  }
+  for (int k = 0; k < nq; ++k) {  // members whose row this wave completed
+    if (!__shfl(last, k, kWave)) continue;  // wave-uniform
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const size_t row_k = size_t(mem[kMemberInts * k]) * H + h;
+    if (lane == 0)  // every partition of this row has counted: reset for the next call
+      __hip_atomic_store(P.counters + row_k, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_partials<DT, D, kUnroll>(P, row_k, mem[kMemberInts * k + 1], lane);
+  }
+}
+
+template <class DT, int D>
+__global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParams P) {
+  group_mfma_body<DT, D>(P, blockIdx.x);
+}
+
+// Shared-prefix decode in one launch (16-bit storage): workgroups
+// [0, num_group_wgs) run the group items, the rest the single items.  Every
+// wave stores its partials with agent-scope stores and counts its rows, and
+// the wave that completes a row merges it, so the two kinds may finish in
+// any order; the group waves' streaming overlaps the short single waves.
+template <class DT, int D>
+__global__ __launch_bounds__(kWave, 2) void decode_shared_kernel(DecodeParams P) {
+  if (blockIdx.x < unsigned(P.num_group_wgs))
+    group_mfma_body<DT, D>(P, blockIdx.x);
+  else
+    wave_body<DT, D, kUnroll>(P, uint3{blockIdx.x - unsigned(P.num_group_wgs), 0u, 0u});
 }
 
 // Second launch of the two-launch form: one wave per (sequence, head) row.
@@ -950,7 +1021,7 @@ static int make_plan(int32_t S, int32_t H, int32_t D, int32_t bs, int32_t max_ct
   return PA_OK;
 }
 
-enum class Launch { kSingles, kGroups, kReduce };
+enum class Launch { kSingles, kGroups, kShared, kReduce };
 
 template <class DT, int D>
 static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t st) {
@@ -974,6 +1045,12 @@ static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t
         hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
       break;
     }
+    case Launch::kShared:  // group and single items in one launch (16-bit storage only)
+      if constexpr (!std::is_same<DT, F32>::value)
+        hipLaunchKernelGGL((decode_shared_kernel<DT, D>),
+                           dim3(unsigned(p.num_group_wgs) + unsigned(n) * unsigned(ngroups)),
+                           dim3(kWave), 0, st, p);
+      break;
     case Launch::kReduce:
       hipLaunchKernelGGL((decode_reduce_kernel<DT, D, kUnroll>), dim3(p.H, S), dim3(kWave), 0,
                          st, p);
@@ -1068,20 +1145,30 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.stride_h = cg.stride_h;
   p.max_tokens = cg.max_tokens;
   p.num_blocks = NB;
+  p.ws_o_bytes = split ? int64_t(S) * H * plan.max_parts * D * int64_t(sizeof(float)) : 0;
+  p.num_group_wgs = 0;
   if (shared && !p.counters) return PA_ERR_INVALID;  // groups need the one-launch merge
   if (shared && cg.on) return PA_ERR_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (what & kDoPartitions) {
-    if (shared) {
-      DecodeParams pg = p;
-      pg.window_tokens = kSharedPartTokens;
-      dispatch(Launch::kGroups, dtype, D, pg, S, sched.num_group_items, st);
-    }
-    if (!sched.scheduled) {
-      dispatch(Launch::kSingles, dtype, D, p, S, 0, st);
-    } else if (sched.num_items > 0 && sched.items) {
-      dispatch(Launch::kSingles, dtype, D, p, S, sched.num_items, st);
+    if (shared && dtype != PA_F32) {
+      // one launch: group waves stream the shared tiles while the single
+      // waves (short private tails) run beside them
+      static_assert(kThreads == kWave, "the fused launch has one wave per workgroup");
+      p.num_group_wgs = sched.num_group_items * H;
+      dispatch(Launch::kShared, dtype, D, p, S, sched.items ? sched.num_items : 0, st);
+    } else {
+      if (shared) {
+        DecodeParams pg = p;
+        pg.window_tokens = kSharedPartTokens;
+        dispatch(Launch::kGroups, dtype, D, pg, S, sched.num_group_items, st);
+      }
+      if (!sched.scheduled) {
+        dispatch(Launch::kSingles, dtype, D, p, S, 0, st);
+      } else if (sched.num_items > 0 && sched.items) {
+        dispatch(Launch::kSingles, dtype, D, p, S, sched.num_items, st);
+      }
     }
   }
   if ((what & kDoReduce) && !(what & kFused) && plan.max_parts > 1)
@@ -1147,8 +1234,8 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
       }
       if (mem.size() < 2) continue;
       // Every member keeps at least one token outside the shared run, so each
-      // row's last partition is a single item of the later launch and group
-      // waves never merge (their partials need no cross-XCD coherence).
+      // row ends in a single item (group waves also count and merge the rows
+      // they complete, so the order of the two kinds does not matter).
       for (int32_t s : mem) common = std::min(common, ctx[s] - 1);
       const int32_t sh = common / kSharedPartTokens * kSharedPartTokens;
       if (sh < kSharedPartTokens) continue;
@@ -1231,6 +1318,7 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
 
 namespace pa {
 uint32_t debug_take_decode() { return debug_take_word(); }
+
 }  // namespace pa
 
 extern "C" {

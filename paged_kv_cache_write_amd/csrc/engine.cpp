@@ -111,8 +111,12 @@ int pa_engine_create(pa_bm* bm, void* k_cache, void* v_cache, int64_t num_blocks
   }
   e->events.assign(size_t(ring), nullptr);
   e->pending.assign(size_t(ring), 0);
+  // The ring events only order work (the host waits on one before it reuses a
+  // staging slot the GPU has read): no timing, and no system-scope fence
+  // (which would write back and invalidate the caches at every record).
+  const unsigned order_only = hipEventDisableTiming | hipEventDisableSystemFence;
   for (auto& ev : e->events) {
-    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+    if (hipEventCreateWithFlags(&ev, order_only) != hipSuccess) {
       pa_engine_destroy(e);
       return PA_ERR_HIP;
     }

@@ -23,6 +23,8 @@ template <class To>
 __device__ __forceinline__ To bits_as(uint32_t w) {
   return __builtin_bit_cast(To, w);
 }
+// The 32 bits of a float (a bit copy; bits_as<uint32_t>(x) would convert the value).
+__device__ __forceinline__ uint32_t float_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 
 // Storage types.  Every kernel moves data as 16-byte vectors (u32x4) and
 // computes in float32.
