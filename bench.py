@@ -443,8 +443,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": ("decode_group_mfma_kernel + decode_wave_kernel "
-                                "(pa_decode_scheduled_shared)" if shared else
+                     "kernel": (("decode_group_kernel + decode_wave_kernel"
+                                 if wl.dtype == "f32" else "decode_shared_kernel") +
+                                " (pa_decode_scheduled_shared)" if shared else
                                 "decode_wave_kernel (pa_decode_scheduled)"),
                      "algorithmic_bytes_per_launch": int(np.mean(uniq_bytes)),
                      "bytes_counted": "distinct blocks once (shared prefixes once)"},
