@@ -265,6 +265,54 @@ class FenceFreeEvents:
         self.hip.hipEventDestroy(ev)
 
 
+def decode_alone(eng, seqs, q, out_step, wl, torch, pk, hev, n):
+    """The decode launch of the engine's last step on its own: the same inputs,
+    schedule and workspace, launched ``n`` times back to back through
+    pa_decode_scheduled_shared between one pair of fence-free events on the
+    launch stream.  Events around every launch each cost the launch a few
+    microseconds of gap and a partly cold L2, so one pair over the run gives
+    the kernel's own duration as it runs inside the marker-free steps.
+    Returns (seconds per launch, context lengths, tables, output == the step's)."""
+    tables, ctx = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
+    dev = q.device
+    S = len(seqs)
+    code = pk.DTYPE_CODES()[q.dtype]
+    sch = pk.decode_schedule_shared(ctx, tables, wl.H, wl.D, wl.bs, code, eng.partition_tokens)
+    ws_bytes = eng.workspace.numel()
+    if sch["workspace_bytes"] > ws_bytes:
+        raise RuntimeError("the engine workspace does not cover the decode")
+    dev_arr = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if a.size else None
+    dt_, dc = dev_arr(tables), dev_arr(ctx)
+    di, dg, dm = dev_arr(sch["items"]), dev_arr(sch["groups"]), dev_arr(sch["members"])
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    o = torch.empty_like(q)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    fn = pk.lib().pa_decode_scheduled_shared
+    argv = (q.data_ptr(), eng.k_cache.data_ptr(), eng.v_cache.data_ptr(), dt_.data_ptr(),
+            int(tables.shape[1]), dc.data_ptr(), S, wl.H, wl.D, wl.bs, eng.NB, float(wl.scale),
+            int(sch["max_context_len"]), code, o.data_ptr(), eng.workspace.data_ptr(), ws_bytes,
+            int(sch["partition_tokens"]), st, ptr(di), int(sch["items"].shape[0]), ptr(dg),
+            int(sch["groups"].shape[0]), ptr(dm))
+
+    def launch():
+        rc = fn(*argv)
+        if rc != 0:
+            raise pk.PAError(rc, "pa_decode_scheduled_shared")
+    launch()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o, out_step))
+    a, b = hev.create(), hev.create()
+    hev.record(a, st)
+    for _ in range(n):
+        launch()
+    hev.record(b, st)
+    torch.cuda.synchronize()
+    sec = hev.elapsed_ms(a, b) * 1e-3 / n
+    hev.destroy(a)
+    hev.destroy(b)
+    return sec, ctx, tables, same
+
+
 def block_manager_stats(eng, seqs, tables, wl):
     """Memory figures of the pool after the timed steps: useful KV fraction
     sum(ctx) / (sum(ceil(ctx/bs)) * bs) (the waste is only each sequence's
@@ -351,6 +399,15 @@ def main():
         eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
     torch.cuda.synchronize()
 
+    # The decode kernel alone (the roofline figure): the last warmup step's
+    # decode, launched back to back between one pair of events, at the
+    # workload's contexts (the timed steps below append one token each).
+    hev = FenceFreeEvents()
+    kern_s, ctx_a, tab_a, same_out = decode_alone(eng, seqs, q, out, wl, torch, pk, hev,
+                                                  args.steps)
+    if not same_out:
+        eprint("warning: the back-to-back decode output differs from the engine step's")
+
     # Loop 1, the steps themselves: nothing but the steps is enqueued (event
     # markers around every decode would add their own gaps to each step).
     ncows, pts, ngroups = 0, set(), set()
@@ -364,9 +421,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    # Loop 2, the decode launch of each step between HIP events recorded on the
-    # step's stream (the roofline figure); the same steps, continued.
-    hev = FenceFreeEvents()
+    # Loop 2, the decode launch of each step between HIP events recorded by
+    # its own dispatch; the same steps, continued.
     evs = [(hev.create(), hev.create()) for _ in range(args.steps)]
     stream_handle = torch.cuda.current_stream().cuda_stream
     for a, b in evs:                      # first records outside the timed loop
@@ -400,13 +456,16 @@ def main():
     bm_stats = block_manager_stats(eng, seqs, tables, wl)
     elapsed = t1 - t0
     ms_per_step = elapsed / args.steps * 1e3
-    kern_ms = np.array([hev.elapsed_ms(a, b) for a, b in evs])
+    step_ms = np.array([hev.elapsed_ms(a, b) for a, b in evs])
     for a, b in evs:
         hev.destroy(a)
         hev.destroy(b)
-    kern_s = float(kern_ms.mean()) / 1e3
-    effective = float(np.mean(dec_bytes)) / kern_s / 1e9
-    achieved = float(np.mean(uniq_bytes)) / kern_s / 1e9
+    step_s = float(step_ms.mean()) / 1e3
+
+    dec_a, kv_a = decode_bytes(ctx_a, wl.H, wl.D, elem, wl.bs)
+    uniq_a = dec_a - kv_a + unique_kv_bytes(tab_a, ctx_a, wl.H, wl.D, elem, wl.bs)
+    effective = dec_a / kern_s / 1e9
+    achieved = uniq_a / kern_s / 1e9
     shared = max(ngroups) > 0
     value = total_step_bytes / elapsed / 1e9
     traffic = load_traffic("decode_" + wl.name)
@@ -435,8 +494,15 @@ def main():
         "seq_steps_per_s": round(S * args.steps / elapsed, 1),
         "decode_seq_steps_per_s": round(S / kern_s, 1),
         "decode_us": round(kern_s * 1e6, 2),
-        "decode_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
-                              round(float(np.percentile(kern_ms, 90)) * 1e3, 2)],
+        "decode_timing": f"the last warmup step's decode launched {args.steps} times back "
+                         "to back between one pair of events on its stream (same inputs, "
+                         "schedule and workspace as the step; output identical to the "
+                         f"step's: {same_out})",
+        "decode_ctx_sum": int(ctx_a.sum()),
+        "decode_us_in_steps": round(step_s * 1e6, 2),
+        "decode_us_in_steps_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+                                       round(float(np.percentile(step_ms, 90)) * 1e3, 2)],
+        "decode_in_steps_distinct_gbps": round(float(np.mean(uniq_bytes)) / step_s / 1e9, 2),
         "decode_gbps": round(effective, 2),
         "decode_pct_hbm_peak": round(100 * effective / HBM_PEAK_GBS, 2),
         "decode_group_items": sorted(ngroups),
@@ -447,7 +513,7 @@ def main():
                                  if wl.dtype == "f32" else "decode_shared_kernel") +
                                 " (pa_decode_scheduled_shared)" if shared else
                                 "decode_wave_kernel (pa_decode_scheduled)"),
-                     "algorithmic_bytes_per_launch": int(np.mean(uniq_bytes)),
+                     "algorithmic_bytes_per_launch": int(uniq_a),
                      "bytes_counted": "distinct blocks once (shared prefixes once)"},
     }
     # cold decode: the same steps after a 1 GiB write (the 256 MB MALL and the

@@ -37,6 +37,9 @@
 //    partitions are merged with the log-sum-exp rule: by the last wave to
 //    finish the row (one launch, an agent-scope counter per row), or by a
 //    second kernel (pa_decode_partitions + pa_decode_reduce).
+
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <type_traits>
 #include <unordered_map>
@@ -1023,49 +1026,64 @@ static int make_plan(int32_t S, int32_t H, int32_t D, int32_t bs, int32_t max_ct
 
 enum class Launch { kSingles, kGroups, kShared, kReduce };
 
+// A launch, with optional HIP events that the dispatch itself records at the
+// kernel's start and end (hipExtLaunchKernelGGL): they time the kernel without
+// marker packets around it.
+struct Timing {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <class... Args, class F>
+static void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t st, Timing t,
+                          Args... args) {
+  if (t.start || t.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, t.start, t.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
+
 template <class DT, int D>
-static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t st) {
+static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t st, Timing t) {
   const int ngroups = (p.H + kWaves - 1) / kWaves;
   switch (what) {
     case Launch::kGroups:
       if constexpr (std::is_same<DT, F32>::value)
-        hipLaunchKernelGGL((decode_group_kernel<DT, D, kGroupUnroll>),
-                           dim3(unsigned(n) * unsigned(ngroups)), dim3(kThreads), 0, st, p);
+        launch_kernel(decode_group_kernel<DT, D, kGroupUnroll>,
+                      dim3(unsigned(n) * unsigned(ngroups)), dim3(kThreads), st, t, p);
       else
-        hipLaunchKernelGGL((decode_group_mfma_kernel<DT, D>), dim3(unsigned(n) * unsigned(p.H)),
-                           dim3(kWave), 0, st, p);
+        launch_kernel(decode_group_mfma_kernel<DT, D>, dim3(unsigned(n) * unsigned(p.H)),
+                      dim3(kWave), st, t, p);
       break;
     case Launch::kSingles: {
       const dim3 grid = p.items ? dim3(unsigned(n) * unsigned(ngroups), 1, 1)
                                 : dim3(ngroups, p.max_parts, S);
       if (p.contig)
-        hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll, true>), grid, dim3(kThreads), 0,
-                           st, p);
+        launch_kernel(decode_wave_kernel<DT, D, kUnroll, true>, grid, dim3(kThreads), st, t, p);
       else
-        hipLaunchKernelGGL((decode_wave_kernel<DT, D, kUnroll>), grid, dim3(kThreads), 0, st, p);
+        launch_kernel(decode_wave_kernel<DT, D, kUnroll>, grid, dim3(kThreads), st, t, p);
       break;
     }
     case Launch::kShared:  // group and single items in one launch (16-bit storage only)
       if constexpr (!std::is_same<DT, F32>::value)
-        hipLaunchKernelGGL((decode_shared_kernel<DT, D>),
-                           dim3(unsigned(p.num_group_wgs) + unsigned(n) * unsigned(ngroups)),
-                           dim3(kWave), 0, st, p);
+        launch_kernel(decode_shared_kernel<DT, D>,
+                      dim3(unsigned(p.num_group_wgs) + unsigned(n) * unsigned(ngroups)),
+                      dim3(kWave), st, t, p);
       break;
     case Launch::kReduce:
-      hipLaunchKernelGGL((decode_reduce_kernel<DT, D, kUnroll>), dim3(p.H, S), dim3(kWave), 0,
-                         st, p);
+      launch_kernel(decode_reduce_kernel<DT, D, kUnroll>, dim3(p.H, S), dim3(kWave), st, t, p);
       break;
   }
 }
 
 static void dispatch(Launch what, int32_t dtype, int32_t D, const DecodeParams& p, int S, int n,
-                     hipStream_t st) {
+                     hipStream_t st, Timing t = Timing()) {
   if (dtype == PA_F32) {
-    if (D == 64) launch<F32, 64>(what, p, S, n, st); else launch<F32, 128>(what, p, S, n, st);
+    if (D == 64) launch<F32, 64>(what, p, S, n, st, t); else launch<F32, 128>(what, p, S, n, st, t);
   } else if (dtype == PA_F16) {
-    if (D == 64) launch<F16, 64>(what, p, S, n, st); else launch<F16, 128>(what, p, S, n, st);
+    if (D == 64) launch<F16, 64>(what, p, S, n, st, t); else launch<F16, 128>(what, p, S, n, st, t);
   } else {
-    if (D == 64) launch<BF16, 64>(what, p, S, n, st); else launch<BF16, 128>(what, p, S, n, st);
+    if (D == 64) launch<BF16, 64>(what, p, S, n, st, t);
+    else launch<BF16, 128>(what, p, S, n, st, t);
   }
 }
 
@@ -1084,6 +1102,7 @@ struct Schedule {
   const int32_t* group_items = nullptr;
   int32_t num_group_items = 0;
   const int32_t* group_members = nullptr;
+  Timing timing;  // optional: recorded at the start of the first and the end of the last launch
 };
 
 static int decode_impl(int what, const void* q, const void* k_cache, const void* v_cache,
@@ -1097,7 +1116,15 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   int rc = make_plan(S, H, D, bs, max_ctx, dtype, partition_tokens, &plan,
                      shared ? kSharedPartTokens : 0);
   if (rc != PA_OK) return rc;
-  if (S == 0) return PA_OK;
+  if (S == 0) {
+    // nothing to launch: the events still mark this point of the stream
+    hipStream_t st0 = reinterpret_cast<hipStream_t>(stream);
+    if (sched.timing.start && hipEventRecord(sched.timing.start, st0) != hipSuccess)
+      return PA_ERR_HIP;
+    if (sched.timing.stop && hipEventRecord(sched.timing.stop, st0) != hipSuccess)
+      return PA_ERR_HIP;
+    return PA_OK;
+  }
   const Contig& cg = sched.contig;
   if (!q || !k_cache || !v_cache || (!block_tables && !cg.on) || !context_lens || !out)
     return PA_ERR_INVALID;
@@ -1151,28 +1178,42 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   if (shared && cg.on) return PA_ERR_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  // the launches of this call, in order; the timing events go to the first
+  // (start) and the last (stop)
+  struct Step {
+    Launch what;
+    const DecodeParams* params;
+    int n;
+  };
+  Step steps[3];
+  int nsteps = 0;
+  DecodeParams pg = p;
   if (what & kDoPartitions) {
     if (shared && dtype != PA_F32) {
       // one launch: group waves stream the shared tiles while the single
       // waves (short private tails) run beside them
       static_assert(kThreads == kWave, "the fused launch has one wave per workgroup");
       p.num_group_wgs = sched.num_group_items * H;
-      dispatch(Launch::kShared, dtype, D, p, S, sched.items ? sched.num_items : 0, st);
+      steps[nsteps++] = {Launch::kShared, &p, sched.items ? sched.num_items : 0};
     } else {
       if (shared) {
-        DecodeParams pg = p;
         pg.window_tokens = kSharedPartTokens;
-        dispatch(Launch::kGroups, dtype, D, pg, S, sched.num_group_items, st);
+        steps[nsteps++] = {Launch::kGroups, &pg, sched.num_group_items};
       }
-      if (!sched.scheduled) {
-        dispatch(Launch::kSingles, dtype, D, p, S, 0, st);
-      } else if (sched.num_items > 0 && sched.items) {
-        dispatch(Launch::kSingles, dtype, D, p, S, sched.num_items, st);
-      }
+      if (!sched.scheduled)
+        steps[nsteps++] = {Launch::kSingles, &p, 0};
+      else if (sched.num_items > 0 && sched.items)
+        steps[nsteps++] = {Launch::kSingles, &p, sched.num_items};
     }
   }
   if ((what & kDoReduce) && !(what & kFused) && plan.max_parts > 1)
-    dispatch(Launch::kReduce, dtype, D, p, S, 0, st);
+    steps[nsteps++] = {Launch::kReduce, &p, 0};
+  for (int i = 0; i < nsteps; ++i) {
+    Timing t;
+    if (i == 0) t.start = sched.timing.start;
+    if (i == nsteps - 1) t.stop = sched.timing.stop;
+    dispatch(steps[i].what, dtype, D, *steps[i].params, S, steps[i].n, st, t);
+  }
   return launch_status();
 }
 
@@ -1319,6 +1360,33 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
 namespace pa {
 uint32_t debug_take_decode() { return debug_take_word(); }
 
+int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                           int32_t max_context_len, int32_t dtype, void* out, void* workspace,
+                           size_t workspace_bytes, int32_t partition_tokens, void* stream,
+                           const int32_t* items, int32_t num_items, const int32_t* group_items,
+                           int32_t num_group_items, const int32_t* members, hipEvent_t start,
+                           hipEvent_t stop) {
+  if (num_seqs > 0 && ((num_items > 0 && !items) || num_items < 0 || num_group_items < 0 ||
+                       (num_group_items > 0 && (!group_items || !members)) ||
+                       num_items + num_group_items <= 0))
+    return PA_ERR_INVALID;
+  Schedule sc;
+  sc.scheduled = true;
+  sc.items = items;
+  sc.num_items = num_items;
+  sc.group_items = group_items;
+  sc.num_group_items = num_group_items;
+  sc.group_members = members;
+  sc.timing.start = start;
+  sc.timing.stop = stop;
+  return decode_impl(kDoPartitions | kDoReduce | kFused, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_heads, head_dim,
+                     block_size, num_blocks, scale, max_context_len, dtype, out, workspace,
+                     workspace_bytes, partition_tokens, stream, sc);
+}
 }  // namespace pa
 
 extern "C" {
@@ -1416,28 +1484,15 @@ int pa_decode_reduce(PA_DECODE_ARGS) { return pa::decode_impl(pa::kDoReduce, PA_
 
 int pa_decode_scheduled(PA_DECODE_ARGS, const int32_t* items, int32_t num_items) {
   if (num_seqs > 0 && (!items || num_items <= 0)) return PA_ERR_INVALID;
-  pa::Schedule sc;
-  sc.scheduled = true;
-  sc.items = items;
-  sc.num_items = num_items;
-  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, PA_DECODE_PASS, sc);
+  return pa::decode_scheduled_timed(PA_DECODE_PASS, items, num_items, nullptr, 0, nullptr,
+                                    nullptr, nullptr);
 }
 
 int pa_decode_scheduled_shared(PA_DECODE_ARGS, const int32_t* items, int32_t num_items,
                                const int32_t* group_items, int32_t num_group_items,
                                const int32_t* members) {
-  if (num_seqs > 0 && ((num_items > 0 && !items) || num_items < 0 || num_group_items < 0 ||
-                       (num_group_items > 0 && (!group_items || !members)) ||
-                       num_items + num_group_items <= 0))
-    return PA_ERR_INVALID;
-  pa::Schedule sc;
-  sc.scheduled = true;
-  sc.items = items;
-  sc.num_items = num_items;
-  sc.group_items = group_items;
-  sc.num_group_items = num_group_items;
-  sc.group_members = members;
-  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, PA_DECODE_PASS, sc);
+  return pa::decode_scheduled_timed(PA_DECODE_PASS, items, num_items, group_items,
+                                    num_group_items, members, nullptr, nullptr);
 }
 
 // Contiguous (non-paged) K/V: the same decode with token rows addressed by

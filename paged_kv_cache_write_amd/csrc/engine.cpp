@@ -40,7 +40,7 @@ struct pa_engine {
   std::vector<hipEvent_t> events;
   std::vector<char> pending;
   std::vector<int32_t> ctx_pre;
-  hipEvent_t ev_start = nullptr, ev_end = nullptr;  // optional, around the decode launch
+  hipEvent_t ev_start = nullptr, ev_end = nullptr;  // optional: the decode kernel's start / end
   bool sharing = true;  // detect shared prefixes in the tables each step
   pa::HostSchedule hs;
 };
@@ -236,24 +236,21 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
                         stream);
     if (rc != PA_OK) return rc;
   }
-  if (e->ev_start && hipEventRecord(e->ev_start, st) != hipSuccess) return PA_ERR_HIP;
   const int32_t* d_tab = reinterpret_cast<const int32_t*>(d + off_tab);
   const int32_t* d_ctx = reinterpret_cast<const int32_t*>(d + off_ctx);
   const int32_t* d_items = reinterpret_cast<const int32_t*>(d + off_items);
-  if (n_groups > 0) {
-    rc = pa_decode_scheduled_shared(q, e->k_cache, e->v_cache, d_tab, e->max_blocks, d_ctx, n,
-                                    e->H, e->D, e->bs, e->num_blocks, scale, max_ctx, e->dtype,
-                                    out, workspace, workspace_bytes, pt, stream,
-                                    n_items ? d_items : nullptr, n_items,
-                                    reinterpret_cast<const int32_t*>(d + off_groups), n_groups,
-                                    reinterpret_cast<const int32_t*>(d + off_members));
-  } else {
-    rc = pa_decode_scheduled(q, e->k_cache, e->v_cache, d_tab, e->max_blocks, d_ctx, n, e->H,
-                             e->D, e->bs, e->num_blocks, scale, max_ctx, e->dtype, out, workspace,
-                             workspace_bytes, pt, stream, d_items, n_items);
-  }
+  // ev_start / ev_end (if set) are recorded by the decode kernel's own dispatch
+  rc = pa::decode_scheduled_timed(q, e->k_cache, e->v_cache, d_tab, e->max_blocks, d_ctx, n,
+                                  e->H, e->D, e->bs, e->num_blocks, scale, max_ctx, e->dtype,
+                                  out, workspace, workspace_bytes, pt, stream,
+                                  n_items ? d_items : nullptr, n_items,
+                                  n_groups ? reinterpret_cast<const int32_t*>(d + off_groups)
+                                           : nullptr,
+                                  n_groups,
+                                  n_groups ? reinterpret_cast<const int32_t*>(d + off_members)
+                                           : nullptr,
+                                  e->ev_start, e->ev_end);
   if (rc != PA_OK) return rc;
-  if (e->ev_end && hipEventRecord(e->ev_end, st) != hipSuccess) return PA_ERR_HIP;
   // Host slot `slot` may be rewritten once this step has run (recorded at the
   // end of the step: no marker between the prologue and the decode).
   if (hipEventRecord(e->events[slot], st) != hipSuccess) return PA_ERR_HIP;

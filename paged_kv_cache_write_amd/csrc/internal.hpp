@@ -38,6 +38,19 @@ int launch_step_prologue(const void* host_src, void* dev_dst, size_t copy_bytes,
                          int32_t head_dim, int32_t block_size, int32_t dtype,
                          hipStream_t stream);
 
+// pa_decode_scheduled (num_group_items == 0) or pa_decode_scheduled_shared,
+// with optional HIP events recorded by the dispatch itself at the start of
+// the decode's first kernel and the end of its last (no marker packets).
+int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                           int32_t max_context_len, int32_t dtype, void* out, void* workspace,
+                           size_t workspace_bytes, int32_t partition_tokens, void* stream,
+                           const int32_t* items, int32_t num_items, const int32_t* group_items,
+                           int32_t num_group_items, const int32_t* members, hipEvent_t start,
+                           hipEvent_t stop);
+
 // Device error words of the translation units with kernels (debug builds:
 // table entries, slots and copy pairs out of range; release builds: 0), each
 // read and cleared.  Synchronous.
