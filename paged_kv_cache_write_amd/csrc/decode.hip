@@ -964,7 +964,7 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams P) {
 }
 
 // ------------------------------------------------------------------ host side
-constexpr int64_t kSchedTargetWaves = 1536;  // 256 CUs x 6
+constexpr int64_t kSchedTargetWaves = 2048;  // 256 CUs x 8
 
 struct Plan {
   int part_tokens;
@@ -1286,9 +1286,10 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
   }
   int32_t pt = requested;
   if (pt == 0) {
-    // Largest partition (up to 1024 tokens and 64 blocks) that still gives
-    // about six waves per CU: long waves stream without pause, the
-    // longest-first order evens out the end, and fewer partials are merged.
+    // Largest partition (up to 1024 tokens and 64 blocks, in steps of 128
+    // tokens) that still gives about eight waves per CU: long waves stream
+    // without pause, the longest-first order evens out the end, and fewer
+    // partials are merged.
     const int max_pt = std::min(64 * bs, 1024);
     pt = max_pt;
     int64_t gwaves = 0;
@@ -1299,7 +1300,7 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
       int64_t waves = gwaves;
       for (int32_t s = 0; s < S; ++s) waves += (ctx[s] - shared[s] + pt - 1) / pt;
       if (waves * H >= kSchedTargetWaves) break;
-      pt /= 2;
+      pt -= 128;
     }
   }
   Plan plan;
