@@ -10,9 +10,13 @@
 //
 // Staging: the caller gives `ring` pinned host slots and one device slot of
 // pa_engine_staging_bytes() each.  A step fills host slot i (slots, context
-// lengths, CoW pairs, block tables, work items), copies exactly the used
-// bytes to the device slot with one hipMemcpyAsync, and records an event;
-// host slot i is reused only after that event.  The device slot is reused in
+// lengths, CoW pairs, block tables, work items); the step prologue kernel
+// reads exactly the used bytes from the mapped host slot into the device slot
+// (or one hipMemcpyAsync does, where the host memory is not mapped).  Events
+// guard the host slots in groups: with an even ring the slots form two halves
+// and one event is recorded after the last step of each half, so a marker
+// packet sits between only every ring/2-th pair of steps; a host slot is
+// rewritten only after the event of its group.  The device slot is reused in
 // stream order.
 #include <hip/hip_runtime_api.h>
 
@@ -37,6 +41,8 @@ struct pa_engine {
   char* dev = nullptr;
   size_t slot_bytes = 0;
   int32_t ring = 0, next = 0;
+  int32_t group = 1;       // host slots per guarding event (the event sits on the group's last)
+  bool unguarded = false;  // steps enqueued since the last recorded guard event
   std::vector<hipEvent_t> events;
   std::vector<char> pending;
   std::vector<int32_t> ctx_pre;
@@ -99,6 +105,7 @@ int pa_engine_create(pa_bm* bm, void* k_cache, void* v_cache, int64_t num_blocks
   e->dev = static_cast<char*>(dev_staging);
   e->slot_bytes = pa_engine_staging_bytes(max_batch, max_blocks_per_seq, block_size);
   e->ring = ring;
+  e->group = (ring % 2 == 0) ? ring / 2 : 1;
   {
     // Pinned host memory is mapped for the device: the step prologue kernel
     // reads the staging straight from it instead of a DMA copy.
@@ -127,6 +134,9 @@ int pa_engine_create(pa_bm* bm, void* k_cache, void* v_cache, int64_t num_blocks
 
 void pa_engine_destroy(pa_engine* e) {
   if (!e) return;
+  // steps after the last guard event may still read the host staging, which
+  // the caller frees after this call
+  if (e->unguarded) (void)hipDeviceSynchronize();
   for (size_t i = 0; i < e->events.size(); ++i) {
     if (e->events[i]) {
       if (e->pending[i]) (void)hipEventSynchronize(e->events[i]);
@@ -180,9 +190,10 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
 
   // 2. Host staging slot.
   const int32_t slot = e->next;
-  if (e->pending[slot]) {
-    if (hipEventSynchronize(e->events[slot]) != hipSuccess) return PA_ERR_HIP;
-    e->pending[slot] = 0;
+  const int32_t guard = slot / e->group * e->group + e->group - 1;  // the group's event
+  if (e->pending[guard]) {
+    if (hipEventSynchronize(e->events[guard]) != hipSuccess) return PA_ERR_HIP;
+    e->pending[guard] = 0;
   }
   char* h = e->host + size_t(slot) * e->slot_bytes;
   const size_t off_slots = 0, off_ctx = 8 * size_t(n), off_cow = off_ctx + 4 * size_t(n);
@@ -251,10 +262,15 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
                                            : nullptr,
                                   e->ev_start, e->ev_end);
   if (rc != PA_OK) return rc;
-  // Host slot `slot` may be rewritten once this step has run (recorded at the
-  // end of the step: no marker between the prologue and the decode).
-  if (hipEventRecord(e->events[slot], st) != hipSuccess) return PA_ERR_HIP;
-  e->pending[slot] = 1;
+  // The host slots of this group may be rewritten once this step has run
+  // (recorded at the end of the group's last step: no marker between the
+  // prologue and the decode, and none after the group's other steps).
+  e->unguarded = true;
+  if (slot == guard) {
+    if (hipEventRecord(e->events[slot], st) != hipSuccess) return PA_ERR_HIP;
+    e->pending[slot] = 1;
+    e->unguarded = false;
+  }
   e->next = (slot + 1) % e->ring;
   if (info) {
     info->num_cow = ncow;

@@ -29,7 +29,7 @@ class PagedKVEngine:
     ``max_blocks_per_seq`` the table width (so contexts up to that many blocks).
     """
 
-    RING = 3  # pinned staging slots in flight
+    RING = 16  # pinned staging slots in flight: two halves, one guard event each
 
     def __init__(self, num_blocks, num_heads, head_dim, block_size, dtype, max_blocks_per_seq,
                  max_batch, free_order=None, pad_block=0, device="cuda", fill=None,
