@@ -5,6 +5,7 @@ attention outputs within 2e-3 absolute of the float64 oracle, finite, with
 never-written pool slots and unused table entries poisoned with NaN.
 """
 import math
+import time
 
 import numpy as np
 import pytest
@@ -288,3 +289,90 @@ def test_fused_merge_repeatable():
         assert bad == 0, f"pt={pt}: {bad} of {len(outs)} fused calls differ from the two-launch merge"
         assert int(ws[: wl.S * wl.H * 4].view(torch.int32).abs().sum().item()) == 0
         log(f"fused merge pt={pt}: 50 calls bit-identical to the two-launch merge")
+
+
+def test_engine_steps_in_flight():
+    """Forty engine steps enqueued behind a long GPU wait, so that the host wraps
+    the pinned staging ring (16 slots, one guard event per half) several times
+    while earlier steps have not run: every step's output, pool write and
+    copy-on-write must match the oracle replaying the same steps in order.
+    Twice a beam-style selection (one fork, one retired sequence) happens on
+    the host between in-flight steps, so later steps copy on write and reuse
+    freed blocks; each step has its own q and new-token K/V."""
+    import dataclasses
+    wl = synth.make_fork_tree(733, 4, 128, "f16", 16, roots=2, forks=6, max_prompt=500,
+                              max_extend=120)
+    nsteps = 40
+    S = int(wl.ctx.size)
+    extra = S * (-(-(nsteps + 2) // wl.bs) + 2)
+    wl2 = dataclasses.replace(
+        wl, NB=wl.NB + extra,
+        free_order=np.concatenate([wl.free_order,
+                                   np.arange(wl.NB, wl.NB + extra, dtype=np.int32)]),
+        max_blocks_per_seq=wl.max_blocks_per_seq + -(-nsteps // wl.bs) + 1)
+    r = oracle.run_workload(wl2, decode=False)     # through the workload's own step
+    bm, kc, vc = r["model"], r["k_cache"], r["v_cache"]
+    seqs = [int(s) for s in wl.ops[-1][1]]
+    g = run_gpu(wl2)
+    eng = g["engine"]
+    assert eng.RING == 16
+    rng = np.random.default_rng(np.random.SeedSequence([733, 77]))
+    qs, ks, vs = [], [], []
+    for _ in range(nsteps):
+        qs.append(synth.to_storage(rng.standard_normal((S, wl.H, wl.D)), "f16"))
+        ks.append(synth.to_storage(rng.standard_normal((S, wl.H, wl.D)), "f16"))
+        vs.append(synth.to_storage(rng.standard_normal((S, wl.H, wl.D)), "f16"))
+    qd = [to_dev(x, "f16") for x in qs]
+    kd = [to_dev(x, "f16") for x in ks]
+    vd = [to_dev(x, "f16") for x in vs]
+    outs = [torch.empty_like(qd[0]) for _ in range(nsteps)]
+    # before step i: fork row p's sequence into a new id that takes row r's place
+    selections = {12: (2, 5, 1000), 27: (0, 3, 1001)}
+    gseqs = list(seqs)
+    torch.cuda.synchronize()
+    # the GPU stays busy (400 writes of 1 GiB, ~60 ms) while the host runs ahead
+    filler = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for j in range(400):
+        filler.fill_(j & 0xFF)
+    f1.record()
+    ahead = None
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        if i == eng.RING // 2:  # half the ring enqueued; the wrap below waits for a guard event
+            ahead = not f1.query()
+            host_ms = (time.perf_counter() - t0) * 1e3
+        if i in selections:
+            p, rr, child = selections[i]
+            eng.select([(gseqs[p], child)], [gseqs[rr]])
+            gseqs[rr] = child
+        eng.step(np.array(gseqs, dtype=np.int64), qd[i], kd[i], vd[i], wl.scale, out=outs[i])
+    torch.cuda.synchronize()
+    ncow = 0
+    for i in range(nsteps):
+        if i in selections:
+            p, rr, child = selections[i]
+            bm.fork(seqs[p], child)
+            bm.free_seq(seqs[rr])
+            seqs[rr] = child
+        slots, cows = [], []
+        for s in seqs:
+            slot, cow = bm.append_slot(s)
+            slots.append(slot)
+            if cow is not None:
+                cows.append(cow)
+        ncow += len(cows)
+        oracle.oracle_copy_blocks(kc, vc, cows)
+        oracle.oracle_cache_write(ks[i], vs[i], slots, kc, vc)
+        tables = bm.table_array(seqs, wl2.max_blocks_per_seq, wl.poison_block)
+        ctx = np.array([bm.lens[s] for s in seqs], dtype=np.int64)
+        ref = oracle.oracle_decode(qs[i], kc, vc, tables, ctx, wl.scale, "f16")
+        compare_outputs(outs[i], ref, what=f"engine step {i + 1} of {nsteps}", cast_dtype="f16")
+    _same_storage(eng.k_cache, kc, "f16", "k pool after the steps")
+    _same_storage(eng.v_cache, vc, "f16", "v pool after the steps")
+    log(f"host enqueued {eng.RING // 2} steps in {host_ms:.2f} ms; the GPU filler took "
+        f"{f0.elapsed_time(f1):.2f} ms")
+    assert ahead, "the host should have filled the staging ring while the GPU was busy"
+    assert ncow >= 2, "the selections should make later steps copy on write"
+    log(f"{nsteps} engine steps in flight: outputs and pools match ({ncow} copies on write)")
