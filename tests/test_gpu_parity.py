@@ -376,3 +376,21 @@ def test_engine_steps_in_flight():
     assert ahead, "the host should have filled the staging ring while the GPU was busy"
     assert ncow >= 2, "the selections should make later steps copy on write"
     log(f"{nsteps} engine steps in flight: outputs and pools match ({ncow} copies on write)")
+
+
+@pytest.mark.parametrize("dtype,D,H,bs", [("bf16", 128, 40, 16), ("f32", 64, 10, 8),
+                                          ("f16", 64, 12, 32)])
+def test_wide_workgroup_launch(dtype, D, H, bs):
+    """Work lists of 8192 waves or more run with workgroups of 4 consecutive heads
+    (head counts that 4 does not divide included): pools bit-exact, every output
+    within tolerance, ragged contexts that also split into several partitions."""
+    rng = np.random.default_rng(np.random.SeedSequence([741, D, H]))
+    S = -(-8400 // H)
+    ctx = rng.integers(1, 1400, size=S)
+    ctx[:7] = [1, 2, 15, 16, 17, 1023, 1399]
+    wl = synth.make_custom(741 + H, H, D, dtype, bs, ctx)
+    g, _, _ = _check_workload(wl, cast_bound=True)
+    info = g["engine"].last_info
+    assert info.num_items * H >= 8192, "the launch should be wide"
+    log(f"wide launch: {info.num_items} items x {H} heads, partitions of "
+        f"{info.partition_tokens} tokens")
