@@ -27,13 +27,15 @@ class PagedKVEngine:
     ``pad_block`` fills the unused tail of every exported table row (never used
     as an address).  ``max_batch`` bounds the sequences of one step and
     ``max_blocks_per_seq`` the table width (so contexts up to that many blocks).
+    ``ring`` pinned staging slots (default RING) let the host run that many
+    steps ahead; with an even count one event guards each half of them.
     """
 
     RING = 16  # pinned staging slots in flight: two halves, one guard event each
 
     def __init__(self, num_blocks, num_heads, head_dim, block_size, dtype, max_blocks_per_seq,
                  max_batch, free_order=None, pad_block=0, device="cuda", fill=None,
-                 partition_tokens=0):
+                 partition_tokens=0, ring=None):
         import torch
         self.torch = torch
         self.NB, self.H, self.D, self.bs = int(num_blocks), int(num_heads), int(head_dim), \
@@ -54,12 +56,13 @@ class PagedKVEngine:
         self.bm = BlockManager(self.NB, self.bs, free_order)
         L = self._lib = lib()  # the library that owns the handle
         slot = int(L.pa_engine_staging_bytes(self.max_batch, self.maxB, self.bs))
-        self._host = torch.empty(slot * self.RING, dtype=torch.uint8, pin_memory=True)
+        self.ring = int(ring or self.RING)
+        self._host = torch.empty(slot * self.ring, dtype=torch.uint8, pin_memory=True)
         self._dev = torch.empty(slot, dtype=torch.uint8, device=self.device)
         h = ctypes.c_void_p()
         rc = L.pa_engine_create(self.bm._h, self.k_cache.data_ptr(), self.v_cache.data_ptr(),
                                 self.NB, self.H, self.D, self.bs, self.dt_code, self.max_batch,
-                                self.maxB, self.pad, self._host.data_ptr(), self.RING,
+                                self.maxB, self.pad, self._host.data_ptr(), self.ring,
                                 self._dev.data_ptr(), ctypes.byref(h))
         _check(rc, "pa_engine_create")
         self._e = h

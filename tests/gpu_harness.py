@@ -50,7 +50,7 @@ def oracle_bits(a, dtype_name):
     return np.ascontiguousarray(a).view(np.int32)
 
 
-def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True):
+def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True, ring=None):
     """Execute wl.ops with PagedKVEngine; returns dict with the engine and the step output."""
     import torch
     from paged_kv_cache_write_amd.engine import PagedKVEngine
@@ -58,7 +58,7 @@ def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True):
     eng = PagedKVEngine(wl.NB, wl.H, wl.D, wl.bs, tdt, wl.max_blocks_per_seq, wl.S,
                         free_order=wl.free_order, pad_block=wl.poison_block,
                         fill=float("nan") if fill_nan else 0.0,
-                        partition_tokens=partition_tokens)
+                        partition_tokens=partition_tokens, ring=ring)
     eng.set_sharing(sharing)
     out = None
     for op in wl.ops:

@@ -291,10 +291,12 @@ def test_fused_merge_repeatable():
         log(f"fused merge pt={pt}: 50 calls bit-identical to the two-launch merge")
 
 
-def test_engine_steps_in_flight():
+@pytest.mark.parametrize("ring", [16, 4, 3])
+def test_engine_steps_in_flight(ring):
     """Forty engine steps enqueued behind a long GPU wait, so that the host wraps
-    the pinned staging ring (16 slots, one guard event per half) several times
-    while earlier steps have not run: every step's output, pool write and
+    the pinned staging ring several times (16 or 4 slots: one guard event per
+    half; 3 slots: one event per step) while earlier steps have not run:
+    every step's output, pool write and
     copy-on-write must match the oracle replaying the same steps in order.
     Twice a beam-style selection (one fork, one retired sequence) happens on
     the host between in-flight steps, so later steps copy on write and reuse
@@ -313,9 +315,9 @@ def test_engine_steps_in_flight():
     r = oracle.run_workload(wl2, decode=False)     # through the workload's own step
     bm, kc, vc = r["model"], r["k_cache"], r["v_cache"]
     seqs = [int(s) for s in wl.ops[-1][1]]
-    g = run_gpu(wl2)
+    g = run_gpu(wl2, ring=ring)
     eng = g["engine"]
-    assert eng.RING == 16
+    assert eng.ring == ring
     rng = np.random.default_rng(np.random.SeedSequence([733, 77]))
     qs, ks, vs = [], [], []
     for _ in range(nsteps):
@@ -340,7 +342,7 @@ def test_engine_steps_in_flight():
     ahead = None
     t0 = time.perf_counter()
     for i in range(nsteps):
-        if i == eng.RING // 2:  # half the ring enqueued; the wrap below waits for a guard event
+        if i == eng.ring // 2:  # half the ring enqueued; the wrap below waits for a guard event
             ahead = not f1.query()
             host_ms = (time.perf_counter() - t0) * 1e3
         if i in selections:
@@ -371,7 +373,7 @@ def test_engine_steps_in_flight():
         compare_outputs(outs[i], ref, what=f"engine step {i + 1} of {nsteps}", cast_dtype="f16")
     _same_storage(eng.k_cache, kc, "f16", "k pool after the steps")
     _same_storage(eng.v_cache, vc, "f16", "v pool after the steps")
-    log(f"host enqueued {eng.RING // 2} steps in {host_ms:.2f} ms; the GPU filler took "
+    log(f"ring {ring}: host enqueued {eng.ring // 2} steps in {host_ms:.2f} ms; the GPU filler took "
         f"{f0.elapsed_time(f1):.2f} ms")
     assert ahead, "the host should have filled the staging ring while the GPU was busy"
     assert ncow >= 2, "the selections should make later steps copy on write"
