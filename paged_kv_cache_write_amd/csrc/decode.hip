@@ -76,6 +76,7 @@ constexpr int kGroupUnroll = 4;            // chunk of a group wave (register bu
 #define PA_SHARED_PART_TOKENS 256
 #endif
 constexpr int kSharedPartTokens = PA_SHARED_PART_TOKENS;  // partition of a shared range
+constexpr float kGroupSlack = 8.0f;  // lazy rescale threshold of the group waves, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so max - max never is NaN
 
@@ -812,22 +813,27 @@ __device__ __forceinline__ void group_mfma_body(DecodeParams P, unsigned block_x
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    l *= alpha;
+    // The reference m moves only when a query's maximum passes it by more
+    // than kGroupSlack (log2 units): weights stay <= 2^kGroupSlack, and O and
+    // l are rescaled on few steps (o / l does not depend on m).
+    if (__builtin_amdgcn_ballot_w64(mx > m + kGroupSlack) != 0) {  // wave-uniform
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int jd = 0; jd < NJ; ++jd) o[jd] *= alpha;
+    }
     u32x4 phi, plo;
 #pragma unroll
     for (int p2 = 0; p2 < 4; ++p2) {
-      const float p0 = fast_exp2(x[2 * p2] - mn), p1 = fast_exp2(x[2 * p2 + 1] - mn);
+      const float p0 = fast_exp2(x[2 * p2] - m), p1 = fast_exp2(x[2 * p2 + 1] - m);
       l += p0 + p1;
       uint32_t hw, lw;
       split_pair(DT{}, p0, p1, hw, lw);
       phi[p2] = hw;
       plo[p2] = lw;
     }
-#pragma unroll
-    for (int jd = 0; jd < NJ; ++jd) o[jd] *= alpha;
 #pragma unroll
     for (int jd = 0; jd < NJ; ++jd) {
       // V^T operand of product jd: element jd of the lane's eight row loads
@@ -864,7 +870,7 @@ __device__ __forceinline__ void group_mfma_body(DecodeParams P, unsigned block_x
   // the four lanes of a query hold partial sums over their token rows
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
-  const float inv = 1.0f / l;  // l >= 1: the running max token contributes 2^0
+  const float inv = 1.0f / l;  // l >= 1: the maximum token contributes 2^(max - m) >= 1
   const bool split = nparts_q > 1;
   if (has_q && !split) {
     T* out = reinterpret_cast<T*>(P.out) + row_q * D;
