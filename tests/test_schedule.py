@@ -208,3 +208,28 @@ def test_shared_schedule_errors():
         pk.decode_schedule_shared(ctx, tables, 8, 128, 16, 1, 0)
     with pytest.raises(pk.PAError):
         pk.decode_schedule_shared(np.array([300], np.int32), tables[:1], 8, 96, 16, 1, 0)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32, 128])
+def test_automatic_partition_size(bs):
+    """The automatic partition size is the largest of 1024, 896, ..., 256 tokens
+    (at most 64 blocks) whose work list still has 2048 waves (8 per CU of the
+    256), or 256 when none has: checked as properties of the chosen size on
+    random batches, from a handful of sequences to hundreds."""
+    pk = _pk()
+    H = 40
+    rng = np.random.default_rng(bs)
+    cap = min(1024, 64 * bs)
+    seen = set()
+    for i in range(40):
+        S = int(rng.integers(1, 12)) if i % 2 else int(rng.integers(12, 300))
+        ctx = rng.integers(1, 4000, size=S).astype(np.int32)
+        items, pt, _ = pk.decode_schedule(ctx, H, 128, bs, 1, 0)
+        seen.add(pt)
+        waves = lambda p: int((-(-ctx.astype(np.int64) // p)).sum()) * H
+        assert 256 <= pt <= cap and (cap - pt) % 128 == 0 and pt % bs == 0
+        assert len(items) * H == waves(pt)
+        assert waves(pt) >= 2048 or pt == 256
+        if pt < cap:
+            assert waves(pt + 128) < 2048, "a larger partition also had enough waves"
+    assert len(seen) > 1
