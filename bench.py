@@ -97,7 +97,8 @@ def build_state(wl, dtype, partition_tokens=0, extra_blocks=64):
 def cpu_baseline(wl, max_seconds=20.0):
     """The oracle (float64 NumPy, one thread) on one step of the same workload:
     the step's cache write plus decode of every sequence.  Repeated until about
-    ``max_seconds`` of work or 3 repetitions."""
+    10 s of work (half of ``max_seconds`` when that is smaller), and never past
+    ``max_seconds`` after the first repetition."""
     import oracle
     from threadpoolctl import threadpool_limits
     r = oracle.run_workload(wl, decode=False)
@@ -106,7 +107,9 @@ def cpu_baseline(wl, max_seconds=20.0):
     new_v = np.stack([wl.kv(int(s), int(c) - 1, int(c))[1][0] for s, c in enumerate(r["ctx"])])
     reps, t_total = 0, 0.0
     with threadpool_limits(limits=1):
-        while reps < 3 and t_total < max_seconds:
+        min_seconds = min(10.0, max_seconds / 2)
+        while reps == 0 or (t_total < min_seconds and reps < 10000 and
+                            t_total * (reps + 1) / reps <= max_seconds):
             t0 = time.perf_counter()
             oracle.oracle_cache_write(new_k, new_v, r["step_slots"], kc, vc)
             oracle.oracle_decode(wl.q, kc, vc, r["tables"], r["ctx"], wl.scale, wl.dtype)
