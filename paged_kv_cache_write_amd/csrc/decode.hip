@@ -356,6 +356,78 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, size_t row
   for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, O[e] / L);
 }
 
+// The same merge for up to kTPI rows at once: the lanes of token row r of
+// the wave (kLPT of them) merge the row `row_id` they were given (active),
+// which has at most kMergeParts partitions.  Lane c of a group holds
+// partition c's (max, sum); every lane loads its columns of all the
+// partitions in one batch, so the rows cost two dependent round trips
+// together instead of two each.
+constexpr int kMergeParts = 8;
+template <class DT, int D, int U>
+__device__ __forceinline__ void merge_partials_grouped(const DecodeParams& P, size_t row_id,
+                                                       int nparts, bool active, int lane) {
+  using T = typename DT::T;
+  using Sh = Shape<DT, D, U>;
+  constexpr int kVec = DT::kVec;
+  static_assert(kMergeParts <= Sh::kLPT, "one lane per partition");
+  const int col = lane % Sh::kLPT;
+  const int base = lane - col;  // first lane of this token row
+  const size_t pi0 = row_id * P.max_parts;
+  const float* ml = P.ws_ml + 2 * pi0;
+  const bool has = active && col < nparts;
+  const float mp = has ? __hip_atomic_load(ml + 2 * col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : kNegBig;
+  const float lp = has ? __hip_atomic_load(ml + 2 * col + 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : 0.f;
+  float M = mp;
+#pragma unroll
+  for (int off = 1; off < Sh::kLPT; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+  const float wl = has ? lp * fast_exp2(mp - M) : 0.f;
+  float L = wl;
+#pragma unroll
+  for (int off = 1; off < Sh::kLPT; off <<= 1) L += __shfl_xor(L, off, kWave);
+  // all loads first (clamped to the row's last partition: in bounds), then
+  // the weighted sum with weight 0 past the row's partitions
+  const int last = active ? max(nparts - 1, 0) : 0;
+  float v[kMergeParts][kVec];
+#pragma unroll
+  for (int p = 0; p < kMergeParts; ++p) {
+    const float* po = P.ws_o + (pi0 + min(p, last)) * D + col;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e)
+      v[p][e] = __hip_atomic_load(po + e * Sh::kLPT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // The sums are formed in merge_partials' order (partition p into the
+  // partial sum of token row p % kTPI, then those pairwise as its shuffles
+  // add them), so either merge gives the same bits for a row.
+  float O[Sh::kTPI][kVec];
+#pragma unroll
+  for (int r = 0; r < Sh::kTPI; ++r)
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) O[r][e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < kMergeParts; ++p) {
+    const float w = __shfl(wl, base + p, kWave);
+    const bool in = p < nparts;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const float acc = O[p % Sh::kTPI][e] + w * v[p][e];
+      O[p % Sh::kTPI][e] = in ? acc : O[p % Sh::kTPI][e];
+    }
+  }
+#pragma unroll
+  for (int stride = 1; stride < Sh::kTPI; stride *= 2)
+#pragma unroll
+    for (int r = 0; r < Sh::kTPI; r += 2 * stride)
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) O[r][e] = O[r][e] + O[r + stride][e];
+  if (!active) return;
+  T* o = reinterpret_cast<T*>(P.out) + row_id * D + col * kVec;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) o[e] = to_store(DT{}, O[0][e] / L);
+}
+
 // End of a (row, partition) for the NQ queries of one wave (rows row_id[g],
 // nparts[g]; the wave's token rows are already merged).  A row with one
 // partition is stored directly.  Otherwise the partial goes to the
@@ -939,13 +1011,45 @@ __device__ __forceinline__ void group_mfma_body(DecodeParams P, unsigned block_x
                                             __HIP_MEMORY_SCOPE_AGENT);
     last = prev == nparts_q - 1 ? 1 : 0;
   }
-  for (int k = 0; k < nq; ++k) {  // members whose row this wave completed
-    if (!__shfl(last, k, kWave)) continue;  // wave-uniform
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // Members whose row this wave completed (a wave-uniform mask): every
+  // partition of such a row has counted, so its counter is reset for the
+  // next call; the rows are merged kTPI at a time, one per token row of the
+  // wave, when they have at most kMergeParts partitions, else one by one.
+  using MSh = Shape<DT, D, kUnroll>;
+  uint32_t done = 0;
+  for (int k = 0; k < nq; ++k)
+    if (__shfl(last, k, kWave)) done |= 1u << k;
+  if (done == 0) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int max_parts = 0;
+  for (uint32_t d = done; d; d &= d - 1) {
+    const int k = __builtin_ctz(d);
     const size_t row_k = size_t(mem[kMemberInts * k]) * H + h;
-    if (lane == 0)  // every partition of this row has counted: reset for the next call
+    if (lane == 0)
       __hip_atomic_store(P.counters + row_k, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merge_partials<DT, D, kUnroll>(P, row_k, mem[kMemberInts * k + 1], lane);
+    max_parts = max(max_parts, mem[kMemberInts * k + 1]);
+  }
+  if (max_parts > kMergeParts) {
+    for (uint32_t d = done; d; d &= d - 1) {
+      const int k = __builtin_ctz(d);
+      merge_partials<DT, D, kUnroll>(P, size_t(mem[kMemberInts * k]) * H + h,
+                                     mem[kMemberInts * k + 1], lane);
+    }
+    return;
+  }
+  const int my_row = lane / MSh::kLPT;  // this lane's token row: one merged row each
+  while (done) {
+    int mine = -1;
+#pragma unroll
+    for (int r = 0; r < MSh::kTPI; ++r) {
+      if (done == 0) break;
+      const int k = __builtin_ctz(done);
+      done &= done - 1;
+      if (r == my_row) mine = k;
+    }
+    const int k = mine < 0 ? 0 : mine;
+    merge_partials_grouped<DT, D, kUnroll>(P, size_t(mem[kMemberInts * k]) * H + h,
+                                           mem[kMemberInts * k + 1], mine >= 0, lane);
   }
 }
 
