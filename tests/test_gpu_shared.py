@@ -166,3 +166,38 @@ def test_shared_entry_point_errors():
                                         None) == -1
     assert L.pa_decode_scheduled_shared(*args, None, 0, None, 0, None) == -1
     torch.cuda.synchronize()
+
+
+def test_config4_merges_repeat_bit_for_bit():
+    """Shared-prefix workload at full size (64 sequences in 8 groups, bf16): a
+    row's partials are merged by whichever wave finishes it last, a group wave
+    (several rows at once) or a single wave (one row), so thirty calls in a row
+    must give the same bits, leave the counters at zero and match the oracle."""
+    import paged_kv_cache_write_amd as pk
+    from gpu_harness import run_gpu
+    wl = synth.make_workload(4)
+    g = run_gpu(wl)
+    eng = g["engine"]
+    step = np.array([op for op in wl.ops if op[0] == "step"][-1][1], dtype=np.int64)
+    tables, ctx = eng.bm.block_tables(step, wl.max_blocks_per_seq, wl.poison_block)
+    d = pk.decode_schedule_shared(ctx, tables, wl.H, wl.D, wl.bs, 2, 0)
+    assert len(d["groups"]) > 0
+    q = to_dev(wl.q, wl.dtype)
+    td, cd = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+    items = torch.from_numpy(d["items"]).cuda()
+    groups = torch.from_numpy(d["groups"]).cuda()
+    members = torch.from_numpy(d["members"]).cuda()
+    ws = torch.zeros(max(d["workspace_bytes"], 16), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(q) for _ in range(30)]
+    for o in outs:
+        pk.decode_scheduled_shared(q, eng.k_cache, eng.v_cache, td, cd, wl.scale,
+                                   d["max_context_len"], items, groups, members,
+                                   d["partition_tokens"], out=o, workspace=ws)
+    torch.cuda.synchronize()
+    want = bits(outs[0])
+    bad = sum(not np.array_equal(bits(o), want) for o in outs)
+    assert bad == 0, f"{bad} of {len(outs)} calls differ"
+    assert int(ws[: len(ctx) * wl.H * 4].view(torch.int32).abs().sum().item()) == 0
+    compare_outputs(g["out"], oracle.run_workload(wl)["out"], what="config 4 engine step")
+    assert np.array_equal(bits(g["out"]), want), "the engine step's own decode differs"
+    log(f"config 4: {len(outs)} calls bit-identical, {len(d['groups'])} group items")
