@@ -110,17 +110,19 @@ def _direct_case(dtype, bs, H=4, D=128, seed=540):
     return kc, vc, q, tables, ctx, poison
 
 
-@pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 32), ("f32", 8)])
-def test_direct_shared_entry_points(dtype, bs):
+@pytest.mark.parametrize("dtype,bs,D", [("f16", 16, 128), ("bf16", 32, 128), ("f32", 8, 128),
+                                        ("bf16", 16, 64), ("f16", 8, 64)])
+def test_direct_shared_entry_points(dtype, bs, D):
     """pa_decode_schedule_shared + pa_decode_scheduled_shared through the C ABI on
-    hand-built tables, against the oracle; called three times (counters return
-    to zero, bits repeat) and against pa_decode without groups."""
+    hand-built tables, against the oracle; called eight times (counters return
+    to zero, bits repeat whichever wave merges a row) and against pa_decode
+    without groups."""
     import paged_kv_cache_write_amd as pk
     codes = {"f32": 0, "f16": 1, "bf16": 2}
-    kc, vc, q, tables, ctx, poison = _direct_case(dtype, bs)
+    kc, vc, q, tables, ctx, poison = _direct_case(dtype, bs, D=D)
     H, D = q.shape[1], q.shape[2]
     scale = 1.0 / np.sqrt(D)
-    log(f"case direct-shared {dtype} bs={bs} S={len(ctx)}")
+    log(f"case direct-shared {dtype} bs={bs} D={D} S={len(ctx)}")
     d = pk.decode_schedule_shared(ctx, tables, H, D, bs, codes[dtype], 0)
     assert len(d["groups"]) > 0
     cnts = sorted(set(map(tuple, d["groups"][:, :2].tolist())))
@@ -136,7 +138,7 @@ def test_direct_shared_entry_points(dtype, bs):
     members = torch.from_numpy(d["members"]).cuda()
     ws = torch.zeros(max(d["workspace_bytes"], 16), dtype=torch.uint8, device="cuda")
     outs = []
-    for _ in range(3):
+    for _ in range(8):
         o = pk.decode_scheduled_shared(qd, kd, vd, td, cd, scale, d["max_context_len"], items,
                                        groups, members, d["partition_tokens"], workspace=ws)
         torch.cuda.synchronize()
