@@ -60,10 +60,11 @@ def test_config4_shared_prefix(cow):
 
 @pytest.mark.parametrize("bs", synth.SWEEP_BLOCK_SIZES)
 def test_config5_block_size_sweep(bs):
+    """All 256 sequences x 40 heads compared with the oracle at every block size,
+    through the launch the engine makes for them (4-head workgroups at this size)."""
     synth.cache_draws(True)
     wl = synth.make_workload(5, bs=bs)
-    seqs = sample_seqs(wl.ctx, 24, seed=bs)
-    _check_workload(wl, seqs=seqs)
+    _check_workload(wl)
 
 
 # ------------------------------------------------- every kernel instance

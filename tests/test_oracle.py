@@ -448,9 +448,44 @@ def test_useful_kv_waste_bounded():
     ctx = synth.config5_ctx()
     for bs in synth.SWEEP_BLOCK_SIZES:
         f = oracle.useful_kv_fraction(ctx, bs)
-        alloc = int(((-(-ctx // bs)) * bs).sum())
-        assert alloc - int(ctx.sum()) <= len(ctx) * (bs - 1)
+        # only each sequence's last block may hold empty slots, at most bs - 1 of them
+        # (comfyai.app 6.4.1; brentwoodlivery "5.3.18" waste card)
+        waste_slots = sum(ctx) / f - sum(ctx)
+        assert -1e-6 <= waste_slots <= len(ctx) * (bs - 1) + 1e-6
         assert 0 < f <= 1
+
+
+def test_useful_kv_fraction_hand_worked():
+    """Values worked out by hand: ctx 17, 16 and 40 at block size 16 occupy 2 + 1 + 3
+    blocks = 96 slots for 73 tokens; one token at block size 128 uses 1 of 128 slots;
+    whole blocks waste nothing; block size 1 never wastes."""
+    assert oracle.useful_kv_fraction([17, 16, 40], 16) == 73 / 96
+    assert oracle.useful_kv_fraction([1], 128) == 1 / 128
+    assert oracle.useful_kv_fraction([16, 32, 4096], 16) == 1.0
+    assert oracle.useful_kv_fraction([3, 5, 999], 1) == 1.0
+    # one token past a block boundary opens a whole block: 17 tokens in 32 slots
+    assert oracle.useful_kv_fraction([17], 16) == 17 / 32
+
+
+def test_useful_kv_fraction_matches_block_pool():
+    """The fraction equals tokens held / slots of the blocks BlockPoolModel actually
+    allocated, after random adds and appends (an independent count of the same
+    allocation rule)."""
+    rng = np.random.default_rng(12)
+    for bs in (8, 16, 32):
+        bm = oracle.BlockPoolModel(4096, bs)
+        lens = {}
+        for s in range(40):
+            n = int(rng.integers(1, 300))
+            bm.add_seq(s, n)
+            lens[s] = n
+        for _ in range(500):
+            s = int(rng.integers(40))
+            bm.append_slot(s)
+            lens[s] += 1
+        ctx = [lens[s] for s in range(40)]
+        slots = sum(len(bm.tables[s]) for s in range(40)) * bs
+        assert oracle.useful_kv_fraction(ctx, bs) == sum(ctx) / slots
 
 
 # ------------------------------------------------------- planted mistakes
