@@ -20,6 +20,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "bm_internal.hpp"
 #include "pa.h"
 
 struct SeqState {
@@ -50,12 +51,7 @@ bool pop_free(pa_bm* bm, int32_t* out) {
   return true;
 }
 
-// What one append did, for undoing it: 0 in place, 1 a new block, 2 a copy.
-struct Undo {
-  int64_t seq;
-  int kind;
-  int32_t src, dst;
-};
+using Undo = pa::AppendUndo;
 
 int append_one(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
                int32_t* cow_dst, Undo* undo = nullptr) {
@@ -184,22 +180,29 @@ int pa_bm_append_slot(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
   return append_one(bm, seq, slot, cow_src, cow_dst);
 }
 
-int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n,
-                       int64_t* slots, int32_t* cow_pairs, int32_t* num_cow,
-                       int32_t* num_done) {
+}  // extern "C"
+
+namespace {
+
+// All or nothing: on failure the appends before the failing one are undone
+// and `log` is left empty.
+int append_slots_logged(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots,
+                        int32_t* cow_pairs, int32_t* num_cow, int32_t* num_done,
+                        std::vector<Undo>& log) {
   if (num_done) *num_done = 0;
   if (num_cow) *num_cow = 0;
+  log.clear();
   if (!bm || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)))
     return PA_ERR_INVALID;
   int32_t ncow = 0;
-  std::vector<Undo> log;
   log.reserve(size_t(n));
   for (int32_t i = 0; i < n; ++i) {
     int32_t src = -1, dst = -1;
     Undo u;
     int rc = append_one(bm, seqs[i], &slots[i], &src, &dst, &u);
-    if (rc < 0) {  // all or nothing: the appends before this one are undone
+    if (rc < 0) {
       undo_appends(bm, log);
+      log.clear();
       return rc;
     }
     log.push_back(u);
@@ -212,6 +215,37 @@ int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n,
   if (num_cow) *num_cow = ncow;
   if (num_done) *num_done = n;
   return PA_OK;
+}
+
+}  // namespace
+
+namespace pa {
+
+int bm_step_logged(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots,
+                   int32_t* cow_pairs, int32_t* num_cow, int32_t* tables, int32_t max_blocks,
+                   int32_t pad, int32_t* context_lens, std::vector<AppendUndo>* log) {
+  int32_t done = 0;
+  int rc = append_slots_logged(bm, seqs, n, slots, cow_pairs, num_cow, &done, *log);
+  if (rc != PA_OK) return rc;
+  rc = pa_bm_block_tables(bm, seqs, n, tables, max_blocks, pad, context_lens);
+  if (rc != PA_OK) {  // a table wider than max_blocks: nothing stays changed
+    undo_appends(bm, *log);
+    log->clear();
+  }
+  return rc;
+}
+
+void bm_undo(pa_bm* bm, const std::vector<AppendUndo>& log) { undo_appends(bm, log); }
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n,
+                       int64_t* slots, int32_t* cow_pairs, int32_t* num_cow,
+                       int32_t* num_done) {
+  std::vector<Undo> log;
+  return append_slots_logged(bm, seqs, n, slots, cow_pairs, num_cow, num_done, log);
 }
 
 int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int32_t n,
@@ -234,10 +268,9 @@ int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int32_t n,
 int pa_bm_step(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots,
                int32_t* cow_pairs, int32_t* num_cow, int32_t* tables,
                int32_t max_blocks, int32_t pad, int32_t* context_lens) {
-  int32_t done = 0;
-  int rc = pa_bm_append_slots(bm, seqs, n, slots, cow_pairs, num_cow, &done);
-  if (rc != PA_OK) return rc;
-  return pa_bm_block_tables(bm, seqs, n, tables, max_blocks, pad, context_lens);
+  std::vector<Undo> log;
+  return pa::bm_step_logged(bm, seqs, n, slots, cow_pairs, num_cow, tables, max_blocks, pad,
+                            context_lens, &log);
 }
 
 int pa_bm_select(pa_bm* bm, const int64_t* parents, const int64_t* children, int32_t n,

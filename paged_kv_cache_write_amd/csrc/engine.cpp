@@ -26,6 +26,7 @@
 #include <new>
 #include <vector>
 
+#include "bm_internal.hpp"
 #include "internal.hpp"
 #include "pa.h"
 
@@ -49,6 +50,7 @@ struct pa_engine {
   hipEvent_t ev_start = nullptr, ev_end = nullptr;  // optional: the decode kernel's start / end
   bool sharing = true;  // detect shared prefixes in the tables each step
   pa::HostSchedule hs;
+  std::vector<pa::AppendUndo> undo;  // the block manager's appends of the current step
 };
 
 namespace {
@@ -84,6 +86,8 @@ int pa_engine_create(pa_bm* bm, void* k_cache, void* v_cache, int64_t num_blocks
   if (!bm || !k_cache || !v_cache || !host_staging || !dev_staging || ring <= 0 ||
       num_blocks <= 0 || num_heads <= 0 || max_batch <= 0 || max_blocks_per_seq <= 0)
     return PA_ERR_INVALID;
+  // the decode and the step prologue launch at most 65535 sequences
+  if (max_batch > 65535) return PA_ERR_UNSUPPORTED;
   if (size_t(host_staging) % 16 || size_t(dev_staging) % 16) return PA_ERR_INVALID;
   size_t ws;
   int rc = pa_decode_plan(1, num_heads, head_dim, block_size, 0, dtype, 0, nullptr, nullptr, &ws);
@@ -205,12 +209,38 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
   int32_t* h_tab = reinterpret_cast<int32_t*>(h + off_tab);
 
   // 3. Commit the appends, then schedule from the new tables and lengths.
+  //    From here on a failure undoes the appends (all or nothing).  If some
+  //    of the step's device work was already enqueued, the host slot counts
+  //    as used: it is rewritten only after its guard event, as for a step
+  //    that succeeded.
   int32_t ncow = 0;
-  int rc = pa_bm_step(e->bm, seqs, n, h_slots, h_cow, &ncow, h_tab, e->max_blocks, e->pad, h_ctx);
+  int rc = pa::bm_step_logged(e->bm, seqs, n, h_slots, h_cow, &ncow, h_tab, e->max_blocks, e->pad,
+                              h_ctx, &e->undo);
   if (rc != PA_OK) return rc;
+  bool enqueued = false;
+  auto advance = [&]() -> int {
+    e->unguarded = true;
+    int status = PA_OK;
+    if (slot == guard) {
+      if (hipEventRecord(e->events[slot], st) == hipSuccess) {
+        e->pending[slot] = 1;
+        e->unguarded = false;
+      } else {
+        status = PA_ERR_HIP;
+      }
+    }
+    e->next = (slot + 1) % e->ring;
+    return status;
+  };
+  auto fail = [&](int code) -> int {
+    pa::bm_undo(e->bm, e->undo);
+    e->undo.clear();
+    if (enqueued) (void)advance();
+    return code;
+  };
   rc = pa::build_schedule(h_ctx, n, e->H, e->D, e->bs, e->dtype, partition_tokens,
                           e->sharing ? h_tab : nullptr, e->max_blocks, &e->hs);
-  if (rc != PA_OK) return rc;
+  if (rc != PA_OK) return fail(rc);
   const pa::HostSchedule& hs = e->hs;
   const int32_t n_items = int32_t(hs.items.size() / 5);
   const int32_t n_groups = int32_t(hs.groups.size() / 5);
@@ -232,20 +262,23 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
     rc = pa::launch_step_prologue(hd, d, used, reinterpret_cast<const int64_t*>(hd + off_slots),
                                   k_new, v_new, n, e->k_cache, e->v_cache, e->num_blocks, e->H,
                                   e->D, e->bs, e->dtype, st);
-    if (rc != PA_OK) return rc;
-  } else if (hipMemcpyAsync(d, h, used, hipMemcpyHostToDevice, st) != hipSuccess) {
-    return PA_ERR_HIP;
-  }
-  if (!fused) {
+    enqueued = true;
+    if (rc != PA_OK) return fail(rc);
+  } else {
+    if (hipMemcpyAsync(d, h, used, hipMemcpyHostToDevice, st) != hipSuccess) {
+      enqueued = true;
+      return fail(PA_ERR_HIP);
+    }
+    enqueued = true;
     if (ncow > 0) {
       rc = pa_copy_blocks(e->k_cache, e->v_cache, reinterpret_cast<const int32_t*>(d + off_cow),
                           ncow, e->num_blocks, e->H, e->D, e->bs, e->dtype, stream);
-      if (rc != PA_OK) return rc;
+      if (rc != PA_OK) return fail(rc);
     }
     rc = pa_cache_write(k_new, v_new, reinterpret_cast<const int64_t*>(d + off_slots), n,
                         e->k_cache, e->v_cache, e->num_blocks, e->H, e->D, e->bs, e->dtype,
                         stream);
-    if (rc != PA_OK) return rc;
+    if (rc != PA_OK) return fail(rc);
   }
   const int32_t* d_tab = reinterpret_cast<const int32_t*>(d + off_tab);
   const int32_t* d_ctx = reinterpret_cast<const int32_t*>(d + off_ctx);
@@ -261,17 +294,12 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
                                   n_groups ? reinterpret_cast<const int32_t*>(d + off_members)
                                            : nullptr,
                                   e->ev_start, e->ev_end);
-  if (rc != PA_OK) return rc;
+  if (rc != PA_OK) return fail(rc);
+  e->undo.clear();
   // The host slots of this group may be rewritten once this step has run
   // (recorded at the end of the group's last step: no marker between the
   // prologue and the decode, and none after the group's other steps).
-  e->unguarded = true;
-  if (slot == guard) {
-    if (hipEventRecord(e->events[slot], st) != hipSuccess) return PA_ERR_HIP;
-    e->pending[slot] = 1;
-    e->unguarded = false;
-  }
-  e->next = (slot + 1) % e->ring;
+  rc = advance();
   if (info) {
     info->num_cow = ncow;
     info->max_context_len = max_ctx;
@@ -282,7 +310,9 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
     for (int32_t i = 0; i < n; ++i) sum += h_ctx[i];
     info->sum_context_len = sum;
   }
-  return PA_OK;
+  // a failed guard record leaves the step done (the decode is enqueued); the
+  // host slot then waits for the next guard event
+  return rc;
 }
 
 int pa_engine_set_sharing(pa_engine* e, int32_t enable) {

@@ -5,8 +5,12 @@
 // through the ABI alone: a block's reference count equals the number of
 // table entries naming it, free + referenced blocks = the pool, a failed
 // call changes nothing, and blocks_needed predicts what an append takes.
+// Engine steps are also undone through the library-internal undo log (what
+// the engine does when a launch after the appends fails): the state,
+// free-list order included, must be exactly as before.
 // Exit status 0 = all checks held (the sanitizers abort on any memory or UB
 // error).
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -16,6 +20,7 @@
 #include <string>
 #include <vector>
 
+#include "bm_internal.hpp"
 #include "pa.h"
 
 namespace {
@@ -32,9 +37,10 @@ struct Snapshot {
   int64_t free_dev = 0, free_host = 0, seqs = 0;
   std::map<int64_t, std::vector<int32_t>> tables;
   std::map<int64_t, int64_t> lens;
+  std::vector<int32_t> free_list;
   bool operator==(const Snapshot& o) const {
     return free_dev == o.free_dev && free_host == o.free_host && seqs == o.seqs &&
-           tables == o.tables && lens == o.lens;
+           tables == o.tables && lens == o.lens && free_list == o.free_list;
   }
 };
 
@@ -43,6 +49,8 @@ Snapshot snap(pa_bm* bm, const std::set<int64_t>& live) {
   s.free_dev = pa_bm_num_free(bm);
   s.free_host = pa_bm_num_free_host(bm);
   s.seqs = pa_bm_num_seqs(bm);
+  s.free_list.resize(size_t(s.free_dev) + 1);
+  s.free_list.resize(size_t(pa_bm_free_list(bm, s.free_list.data(), int64_t(s.free_list.size()))));
   for (int64_t q : live) {
     int32_t n = 0;
     std::vector<int32_t> t(kTableCap);
@@ -226,11 +234,38 @@ int main(int argc, char** argv) {
         std::vector<int32_t> cow(2 * seqs.size()), tables(seqs.size() * kTableCap),
             lens(seqs.size());
         int32_t ncow = 0;
-        rc = pa_bm_step(bm, seqs.data(), int32_t(seqs.size()), slots.data(), cow.data(), &ncow,
-                        tables.data(), kTableCap, -1, lens.data());
-        seen[rc == PA_OK ? "step" : "step_full"]++;
-        if (rc == PA_ERR_NO_BLOCKS) changed = false;
-        else if (rc != PA_OK) fail("step status", step);
+        const int kind = int(pick(4));
+        if (kind == 0) {  // a step whose later launch fails: the engine undoes it
+          std::vector<pa::AppendUndo> log;
+          rc = pa::bm_step_logged(bm, seqs.data(), int32_t(seqs.size()), slots.data(), cow.data(),
+                                  &ncow, tables.data(), kTableCap, -1, lens.data(), &log);
+          if (rc == PA_OK) {
+            if (log.size() != seqs.size()) fail("undo log length", step);
+            pa::bm_undo(bm, log);
+            seen["step_undone"]++;
+          } else if (rc == PA_ERR_NO_BLOCKS) {
+            if (!log.empty()) fail("log of a failed step", step);
+            seen["step_full"]++;
+          } else {
+            fail("logged step status", step);
+          }
+          changed = false;
+        } else if (kind == 1) {  // tables wider than the caller's rows: nothing changes
+          rc = pa_bm_step(bm, seqs.data(), int32_t(seqs.size()), slots.data(), cow.data(), &ncow,
+                          tables.data(), 1, -1, lens.data());
+          int64_t longest = 0;
+          for (int64_t q : seqs) longest = std::max(longest, pa_bm_seq_len(bm, q));
+          if (rc == PA_ERR_CAPACITY) seen["step_capacity"]++;
+          else if (rc == PA_OK && longest <= bs) seen["step"]++;
+          else if (rc == PA_OK || rc != PA_ERR_NO_BLOCKS) fail("narrow step status", step);
+          changed = rc != PA_OK ? false : true;
+        } else {
+          rc = pa_bm_step(bm, seqs.data(), int32_t(seqs.size()), slots.data(), cow.data(), &ncow,
+                          tables.data(), kTableCap, -1, lens.data());
+          seen[rc == PA_OK ? "step" : "step_full"]++;
+          if (rc == PA_ERR_NO_BLOCKS) changed = false;
+          else if (rc != PA_OK) fail("step status", step);
+        }
       }
     }
     if (!changed && !(snap(bm, live) == before)) fail("a failed call changed the state", step);

@@ -112,3 +112,22 @@ def test_engine_staging_and_errors():
     h = ctypes.c_void_p()
     assert lib.pa_engine_create(None, None, None, 1, 1, 128, 16, 1, 1, 1, 0, None, 1, None,
                                 ctypes.byref(h)) == -1
+
+
+def test_engine_rejects_batches_the_launches_cannot_hold():
+    """More than 65535 sequences per step cannot be launched: pa_engine_create says
+    so up front (no GPU call is made before that check), so no step can fail after
+    its appends for that reason."""
+    import ctypes
+    import paged_kv_cache_write_amd as pk
+    lib = pk.lib()
+    bm = ctypes.c_void_p()
+    assert lib.pa_bm_create(64, 16, None, 0, ctypes.byref(bm)) == 0
+    try:
+        h = ctypes.c_void_p()
+        fake = 256                                     # aligned stand-ins, never dereferenced
+        assert lib.pa_engine_create(bm, fake, fake, 64, 4, 128, 16, 1, 65536, 4, 0, fake, 2,
+                                    fake, ctypes.byref(h)) == -2
+        assert not h.value
+    finally:
+        lib.pa_bm_destroy(bm)

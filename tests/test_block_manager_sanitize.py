@@ -20,7 +20,8 @@ def test_block_manager_under_sanitizers(tmp_path):
            os.path.join(ROOT, "paged_kv_cache_write_amd", "csrc", "block_manager.cpp")]
     cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
-           "-I", os.path.join(ROOT, "include"), *src, "-o", exe]
+           "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "paged_kv_cache_write_amd", "csrc"), *src, "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
@@ -32,5 +33,5 @@ def test_block_manager_under_sanitizers(tmp_path):
     counts = dict(line.split() for line in r.stdout.splitlines()[1:])
     for outcome in ("add", "add_full", "fork", "append", "append_cow", "append_full", "free",
                     "free_swapped", "select", "swap_out", "swap_out_refused", "swap_in", "step",
-                    "step_full"):
+                    "step_full", "step_undone", "step_capacity"):
         assert int(counts.get(outcome, 0)) > 0, (outcome, counts)
