@@ -19,6 +19,7 @@ __all__ = [
     "decode_scheduled", "decode_schedule_shared", "decode_scheduled_shared", "stream_read",
     "decode_contiguous", "copy_blocks_between", "prefill",
     "debug_status", "use_debug_library", "PA_DEBUG_TABLE", "PA_DEBUG_SLOT", "PA_DEBUG_PAIR",
+    "PA_DEBUG_ITEM",
     "BlockManager",
     "DTYPE_CODES", "LIB_PATH",
 ]
@@ -33,6 +34,7 @@ _USE_DEBUG = False
 PA_DEBUG_TABLE = 1
 PA_DEBUG_SLOT = 2
 PA_DEBUG_PAIR = 4
+PA_DEBUG_ITEM = 8
 
 PA_OK = 0
 PA_ERR_NO_BLOCKS = -4

@@ -112,6 +112,7 @@ struct DecodeParams {
   bool contig;
   int64_t stride_s, stride_t, stride_h, max_tokens;
   int64_t num_blocks;  // pool size (checked against table entries in debug builds)
+  int num_seqs;        // sequences of the launch (checked against work items in debug builds)
   int64_t ws_o_bytes;  // bytes of the ws_o region
   int num_group_wgs;   // decode_shared_kernel: workgroups of the group items
 };
@@ -453,7 +454,9 @@ __device__ __forceinline__ void finish(const DecodeParams& P, const size_t (&row
 #pragma unroll
   for (int g = 0; g < NQ; ++g) {
     if (g >= nq) break;
-    const float inv = 1.0f / l[g];  // l >= 1: the running max token contributes 2^0
+    // l >= 1 after any token (the running max token contributes 2^0); l = 0
+    // for a group item that streamed nothing (its partial has weight zero)
+    const float inv = l[g] > 0.f ? 1.0f / l[g] : 0.f;
     if (nparts[g] <= 1) {
       if (row == 0) {
         T* o = reinterpret_cast<T*>(P.out) + row_id[g] * D + col * kVec;
@@ -591,6 +594,16 @@ __device__ __forceinline__ void wave_body(DecodeParams P, uint3 block) {
     s = it[0];
     part = it[1];
     t0 = it[2];
+#ifdef PA_DEBUG
+    // an item outside the launch (sequence), the workspace (partition index
+    // and count) or the table window (first token, tokens) does nothing
+    const int nt = it[3], np = it[4];
+    if (s < 0 || s >= P.num_seqs || part < 0 || t0 < 0 || nt < 0 || nt > P.window_tokens ||
+        np < 0 || np > P.max_parts || (np > 0 && part >= np) || (nt > 0 && np == 0)) {
+      if (threadIdx.x == 0) debug_flag(PA_DEBUG_ITEM);
+      return;
+    }
+#endif
   } else {
     hg = block.x;
     part = block.y;
@@ -713,11 +726,22 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeParams P) 
   const int part = it[2];
   const int t0 = it[3];
   const int ntok = it[4];
+  // A group item is one whole shared partition of 1..kGroup members.  Any
+  // other item streams nothing; if its partition index exists, each member
+  // still stores a partial of weight zero there and counts it (as the
+  // matrix-core group kernel does).
+  const bool part_ok = part >= 0 && part < P.max_parts;
+  const bool stream = part_ok && it[1] >= 1 && it[1] <= kGroup && ntok == kSharedPartTokens &&
+                      t0 >= 0;
+  if (!stream) {
+    if (threadIdx.x == 0) debug_flag(PA_DEBUG_ITEM);
+    if (!part_ok || nq <= 0) return;
+  }
+  const int ntok_s = stream ? ntok : 0;
   const int32_t* mem = P.group_members + kMemberInts * moff;
-  ChunkCtx cx = make_ctx<DT, D, U>(P, mem[0], h, t0, lane);
-  if (ntok <= 0 || nq <= 0) return;
-  cx.ntok = ntok;
-  cx.last_group = (ntok - 1) & ~(Sh::kTPI - 1);
+  ChunkCtx cx = make_ctx<DT, D, U>(P, mem[0], h, stream ? t0 : 0, lane);
+  cx.ntok = ntok_s;
+  cx.last_group = (max(ntok_s, 1) - 1) & ~(Sh::kTPI - 1);
   const int col = lane % Sh::kLPT;
 
   size_t rows[kGroup];
@@ -735,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeParams P) 
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc[g][e] = 0.f;
   }
-  const int nfull = ntok / Sh::kChunk;
+  const int nfull = ntok_s / Sh::kChunk;
   int c = 0;
   for (; c < nfull; ++c) {
     u32x4 kr[U], vr[U];
@@ -745,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeParams P) 
     for (int g = 0; g < kGroup; ++g)
       if (g < nq) chunk_apply<DT, D, U, false>(cx, kr, vr, ok, qv[g], m[g], l[g], acc[g]);
   }
-  if (c * Sh::kChunk < ntok) {
+  if (c * Sh::kChunk < ntok_s) {
     u32x4 kr[U], vr[U];
     bool ok[U];
     chunk_load<DT, D, U, true>(cx, c * Sh::kChunk, kr, vr, ok);
@@ -796,8 +820,17 @@ __device__ __forceinline__ void group_mfma_body(DecodeParams P, unsigned block_x
   const int part = it[2];
   const int t0 = it[3];
   const int ntok = it[4];
-  // a group item is always one whole shared partition
-  if (nq <= 0 || ntok != kSharedPartTokens) return;
+  // A group item is one whole shared partition of 1..kGroupMfma members.
+  // Any other item streams nothing; if its partition index exists, each
+  // member still stores a partial of weight zero there and counts it, so the
+  // rows complete and the counters return to zero.
+  const bool part_ok = part >= 0 && part < P.max_parts;
+  const bool stream = part_ok && it[1] >= 1 && it[1] <= kGroupMfma &&
+                      ntok == kSharedPartTokens && t0 >= 0;
+  if (!stream) {
+    if (lane == 0) debug_flag(PA_DEBUG_ITEM);
+    if (!part_ok || nq <= 0) return;
+  }
   const int32_t* mem = P.group_members + kMemberInts * moff;
   const int qi = lane & 15;  // this lane's query (B column, output column)
   const int g = lane >> 4;   // this lane's k / row group
@@ -812,7 +845,7 @@ __device__ __forceinline__ void group_mfma_body(DecodeParams P, unsigned block_x
   const int log2_tile = kLog2Row + log2_bs;
   const int blk0 = t0 >> log2_bs;
   int tbl = 0;
-  if (lane < (kSharedPartTokens >> log2_bs) && blk0 + lane < P.maxB) {
+  if (stream && lane < (kSharedPartTokens >> log2_bs) && blk0 + lane < P.maxB) {
     tbl = P.block_tables[size_t(mem[0]) * P.maxB + blk0 + lane];
     if (debug_bad(tbl, P.num_blocks, PA_DEBUG_TABLE)) tbl = 0;  // every entry is used
   }
@@ -926,23 +959,27 @@ __device__ __forceinline__ void group_mfma_body(DecodeParams P, unsigned block_x
   // counts are exact (a conditional issue would make it wait for everything
   // at the join).
   constexpr int kSteps = kSharedPartTokens / 32;
-  KStep ks[2];
-  VStep vs[2];
-  issue_k(ks[0], 0);
-  issue_v(vs[0], 0);
+  if (stream) {  // wave-uniform
+    KStep ks[2];
+    VStep vs[2];
+    issue_k(ks[0], 0);
+    issue_v(vs[0], 0);
 #pragma unroll
-  for (int c = 0; c < kSteps; ++c) {
-    if (c + 1 < kSteps) issue_k(ks[(c + 1) & 1], c + 1);
-    f32x4 sc[2];
-    qk(ks[c & 1], sc);
-    if (c + 1 < kSteps) issue_v(vs[(c + 1) & 1], c + 1);
-    softmax_pv(sc, vs[c & 1]);
+    for (int c = 0; c < kSteps; ++c) {
+      if (c + 1 < kSteps) issue_k(ks[(c + 1) & 1], c + 1);
+      f32x4 sc[2];
+      qk(ks[c & 1], sc);
+      if (c + 1 < kSteps) issue_v(vs[(c + 1) & 1], c + 1);
+      softmax_pv(sc, vs[c & 1]);
+    }
   }
 
   // the four lanes of a query hold partial sums over their token rows
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
-  const float inv = 1.0f / l;  // l >= 1: the maximum token contributes 2^(max - m) >= 1
+  // l >= 1 after streaming (the maximum token contributes 2^(max - m) >= 1);
+  // l = 0 for an item that streamed nothing (its partial has weight zero)
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
   const bool split = nparts_q > 1;
   if (has_q && !split) {
     T* out = reinterpret_cast<T*>(P.out) + row_q * D;
@@ -1298,6 +1335,7 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.stride_h = cg.stride_h;
   p.max_tokens = cg.max_tokens;
   p.num_blocks = NB;
+  p.num_seqs = S;
   p.ws_o_bytes = split ? int64_t(S) * H * plan.max_parts * D * int64_t(sizeof(float)) : 0;
   p.num_group_wgs = 0;
   if (shared && !p.counters) return PA_ERR_INVALID;  // groups need the one-launch merge

@@ -184,6 +184,8 @@ __device__ __forceinline__ bool debug_bad(int64_t v, int64_t n, uint32_t bit) {
   atomicOr(&pa_debug_word, bit);
   return true;
 }
+// Report `bit` (a check that does not guard an address).
+__device__ __forceinline__ void debug_flag(uint32_t bit) { atomicOr(&pa_debug_word, bit); }
 // The error word of this translation unit, then cleared (host; synchronous).
 static inline uint32_t debug_take_word() {
   uint32_t w = 0, zero = 0;
@@ -193,6 +195,7 @@ static inline uint32_t debug_take_word() {
 }
 #else
 __device__ __forceinline__ bool debug_bad(int64_t, int64_t, uint32_t) { return false; }
+__device__ __forceinline__ void debug_flag(uint32_t) {}
 static inline uint32_t debug_take_word() { return 0; }
 #endif
 

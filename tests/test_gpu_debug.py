@@ -181,3 +181,82 @@ def test_debug_prefill_table_entry(pk_debug):
     rows0 = torch.arange(int(cu_q[0]), int(cu_q[1]), device="cuda")
     compare_outputs(out[rows0], ref[cu_q[0]:cu_q[1]], what="debug prefill bad",
                     cast_dtype="f16")
+
+
+@pytest.mark.parametrize("debug", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_malformed_group_item_keeps_counters(debug, dtype):
+    """A shared-prefix group item whose token count is not one whole 256-token
+    partition streams nothing: each member gets a partial of weight zero at the
+    item's partition, every row still completes, and the row counters return to
+    zero, so the next call with the builder's lists on the same workspace gives
+    the bits of a call on a fresh one.  The debug build also reports
+    PA_DEBUG_ITEM; every kernel exits normally in both builds."""
+    import paged_kv_cache_write_amd as pk
+    from test_gpu_shared import _direct_case
+    prev = pk.use_debug_library(debug)
+    try:
+        pk.debug_status()
+        codes = {"f32": 0, "f16": 1, "bf16": 2}
+        kc, vc, q, tables, ctx, poison = _direct_case(dtype, 16)
+        H, D = q.shape[1], q.shape[2]
+        scale = 1.0 / np.sqrt(D)
+        d = pk.decode_schedule_shared(ctx, tables, H, D, 16, codes[dtype], 0)
+        assert len(d["groups"]) > 1
+        log(f"case malformed group item {dtype} debug={debug}: {len(d['groups'])} group items")
+        kd, vd, qd = to_dev(kc, dtype), to_dev(vc, dtype), to_dev(q, dtype)
+        td, cd = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+        items = torch.from_numpy(d["items"]).cuda()
+        members = torch.from_numpy(d["members"]).cuda()
+        good = torch.from_numpy(d["groups"]).cuda()
+        bad_h = d["groups"].copy()
+        bad_h[0, 4] = 128                       # half a shared partition
+        bad = torch.from_numpy(bad_h).cuda()
+        run = lambda groups, ws: pk.decode_scheduled_shared(
+            qd, kd, vd, td, cd, scale, d["max_context_len"], items, groups, members,
+            d["partition_tokens"], workspace=ws)
+        nbytes = max(d["workspace_bytes"], 16)
+        fresh = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        ref = bits(run(good, fresh))
+        torch.cuda.synchronize()
+        assert pk.debug_status() == 0
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        o = run(bad, ws)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(o.float()).all())
+        assert int(ws[: len(ctx) * H * 4].view(torch.int32).abs().sum().item()) == 0
+        assert pk.debug_status() == (pk.PA_DEBUG_ITEM if debug else 0)
+        again = bits(run(good, ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(again, ref)
+        assert pk.debug_status() == 0
+    finally:
+        pk.use_debug_library(prev)
+
+
+def test_debug_flags_single_item_outside_workspace(pk_debug):
+    """Debug build: a single work item whose partition index lies past the
+    workspace does nothing (no store) and sets PA_DEBUG_ITEM; after the workspace
+    is zero-filled again, the builder's list gives the reference bits.  (A release
+    build trusts the list: this case runs on the debug build only.)"""
+    pk = pk_debug
+    kc, vc, q, tables, ctx = _case()
+    scale = 1 / np.sqrt(q.shape[2])
+    items_h, pt, mx = pk.decode_schedule(ctx, 4, 128, 16, 1, 256)
+    kd, vd, qd = to_dev(kc, "f16"), to_dev(vc, "f16"), to_dev(q, "f16")
+    td, cd = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+    nbytes = max(pk.decode_workspace_size(len(ctx), 4, 128, 16, mx, 1, pt), 16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    items = torch.from_numpy(items_h).cuda()
+    ref = bits(pk.decode_scheduled(qd, kd, vd, td, cd, scale, mx, items, pt, workspace=ws))
+    torch.cuda.synchronize()
+    assert pk.debug_status() == 0
+    bad_h = items_h.copy()
+    bad_h[0, 1] = 1 << 20                        # partition index far past the workspace
+    pk.decode_scheduled(qd, kd, vd, td, cd, scale, mx, torch.from_numpy(bad_h).cuda(), pt,
+                        workspace=ws)
+    assert pk.debug_status() == pk.PA_DEBUG_ITEM
+    ws.zero_()
+    again = bits(pk.decode_scheduled(qd, kd, vd, td, cd, scale, mx, items, pt, workspace=ws))
+    torch.cuda.synchronize()
+    assert np.array_equal(again, ref)
