@@ -53,13 +53,7 @@
 
 namespace pa {
 
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 1
-#endif
-#ifndef PA_DECODE_UNROLL
-#define PA_DECODE_UNROLL 8
-#endif
-constexpr int kWaves = PA_DECODE_WAVES;  // waves per workgroup
+constexpr int kWaves = 1;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 // Scheduled launches of at least this many waves (several rounds of the
 // wave slots) use workgroups of kWideWaves consecutive heads: their waves
@@ -68,14 +62,11 @@ constexpr int kThreads = kWaves * kWave;
 // workgroups spread unevenly over the CUs).
 constexpr int64_t kWideLaunchWaves = 8192;
 constexpr int kWideWaves = 4;
-constexpr int kUnroll = PA_DECODE_UNROLL;  // 16-byte K loads (and V loads) per lane per chunk
+constexpr int kUnroll = 8;   // 16-byte K loads (and V loads) per lane per chunk
 constexpr int kGroup = 8;                  // queries per group wave (float32, vector ALU)
 constexpr int kGroupMfma = 16;             // queries per group wave on the matrix cores
 constexpr int kGroupUnroll = 4;            // chunk of a group wave (register budget)
-#ifndef PA_SHARED_PART_TOKENS
-#define PA_SHARED_PART_TOKENS 256
-#endif
-constexpr int kSharedPartTokens = PA_SHARED_PART_TOKENS;  // partition of a shared range
+constexpr int kSharedPartTokens = 256;  // partition of a shared range
 constexpr float kGroupSlack = 8.0f;  // lazy rescale threshold of the group waves, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so max - max never is NaN
@@ -144,22 +135,14 @@ __device__ __forceinline__ u32x4 load16(const char* p) {
 // K/V are read exactly once per decode: non-temporal loads keep them from
 // displacing reusable lines (measured ~15% faster on the 13B-layer shape).
 __device__ __forceinline__ u32x4 load_stream(const char* p) {
-#ifdef PA_TEMPORAL_LOADS
-  return *reinterpret_cast<const u32x4*>(p);
-#else
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#endif
 }
 
 // Loads of the matrix-core group kernel: each K line is read by two load
-// instructions (half a row each), so these default to ordinary loads.
+// instructions (half a row each), so these are ordinary (temporal) loads.
 template <class V>
 __device__ __forceinline__ V group_load(const char* p) {
-#ifdef PA_GROUP_NT_LOADS
-  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
-#else
   return *reinterpret_cast<const V*>(p);
-#endif
 }
 
 // Per-wave state for streaming one partition's chunks.
@@ -432,13 +415,32 @@ __device__ __forceinline__ void merge_partials_grouped(const DecodeParams& P, si
 // End of a (row, partition) for the NQ queries of one wave (rows row_id[g],
 // nparts[g]; the wave's token rows are already merged).  A row with one
 // partition is stored directly.  Otherwise the partial goes to the
-// workspace; in the one-launch form the partials are then counted: the
-// partial stores are complete (s_waitcnt) before the counter increments are
-// issued, and the wave whose increment returns the count of all the others
-// merges that row (after its increment returned, so every partial is
-// visible) and resets its counter.  Partials and counters are exchanged only
-// through agent-scope atomic accesses, coherent across the XCDs' L2s without
-// cache-wide write-back/invalidate fences.
+// workspace; in the one-launch form the partials are then counted, and the
+// wave whose increment returns the count of all the others merges the row
+// and resets its counter.
+//
+// Why the merging wave sees every partial (AMDGPU memory model for
+// gfx942/gfx950, where each XCD has its own L2 and device-scope coherence is
+// chosen per instruction by its scope bits):
+//  1. Partials are relaxed atomic stores at agent scope, which compile to
+//     stores with the device scope bit (sc1): they are written through the
+//     XCD's L2 to the device's point of coherence.
+//  2. s_waitcnt vmcnt(0) returns only once those stores are complete, i.e.
+//     performed at device scope; only then is the counter increment (a
+//     device-scope atomic, sc1, performed at the point of coherence) issued.
+//  3. The increments of one counter are totally ordered at that point.  The
+//     wave that reads count = nparts - 1 comes after every other increment,
+//     and so after every other wave's partial stores were performed.
+//  4. The merging wave issues its partial loads only after its increment
+//     has returned (they sit behind a branch on the returned value, which
+//     waits for it; in-order issue), and they are relaxed atomic loads at
+//     agent scope (sc1): they miss the CU's L1 and any stale L2 line and
+//     read the point of coherence, where step 3's stores already are.
+// The signal fences keep the compiler from moving memory accesses across
+// the wait and the branch.  In C++ terms the accesses are relaxed; the
+// release/acquire form would compile to a write-back of the whole L2 at each
+// producer and an invalidate at the consumer (buffer_wbl2 / buffer_inv),
+// which measured about 3x slower for this launch.
 template <class DT, int D, int U, int NQ>
 __device__ __forceinline__ void finish(const DecodeParams& P, const size_t (&row_id)[NQ],
                                        const int (&nparts)[NQ], int nq, int part,
@@ -1038,6 +1040,10 @@ __device__ __forceinline__ void group_mfma_body(DecodeParams P, unsigned block_x
       __hip_atomic_store(P.ws_ml + 2 * pi + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  // Count the rows, then merge the ones this wave completes: the same
+  // ordering argument as in finish() (device-scope partial stores complete
+  // before the device-scope increment; merge loads at device scope after the
+  // increment returned).
   if (!P.counters) return;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // all counters zero: this wave's stores are complete
