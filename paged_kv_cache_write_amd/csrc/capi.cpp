@@ -27,7 +27,7 @@ int pa_debug_status(void* stream) {
   if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_HIP;
   const uint32_t w = pa::debug_take_decode() | pa::debug_take_prefill() | pa::debug_take_cache_ops();
   if (w == ~0u) return PA_ERR_HIP;  // a symbol copy failed
-  return int(w & (PA_DEBUG_TABLE | PA_DEBUG_SLOT | PA_DEBUG_PAIR));
+  return int(w & (PA_DEBUG_TABLE | PA_DEBUG_SLOT | PA_DEBUG_PAIR | PA_DEBUG_ITEM));
 }
 
 int pa_debug_enabled(void) {
