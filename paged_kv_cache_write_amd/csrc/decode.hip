@@ -1135,11 +1135,15 @@ struct Plan {
   size_t ws_bytes;
 };
 
-// Workspace: [S*H int32 counters, padded to 256 B][S*H*P*2 float (max, sum), padded to
-// 16 B][S*H*P*D float]
-static size_t counter_bytes(int32_t S, int32_t H) {
-  return (size_t(S) * H * sizeof(int) + 255) & ~size_t(255);
+// Workspace: [R int32 counters, padded to 256 B][S*H*P*2 float (max, sum), padded to
+// 16 B][S*H*P*D float], with R = S*H rows, or more when the caller reserves a
+// counter region that does not depend on the call (the engine: its largest
+// batch; the no-allocation entry point: a fixed prefix of its array), so that
+// no call's partials ever lie where a later, larger call's counters are.
+static size_t counter_bytes_rows(int64_t rows) {
+  return (size_t(rows) * sizeof(int) + 255) & ~size_t(255);
 }
+static size_t counter_bytes(int32_t S, int32_t H) { return counter_bytes_rows(int64_t(S) * H); }
 
 // (max, sum) floats of all partials, padded so the outputs start 16-byte aligned
 static size_t ml_floats(int32_t S, int32_t H, int max_parts) {
@@ -1272,6 +1276,7 @@ struct Schedule {
   int32_t num_group_items = 0;
   const int32_t* group_members = nullptr;
   Timing timing;  // optional: recorded at the start of the first and the end of the last launch
+  int64_t counter_rows = 0;  // counters reserved at the workspace start (0: S*H of the call)
 };
 
 static int decode_impl(int what, const void* q, const void* k_cache, const void* v_cache,
@@ -1309,8 +1314,12 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return PA_ERR_INVALID;
   if (shared && (kSharedPartTokens % bs != 0 || !sched.group_members)) return PA_ERR_INVALID;
-  if (plan.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE;
+  // counters first (the reserved region, at least one per row), then the partials
+  const bool split = plan.ws_bytes > 0;
+  const size_t cbytes = counter_bytes_rows(std::max<int64_t>(int64_t(S) * H, sched.counter_rows));
+  const size_t ws_need = split ? plan.ws_bytes - counter_bytes(S, H) + cbytes : 0;
+  if (split) {
+    if (!workspace || workspace_bytes < ws_need) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_INVALID;
   }
   DecodeParams p;
@@ -1321,9 +1330,8 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.context_lens = context_lens;
   p.out = out;
   char* ws = reinterpret_cast<char*>(workspace);
-  const bool split = plan.ws_bytes > 0;
   p.counters = (split && (what & kFused)) ? reinterpret_cast<int*>(ws) : nullptr;
-  p.ws_ml = split ? reinterpret_cast<float*>(ws + counter_bytes(S, H)) : nullptr;
+  p.ws_ml = split ? reinterpret_cast<float*>(ws + cbytes) : nullptr;
   p.ws_o = split ? p.ws_ml + ml_floats(S, H, plan.max_parts) : nullptr;
   p.items = sched.items;
   p.group_items = sched.group_items;
@@ -1539,7 +1547,7 @@ int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cac
                            size_t workspace_bytes, int32_t partition_tokens, void* stream,
                            const int32_t* items, int32_t num_items, const int32_t* group_items,
                            int32_t num_group_items, const int32_t* members, hipEvent_t start,
-                           hipEvent_t stop) {
+                           hipEvent_t stop, int64_t counter_rows) {
   if (num_seqs > 0 && ((num_items > 0 && !items) || num_items < 0 || num_group_items < 0 ||
                        (num_group_items > 0 && (!group_items || !members)) ||
                        num_items + num_group_items <= 0))
@@ -1553,6 +1561,7 @@ int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cac
   sc.group_members = members;
   sc.timing.start = start;
   sc.timing.stop = stop;
+  sc.counter_rows = counter_rows;
   return decode_impl(kDoPartitions | kDoReduce | kFused, q, k_cache, v_cache, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, num_heads, head_dim,
                      block_size, num_blocks, scale, max_context_len, dtype, out, workspace,
@@ -1656,14 +1665,14 @@ int pa_decode_reduce(PA_DECODE_ARGS) { return pa::decode_impl(pa::kDoReduce, PA_
 int pa_decode_scheduled(PA_DECODE_ARGS, const int32_t* items, int32_t num_items) {
   if (num_seqs > 0 && (!items || num_items <= 0)) return PA_ERR_INVALID;
   return pa::decode_scheduled_timed(PA_DECODE_PASS, items, num_items, nullptr, 0, nullptr,
-                                    nullptr, nullptr);
+                                    nullptr, nullptr, 0);
 }
 
 int pa_decode_scheduled_shared(PA_DECODE_ARGS, const int32_t* items, int32_t num_items,
                                const int32_t* group_items, int32_t num_group_items,
                                const int32_t* members) {
   return pa::decode_scheduled_timed(PA_DECODE_PASS, items, num_items, group_items,
-                                    num_group_items, members, nullptr, nullptr);
+                                    num_group_items, members, nullptr, nullptr, 0);
 }
 
 // Contiguous (non-paged) K/V: the same decode with token rows addressed by

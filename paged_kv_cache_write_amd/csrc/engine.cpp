@@ -293,7 +293,7 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
                                   n_groups,
                                   n_groups ? reinterpret_cast<const int32_t*>(d + off_members)
                                            : nullptr,
-                                  e->ev_start, e->ev_end);
+                                  e->ev_start, e->ev_end, int64_t(e->max_batch) * e->H);
   if (rc != PA_OK) return fail(rc);
   e->undo.clear();
   // The host slots of this group may be rewritten once this step has run

@@ -40,7 +40,10 @@ int launch_step_prologue(const void* host_src, void* dev_dst, size_t copy_bytes,
 
 // pa_decode_scheduled (num_group_items == 0) or pa_decode_scheduled_shared,
 // with optional HIP events recorded by the dispatch itself at the start of
-// the decode's first kernel and the end of its last (no marker packets).
+// the decode's first kernel and the end of its last (no marker packets), and
+// counter_rows row counters reserved at the start of the workspace (0: one
+// per row of this call; the engine reserves its largest batch's rows, so the
+// counters stay in place when the batch grows).
 int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
@@ -49,7 +52,7 @@ int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cac
                            size_t workspace_bytes, int32_t partition_tokens, void* stream,
                            const int32_t* items, int32_t num_items, const int32_t* group_items,
                            int32_t num_group_items, const int32_t* members, hipEvent_t start,
-                           hipEvent_t stop);
+                           hipEvent_t stop, int64_t counter_rows);
 
 // Device error words of the translation units with kernels (debug builds:
 // table entries, slots and copy pairs out of range; release builds: 0), each

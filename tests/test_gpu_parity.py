@@ -397,3 +397,40 @@ def test_wide_workgroup_launch(dtype, D, H, bs):
     assert info.num_items * H >= 8192, "the launch should be wide"
     log(f"wide launch: {info.num_items} items x {H} heads, partitions of "
         f"{info.partition_tokens} tokens")
+
+
+def test_engine_batch_grows_between_steps():
+    """Steps over 3, then 8, then 5, then 8 sequences of long (split) contexts on
+    one engine and one workspace.  The engine reserves its workspace counters for
+    its largest batch, so the partials a small step leaves never sit where a
+    larger step's counters are.  Each step's output is compared with the oracle's
+    decode of the engine's own pool and tables after that step."""
+    from paged_kv_cache_write_amd.engine import PagedKVEngine
+    synth.cache_draws(False)
+    ctx0 = [1500, 2900, 700, 2200, 3000, 1800, 999, 2500]
+    wl = synth.make_custom(781, 40, 128, "f16", 16, ctx0)
+    extra = 4
+    NB = wl.NB + len(ctx0) * extra
+    free_order = np.concatenate([wl.free_order, np.arange(wl.NB, NB, dtype=np.int32)])
+    eng = PagedKVEngine(NB, wl.H, wl.D, wl.bs, torch.float16, wl.max_blocks_per_seq + extra,
+                        len(ctx0), free_order=free_order, pad_block=wl.poison_block,
+                        fill=float("nan"))
+    for op in wl.ops:
+        if op[0] == "add":
+            k, v = wl.kv(op[1], 0, op[2])
+            eng.add_sequence(op[1], to_dev(k, wl.dtype), to_dev(v, wl.dtype))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(781)
+    for step, seqs in enumerate([[0, 1, 2], list(range(8)), [3, 4, 5, 6, 7], list(range(8))]):
+        log(f"case growing batch: step {step}, {len(seqs)} sequences")
+        n = len(seqs)
+        q = torch.randn(n, wl.H, wl.D, device="cuda", generator=gen).half()
+        k_new = torch.randn(n, wl.H, wl.D, device="cuda", generator=gen).half()
+        v_new = torch.randn(n, wl.H, wl.D, device="cuda", generator=gen).half()
+        out = eng.step(np.array(seqs, dtype=np.int64), q, k_new, v_new, wl.scale)
+        torch.cuda.synchronize()
+        assert eng.last_info.partition_tokens < 3000        # the long rows are split
+        tables, ctx = eng.bm.block_tables(np.array(seqs), eng.maxB, wl.poison_block)
+        ref = oracle.oracle_decode(q.cpu().numpy(), eng.k_cache.cpu().numpy(),
+                                   eng.v_cache.cpu().numpy(), tables, ctx, wl.scale, "f16")
+        compare_outputs(out, ref, what=f"growing batch step {step}")
