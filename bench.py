@@ -94,29 +94,63 @@ def build_state(wl, dtype, partition_tokens=0, extra_blocks=64):
     return eng, step_seqs
 
 
-def cpu_baseline(wl, max_seconds=20.0):
-    """The oracle (float64 NumPy, one thread) on one step of the same workload:
-    the step's cache write plus decode of every sequence.  Repeated until about
-    10 s of work (half of ``max_seconds`` when that is smaller), and never past
-    ``max_seconds`` after the first repetition."""
-    import oracle
+_ORACLE_STATE = {}
+
+
+def _one_blas_thread():
     from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def _oracle_share(seqs):
+    """One worker's share of an oracle step: the step's cache write (into the
+    worker's own copy of the pools) and the decode of its sequences."""
+    import oracle
+    st = _ORACLE_STATE
+    oracle.oracle_cache_write(st["new_k"], st["new_v"], st["slots"], st["kc"], st["vc"])
+    oracle.oracle_decode(st["q"], st["kc"], st["vc"], st["tables"], st["ctx"], st["scale"],
+                         st["dtype"], seqs=list(seqs))
+    return len(seqs)
+
+
+def cpu_baseline(wl, max_seconds=20.0, max_workers=16):
+    """The oracle (float64 NumPy, as it stands) on one step of the same workload
+    on the host's cores: one forked worker process per core of this process's
+    affinity set (at most ``max_workers``), one BLAS thread each; every worker
+    takes a contiguous slice of the sequences (slices of about equal context
+    sums) and makes the step's cache write in its own copy of the pools.  The
+    step is repeated for about 10 s of wall clock (half of ``max_seconds`` when
+    that is smaller).  Call it before this process touches the GPU: the workers
+    are forked from it."""
+    import multiprocessing as mp
+    import oracle
     r = oracle.run_workload(wl, decode=False)
-    kc, vc = r["k_cache"], r["v_cache"]
-    new_k = np.stack([wl.kv(int(s), int(c) - 1, int(c))[0][0] for s, c in enumerate(r["ctx"])])
-    new_v = np.stack([wl.kv(int(s), int(c) - 1, int(c))[1][0] for s, c in enumerate(r["ctx"])])
+    ctx = np.asarray(r["ctx"], dtype=np.int64)
+    S = ctx.size
+    new_k = np.stack([wl.kv(int(s), int(c) - 1, int(c))[0][0] for s, c in enumerate(ctx)])
+    new_v = np.stack([wl.kv(int(s), int(c) - 1, int(c))[1][0] for s, c in enumerate(ctx)])
+    _ORACLE_STATE.update(new_k=new_k, new_v=new_v, slots=r["step_slots"], kc=r["k_cache"],
+                         vc=r["v_cache"], q=wl.q, tables=r["tables"], ctx=ctx, scale=wl.scale,
+                         dtype=wl.dtype)
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_workers, S))
+    cum = np.cumsum(ctx)
+    cuts = [0] + [int(np.searchsorted(cum, cum[-1] * k / cores)) + 1 for k in range(1, cores)] + [S]
+    cuts = sorted(set(min(max(c, 0), S) for c in cuts))
+    shares = [list(range(a, b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
     reps, t_total = 0, 0.0
-    with threadpool_limits(limits=1):
-        min_seconds = min(10.0, max_seconds / 2)
+    min_seconds = min(10.0, max_seconds / 2)
+    with mp.get_context("fork").Pool(len(shares), initializer=_one_blas_thread) as pool:
+        pool.map(_oracle_share, [[0]] * len(shares))    # fork and first touch, untimed
         while reps == 0 or (t_total < min_seconds and reps < 10000 and
                             t_total * (reps + 1) / reps <= max_seconds):
             t0 = time.perf_counter()
-            oracle.oracle_cache_write(new_k, new_v, r["step_slots"], kc, vc)
-            oracle.oracle_decode(wl.q, kc, vc, r["tables"], r["ctx"], wl.scale, wl.dtype)
+            done = sum(pool.map(_oracle_share, shares, chunksize=1))
             t_total += time.perf_counter() - t0
             reps += 1
+            assert done == S
+    _ORACLE_STATE.clear()
     per = t_total / reps
-    b = step_bytes(r["ctx"], wl.H, wl.D, wl.elem_bytes, wl.bs, 0)
+    b = step_bytes(ctx, wl.H, wl.D, wl.elem_bytes, wl.bs, 0)
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -126,11 +160,13 @@ def cpu_baseline(wl, max_seconds=20.0):
                     break
     except OSError:
         pass
-    return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one full step of {wl.name} (cache write of {wl.S} tokens + decode of "
-                      f"{wl.S} seqs x {wl.H} heads, sum(ctx)={int(r['ctx'].sum())}), "
-                      f"{reps} rep(s), {per:.2f} s each, float64 NumPy, 1 thread, {model}",
-            "seconds_per_step": round(per, 3)}
+    return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": len(shares),
+            "kind": "oracle",
+            "sample": f"one full step of {wl.name} (cache write of {S} tokens + decode of "
+                      f"{S} seqs x {wl.H} heads, sum(ctx)={int(ctx.sum())}), {reps} rep(s), "
+                      f"{per:.3f} s each, float64 NumPy, {len(shares)} forked worker processes "
+                      f"(one BLAS thread each, contiguous slices of the sequences), {model}",
+            "seconds_per_step": round(per, 4)}
 
 
 def load_traffic(kernel_tag):
@@ -163,10 +199,10 @@ def contiguous_compare(eng, seqs, q, wl, torch, pk, per_call):
     tab = torch.from_numpy(tables[:, :nb].astype(np.int64)).to(dev)
     L = nb * bs
     code = pk.DTYPE_CODES()[q.dtype]
-    pt = eng.last_info.partition_tokens
-    items, pt2, mx = pk.decode_schedule(ctx, wl.H, wl.D, bs, code, pt)
-    items_c, ptc, _ = pk.decode_schedule(ctx, wl.H, wl.D, 16, code, pt)
-    di, dic = torch.from_numpy(items).to(dev), torch.from_numpy(items_c).to(dev)
+    # the engine's automatic work list for these contexts, used by both launches
+    items, pt2, mx = pk.decode_schedule(ctx, wl.H, wl.D, bs, code, 0)
+    ptc = pt2
+    di = dic = torch.from_numpy(items).to(dev)
     dt_, dc = torch.from_numpy(tables).to(dev), torch.from_numpy(ctx).to(dev)
     ws = torch.zeros(max(pk.decode_workspace_size(S, wl.H, wl.D, bs, mx, code, pt2),
                          pk.decode_workspace_size(S, wl.H, wl.D, 16, mx, code, ptc), 16),
@@ -332,6 +368,192 @@ def block_manager_stats(eng, seqs, tables, wl):
             "sharing_saving": round(1.0 - distinct / max(logical, 1), 4)}
 
 
+def per_call_fn(torch):
+    def per_call(fn, n=20):
+        """Seconds per call of n back-to-back calls between one pair of events
+        (markers around every call would cost more than these short kernels)."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
+    return per_call
+
+
+def measure_workload(wl, args, torch, pk, hev, steps, warmup, cold_steps, partition_tokens=0):
+    """One workload on the GPU: build its pool, ``warmup`` engine steps, the decode
+    alone (the last warmup step's decode, ``steps`` back-to-back launches), loop 1
+    (``steps`` marker-free engine steps, wall clock), loop 2 (``steps`` steps with
+    the decode's own start/end events) and ``cold_steps`` steps after a cache
+    flush.  Returns (record, state) where state keeps what the headline's extra
+    measurements reuse."""
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.dtype]
+    pt_req = partition_tokens or wl.partition_tokens
+    grow = warmup + 2 * steps + cold_steps
+    eng, seqs = build_state(wl, tdt, pt_req, extra_blocks=-(-grow // wl.bs) + 1)
+    from synth import to_torch as to_dev
+    S = seqs.size
+    q = to_dev(wl.q, wl.dtype)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    k_new = torch.randn(S, wl.H, wl.D, device=dev, generator=gen).to(tdt)
+    v_new = torch.randn(S, wl.H, wl.D, device=dev, generator=gen).to(tdt)
+    out = torch.empty_like(q)
+
+    for _ in range(warmup):
+        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
+    torch.cuda.synchronize()
+
+    # The decode kernel alone (the roofline figure): the last warmup step's
+    # decode, launched back to back between one pair of events, at the
+    # workload's contexts (the timed steps below append one token each).
+    kern_s, ctx_a, tab_a, same_out = decode_alone(eng, seqs, q, out, wl, torch, pk, hev, steps)
+    if not same_out:
+        eprint(f"warning: {wl.name}: the back-to-back decode output differs from the step's")
+
+    # Loop 1, the steps themselves: nothing but the steps is enqueued (event
+    # markers around every decode would add their own gaps to each step).
+    ncows, pts, ngroups = 0, set(), set()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
+        ncows += eng.last_info.num_cow
+        pts.add(eng.last_info.partition_tokens)
+        ngroups.add(eng.last_info.num_group_items)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    # Loop 2, the decode launch of each step between HIP events recorded by
+    # its own dispatch; the same steps, continued.
+    evs = [(hev.create(), hev.create()) for _ in range(steps)]
+    stream_handle = torch.cuda.current_stream().cuda_stream
+    for a, b in evs:                      # first records outside the timed loop
+        hev.record(a, stream_handle)
+        hev.record(b, stream_handle)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(steps):
+        eng.set_decode_events(*evs[i])
+        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
+        pts.add(eng.last_info.partition_tokens)
+        ngroups.add(eng.last_info.num_group_items)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    eng.set_decode_events(None, None)
+
+    # each step appends one token to every sequence: the contexts of step i of
+    # loop 1 are the workload's step contexts + warmup + i, loop 2 continues
+    ctxs = [wl.ctx + warmup + i for i in range(steps)]
+    ctxs2 = [wl.ctx + warmup + steps + i for i in range(steps)]
+    elem = wl.elem_bytes
+    total_step_bytes = sum(step_bytes(c, wl.H, wl.D, elem, wl.bs, 0) for c in ctxs) + \
+        ncows * 2 * 2 * wl.H * wl.bs * wl.D * elem
+    dec_bytes = [decode_bytes(c, wl.H, wl.D, elem, wl.bs)[0] for c in ctxs2]
+    # distinct blocks: the steps only append, so step i's tables are a prefix
+    # of the final ones
+    tables, _ = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
+    uniq_bytes = [b - decode_bytes(c, wl.H, wl.D, elem, wl.bs)[1] +
+                  unique_kv_bytes(tables, c, wl.H, wl.D, elem, wl.bs)
+                  for b, c in zip(dec_bytes, ctxs2)]
+    bm_stats = block_manager_stats(eng, seqs, tables, wl)
+    elapsed = t1 - t0
+    step_ms = np.array([hev.elapsed_ms(a, b) for a, b in evs])
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+    step_s = float(step_ms.mean()) / 1e3
+
+    dec_a, kv_a = decode_bytes(ctx_a, wl.H, wl.D, elem, wl.bs)
+    uniq_a = dec_a - kv_a + unique_kv_bytes(tab_a, ctx_a, wl.H, wl.D, elem, wl.bs)
+    effective = dec_a / kern_s / 1e9
+    achieved = uniq_a / kern_s / 1e9
+    shared = max(ngroups) > 0
+    rec = {
+        "workload": wl.name, "placement": wl.placement if hasattr(wl, "placement") else None,
+        "seqs": int(S), "heads": wl.H, "head_dim": wl.D, "block_size": wl.bs,
+        "storage_dtype": wl.dtype, "num_blocks": wl.NB,
+        "partition_tokens": sorted(pts), "decode_group_items": sorted(ngroups),
+        "step_us": round(elapsed / steps * 1e6, 2),
+        "step_gbps": round(total_step_bytes / elapsed / 1e9, 2),
+        "seq_steps_per_s": round(S * steps / elapsed, 1),
+        "decode_us": round(kern_s * 1e6, 2),
+        "decode_ctx_sum": int(ctx_a.sum()),
+        "decode_gbps": round(achieved, 2),
+        "decode_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "decode_effective_gbps": round(effective, 2),
+        "decode_seq_steps_per_s": round(S / kern_s, 1),
+        "decode_bytes_counted": "distinct blocks once (shared prefixes once)",
+        "decode_algorithmic_bytes": int(uniq_a),
+        "decode_output_same_as_step": bool(same_out),
+        "decode_us_in_steps": round(step_s * 1e6, 2),
+        "decode_us_in_steps_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+                                       round(float(np.percentile(step_ms, 90)) * 1e3, 2)],
+        "decode_in_steps_distinct_gbps": round(float(np.mean(uniq_bytes)) / step_s / 1e9, 2),
+        "ms_per_step_with_decode_events": round((t3 - t2) / steps * 1e3, 4),
+        "kernel": (("decode_group_kernel + decode_wave_kernel" if wl.dtype == "f32"
+                    else "decode_shared_kernel") + " (pa_decode_scheduled_shared)" if shared
+                   else "decode_wave_kernel (pa_decode_scheduled)"),
+        "block_manager": bm_stats,
+    }
+    # cold decode: the same steps after a 1 GiB write (the 256 MB MALL and the
+    # L2s hold no K/V when the decode starts); decode events only
+    if cold_steps > 0:
+        # write 1 GiB (the protocol's flush), then read another 1 GiB so the
+        # dirty lines are written back before, not during, the timed decode
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        clean = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(cold_steps)]
+        for a, b in cev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for i in range(cold_steps):
+            scratch.fill_(i & 0xFF)
+            clean.sum()
+            eng.set_decode_events(*cev[i])
+            eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
+        torch.cuda.synchronize()
+        eng.set_decode_events(None, None)
+        ctables, _ = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
+        cms = np.array([a.elapsed_time(b) for a, b in cev]) * 1e3
+        c0 = warmup + 2 * steps
+        cbytes = [decode_bytes(wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)[0]
+                  for i in range(cold_steps)]
+        cuniq = [b - decode_bytes(wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)[1] +
+                 unique_kv_bytes(ctables, wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)
+                 for i, b in enumerate(cbytes)]
+        med = float(np.median(cms))
+        cg = float(np.mean(cuniq)) / (med * 1e-6) / 1e9
+        rec["decode_cold"] = {"steps": cold_steps,
+                              "flush": "1 GiB written, then 1 GiB of another buffer read, "
+                                       "before each step",
+                              "decode_us_median": round(med, 2),
+                              "decode_us_p10_p90": [round(float(np.percentile(cms, 10)), 2),
+                                                    round(float(np.percentile(cms, 90)), 2)],
+                              "decode_gbps": round(cg, 2),
+                              "decode_frac": round(cg / HBM_PEAK_GBS, 4)}
+        del scratch, clean
+    else:
+        rec["decode_cold"] = None
+    state = dict(eng=eng, seqs=seqs, q=q, k_new=k_new, v_new=v_new, tables=tables, S=S,
+                 total_step_bytes=total_step_bytes, elapsed=elapsed, ctxs=ctxs,
+                 achieved=achieved, uniq_a=uniq_a, kern_s=kern_s, shared=shared)
+    return rec, state
+
+
+# the other workloads of the same JSON line (compact records): (config, block
+# size, placement, also time the decode over contiguous copies of the K/V)
+OTHER_WORKLOADS = [(1, None, "random", False), (3, None, "random", True),
+                   (4, None, "random", False), (2, None, "identity", False)] + \
+                  [(5, b, "random", False) for b in (8, 16, 32, 64, 128)]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,35 +579,36 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run 3 plain elementwise copies (neg) of this many MiB: a "
                          "known-size reference for the HBM traffic counters")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the compact records of the other workloads")
+    ap.add_argument("--other-steps", type=int, default=20,
+                    help="timed steps (and back-to-back decodes) per other workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
               "cross-GPU component to measure", file=sys.stderr)
         sys.exit(2)
 
-    import torch
     import synth
+    t_setup = time.perf_counter()
+    wl = synth.make_workload(args.config, bs=args.bs, placement=args.placement)
+    eprint(f"setup {time.perf_counter() - t_setup:.1f} s: {wl.name}, S={wl.S}, "
+           f"sum(ctx)={int(wl.ctx.sum())}")
+    # The oracle's CPU baseline runs first, before this process touches the
+    # GPU: its worker processes are forked from this one.
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.perf_counter()
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        eprint(f"cpu baseline {time.perf_counter() - t:.1f} s on {cpu['cores']} cores")
+
+    import torch
     import paged_kv_cache_write_amd as pk
     pk.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    t_setup = time.perf_counter()
-    wl = synth.make_workload(args.config, bs=args.bs, placement=args.placement)
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.dtype]
-    pt_req = args.partition_tokens or wl.partition_tokens
-    grow = args.warmup + 2 * args.steps + args.cold_steps
-    eng, seqs = build_state(wl, tdt, pt_req, extra_blocks=-(-grow // wl.bs) + 1)
-    from synth import to_torch as to_dev
-    S = seqs.size
-    q = to_dev(wl.q, wl.dtype)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(0)
-    k_new = torch.randn(S, wl.H, wl.D, device=dev, generator=gen).to(tdt)
-    v_new = torch.randn(S, wl.H, wl.D, device=dev, generator=gen).to(tdt)
-    out = torch.empty_like(q)
-    eprint(f"setup {time.perf_counter() - t_setup:.1f} s: {wl.name}, S={S}, "
-           f"sum(ctx)={int(wl.ctx.sum())}")
+    hev = FenceFreeEvents()
+    per_call = per_call_fn(torch)
 
     if args.copy_calibration_mib:
         # a plain elementwise kernel that reads and writes exactly nbytes each
@@ -398,79 +621,10 @@ def main():
         del src, dst
         eprint(f"copy calibration: 3 elementwise kernels reading and writing {nbytes} bytes")
 
-    for _ in range(args.warmup):
-        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
-    torch.cuda.synchronize()
-
-    # The decode kernel alone (the roofline figure): the last warmup step's
-    # decode, launched back to back between one pair of events, at the
-    # workload's contexts (the timed steps below append one token each).
-    hev = FenceFreeEvents()
-    kern_s, ctx_a, tab_a, same_out = decode_alone(eng, seqs, q, out, wl, torch, pk, hev,
-                                                  args.steps)
-    if not same_out:
-        eprint("warning: the back-to-back decode output differs from the engine step's")
-
-    # Loop 1, the steps themselves: nothing but the steps is enqueued (event
-    # markers around every decode would add their own gaps to each step).
-    ncows, pts, ngroups = 0, set(), set()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
-        ncows += eng.last_info.num_cow
-        pts.add(eng.last_info.partition_tokens)
-        ngroups.add(eng.last_info.num_group_items)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    # Loop 2, the decode launch of each step between HIP events recorded by
-    # its own dispatch; the same steps, continued.
-    evs = [(hev.create(), hev.create()) for _ in range(args.steps)]
-    stream_handle = torch.cuda.current_stream().cuda_stream
-    for a, b in evs:                      # first records outside the timed loop
-        hev.record(a, stream_handle)
-        hev.record(b, stream_handle)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for i in range(args.steps):
-        eng.set_decode_events(*evs[i])
-        eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
-        pts.add(eng.last_info.partition_tokens)
-        ngroups.add(eng.last_info.num_group_items)
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    eng.set_decode_events(None, None)
-
-    # each step appends one token to every sequence: the contexts of step i of
-    # loop 1 are the workload's step contexts + warmup + i, loop 2 continues
-    ctxs = [wl.ctx + args.warmup + i for i in range(args.steps)]
-    ctxs2 = [wl.ctx + args.warmup + args.steps + i for i in range(args.steps)]
-    elem = wl.elem_bytes
-    total_step_bytes = sum(step_bytes(c, wl.H, wl.D, elem, wl.bs, 0) for c in ctxs) + \
-        ncows * 2 * 2 * wl.H * wl.bs * wl.D * elem
-    dec_bytes = [decode_bytes(c, wl.H, wl.D, elem, wl.bs)[0] for c in ctxs2]
-    # distinct blocks: the steps only append, so step i's tables are a prefix
-    # of the final ones
-    tables, _ = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
-    uniq_bytes = [b - decode_bytes(c, wl.H, wl.D, elem, wl.bs)[1] +
-                  unique_kv_bytes(tables, c, wl.H, wl.D, elem, wl.bs)
-                  for b, c in zip(dec_bytes, ctxs2)]
-    bm_stats = block_manager_stats(eng, seqs, tables, wl)
-    elapsed = t1 - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    step_ms = np.array([hev.elapsed_ms(a, b) for a, b in evs])
-    for a, b in evs:
-        hev.destroy(a)
-        hev.destroy(b)
-    step_s = float(step_ms.mean()) / 1e3
-
-    dec_a, kv_a = decode_bytes(ctx_a, wl.H, wl.D, elem, wl.bs)
-    uniq_a = dec_a - kv_a + unique_kv_bytes(tab_a, ctx_a, wl.H, wl.D, elem, wl.bs)
-    effective = dec_a / kern_s / 1e9
-    achieved = uniq_a / kern_s / 1e9
-    shared = max(ngroups) > 0
-    value = total_step_bytes / elapsed / 1e9
+    rec, st = measure_workload(wl, args, torch, pk, hev, args.steps, args.warmup,
+                               args.cold_steps, args.partition_tokens)
+    S, eng, tables = st["S"], st["eng"], st["tables"]
+    value = st["total_step_bytes"] / st["elapsed"] / 1e9
     traffic = load_traffic("decode_" + wl.name)
     res = {
         "metric": METRIC,
@@ -479,8 +633,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_with_decode_events": round((t3 - t2) / args.steps * 1e3, 4),
+        "ms_per_step": round(st["elapsed"] / args.steps * 1e3, 4),
+        "ms_per_step_with_decode_events": rec["ms_per_step_with_decode_events"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -490,73 +644,31 @@ def main():
         "config": {"workload": wl.name, "placement": args.placement, "seqs": int(S),
                    "heads": wl.H, "head_dim": wl.D,
                    "block_size": wl.bs, "num_blocks": wl.NB,
-                   "ctx_sum_first_step": int(ctxs[0].sum()),
-                   "ctx_sum_last_step": int(ctxs[-1].sum()),
-                   "partition_tokens": sorted(pts)},
+                   "ctx_sum_first_step": int(st["ctxs"][0].sum()),
+                   "ctx_sum_last_step": int(st["ctxs"][-1].sum()),
+                   "partition_tokens": rec["partition_tokens"]},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "seq_steps_per_s": round(S * args.steps / elapsed, 1),
-        "decode_seq_steps_per_s": round(S / kern_s, 1),
-        "decode_us": round(kern_s * 1e6, 2),
+        "seq_steps_per_s": rec["seq_steps_per_s"],
+        "decode_seq_steps_per_s": rec["decode_seq_steps_per_s"],
+        "decode_us": rec["decode_us"],
         "decode_timing": f"the last warmup step's decode launched {args.steps} times back "
                          "to back between one pair of events on its stream (same inputs, "
                          "schedule and workspace as the step; output identical to the "
-                         f"step's: {same_out})",
-        "decode_ctx_sum": int(ctx_a.sum()),
-        "decode_us_in_steps": round(step_s * 1e6, 2),
-        "decode_us_in_steps_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),
-                                       round(float(np.percentile(step_ms, 90)) * 1e3, 2)],
-        "decode_in_steps_distinct_gbps": round(float(np.mean(uniq_bytes)) / step_s / 1e9, 2),
-        "decode_gbps": round(effective, 2),
-        "decode_pct_hbm_peak": round(100 * effective / HBM_PEAK_GBS, 2),
-        "decode_group_items": sorted(ngroups),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": (("decode_group_kernel + decode_wave_kernel"
-                                 if wl.dtype == "f32" else "decode_shared_kernel") +
-                                " (pa_decode_scheduled_shared)" if shared else
-                                "decode_wave_kernel (pa_decode_scheduled)"),
-                     "algorithmic_bytes_per_launch": int(uniq_a),
+                         f"step's: {rec['decode_output_same_as_step']})",
+        "decode_ctx_sum": rec["decode_ctx_sum"],
+        "decode_us_in_steps": rec["decode_us_in_steps"],
+        "decode_us_in_steps_p10_p90": rec["decode_us_in_steps_p10_p90"],
+        "decode_in_steps_distinct_gbps": rec["decode_in_steps_distinct_gbps"],
+        "decode_gbps": rec["decode_effective_gbps"],
+        "decode_pct_hbm_peak": round(100 * rec["decode_effective_gbps"] / HBM_PEAK_GBS, 2),
+        "decode_group_items": rec["decode_group_items"],
+        "roofline": {"bound": "hbm", "achieved": round(st["achieved"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(st["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": rec["kernel"],
+                     "algorithmic_bytes_per_launch": int(st["uniq_a"]),
                      "bytes_counted": "distinct blocks once (shared prefixes once)"},
+        "decode_cold": rec["decode_cold"],
     }
-    # cold decode: the same steps after a 1 GiB write (the 256 MB MALL and the
-    # L2s hold no K/V when the decode starts); decode events only
-    cold = None
-    if args.cold_steps > 0:
-        # write 1 GiB (the protocol's flush), then read another 1 GiB so the
-        # dirty lines are written back before, not during, the timed decode
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        clean = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.cold_steps)]
-        for a, b in cev:
-            a.record()
-            b.record()
-        torch.cuda.synchronize()
-        for i in range(args.cold_steps):
-            scratch.fill_(i & 0xFF)
-            clean.sum()
-            eng.set_decode_events(*cev[i])
-            eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
-        torch.cuda.synchronize()
-        eng.set_decode_events(None, None)
-        ctables, _ = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
-        cms = np.array([a.elapsed_time(b) for a, b in cev]) * 1e3
-        c0 = args.warmup + 2 * args.steps
-        cbytes = [decode_bytes(wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)[0]
-                  for i in range(args.cold_steps)]
-        cuniq = [b - decode_bytes(wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)[1] +
-                 unique_kv_bytes(ctables, wl.ctx + c0 + i, wl.H, wl.D, elem, wl.bs)
-                 for i, b in enumerate(cbytes)]
-        med = float(np.median(cms))
-        cold = {"steps": args.cold_steps, "flush": "1 GiB written, then 1 GiB of another "
-                                                    "buffer read, before each step",
-                "decode_us_median": round(med, 2),
-                "decode_us_p10_p90": [round(float(np.percentile(cms, 10)), 2),
-                                      round(float(np.percentile(cms, 90)), 2)],
-                "decode_gbps": round(float(np.mean(cuniq)) / (med * 1e-6) / 1e9, 2)}
-        del scratch, clean
-    res["decode_cold"] = cold
 
     # achievable read: the library's plain streaming read over a large buffer
     if args.read_gib > 0:
@@ -574,27 +686,16 @@ def main():
         rgbps = buf.numel() / best / 1e9
         res["achievable_read"] = {"gbps": round(rgbps, 1), "bytes": buf.numel(),
                                   "kernel": "stream_read_kernel (pa_stream_read), best of 5"}
-        res["roofline"]["frac_of_achievable_read"] = round(achieved / rgbps, 4)
+        res["roofline"]["frac_of_achievable_read"] = round(st["achieved"] / rgbps, 4)
         del buf
 
     # secondary: the cache write and the copy-on-write copy on their own
     sec = {}
+    elem = wl.elem_bytes
+    k_new, v_new = st["k_new"], st["v_new"]
     last = eng.last_step
     slots_d = torch.from_numpy(last["slots"]).to(dev)
     pk.cache_write(k_new, v_new, slots_d, eng.k_cache, eng.v_cache)
-
-    def per_call(fn, n=20):
-        """Seconds per call of n back-to-back calls between one pair of events
-        (markers around every call would cost more than these short kernels)."""
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(n):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e-3 / n
-
     wt = per_call(lambda: pk.cache_write(k_new, v_new, slots_d, eng.k_cache, eng.v_cache))
     sec["cache_write_us"] = round(wt * 1e6, 2)
     sec["cache_write_gbps"] = round(4 * S * wl.H * wl.D * elem / wt / 1e9, 2)
@@ -633,20 +734,37 @@ def main():
         sec["swap_in_gbps"] = round(nswap * blk / si / 1e9, 2)
     sec["swap_blocks"] = nswap
     res["secondary"] = sec
-    res["block_manager"] = bm_stats
+    res["block_manager"] = rec["block_manager"]
 
-    if args.contiguous:
-        res["contiguous"] = contiguous_compare(eng, seqs, q, wl, torch, pk, per_call)
+    if args.contiguous or not args.headline_only:
+        res["contiguous"] = contiguous_compare(eng, st["seqs"], st["q"], wl, torch, pk, per_call)
     if args.prefill:
         res["prefill"] = prefill_measure(torch, pk, per_call,
                                          "f16" if wl.dtype == "f32" else wl.dtype)
+    del st, eng
+    torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
-        t = time.perf_counter()
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-        eprint(f"cpu baseline {time.perf_counter() - t:.1f} s")
-    else:
-        res["cpu_baseline"] = None
+    if not args.headline_only:
+        others = []
+        for cfg, bs, placement, contig in OTHER_WORKLOADS:
+            t = time.perf_counter()
+            owl = synth.make_workload(cfg, bs=bs, placement=placement)
+            orec, ost = measure_workload(owl, args, torch, pk, hev, args.other_steps, 5,
+                                         5 if cfg != 1 else 0)
+            orec["config"] = cfg
+            orec["placement"] = placement
+            if contig:
+                orec["contiguous"] = contiguous_compare(ost["eng"], ost["seqs"], ost["q"], owl,
+                                                        torch, pk, per_call)
+            del orec["block_manager"]["pool_blocks"]
+            others.append(orec)
+            del ost
+            torch.cuda.empty_cache()
+            eprint(f"{owl.name} bs={owl.bs} {placement}: decode {orec['decode_us']} us "
+                   f"({orec['decode_frac']:.3f}), step {orec['step_us']} us, "
+                   f"{time.perf_counter() - t:.1f} s")
+        res["workloads"] = others
+    res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

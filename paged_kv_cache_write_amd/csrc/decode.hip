@@ -1462,23 +1462,32 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
       groups.push_back(std::move(mem));
     }
   }
+  // Automatic partitions are balanced: a row's tokens after its shared run
+  // are cut into ceil(rest / pt) partitions of nearly equal length (whole
+  // units of q tokens, so every partition starts on a block and chunk
+  // boundary; at most pt tokens each), where pt is the smallest size (from 256
+  // up, in steps of q) whose launch fits kSchedTargetWaves waves.  All waves
+  // of such a launch start together and, with equal work, end together; a
+  // launch that does not fit even at the largest size runs several rounds,
+  // longest items first.  A requested size cuts full partitions of exactly
+  // that size and one shorter last partition per row.
+  const bool balanced = requested == 0;
+  const int32_t q = std::max<int32_t>(32, bs);
   int32_t pt = requested;
-  if (pt == 0) {
-    // Largest partition (up to 1024 tokens and 64 blocks, in steps of 128
-    // tokens) that still gives about eight waves per CU: long waves stream
-    // without pause, the longest-first order evens out the end, and fewer
-    // partials are merged.
+  if (balanced) {
     const int max_pt = std::min(64 * bs, 1024);
-    pt = max_pt;
     int64_t gwaves = 0;
     for (auto& g : groups)
       gwaves += int64_t((g.size() + max_members - 1) / max_members) *
                 (shared[g[0]] / kSharedPartTokens);
-    while (pt > 256 && pt > bs) {
+    pt = max_pt;
+    for (int32_t t = std::min(256, max_pt); t <= max_pt; t += q) {
       int64_t waves = gwaves;
-      for (int32_t s = 0; s < S; ++s) waves += (ctx[s] - shared[s] + pt - 1) / pt;
-      if (waves * H >= kSchedTargetWaves) break;
-      pt -= 128;
+      for (int32_t s = 0; s < S; ++s) waves += (ctx[s] - shared[s] + t - 1) / t;
+      if (waves * H <= kSchedTargetWaves) {
+        pt = t;
+        break;
+      }
     }
   }
   Plan plan;
@@ -1499,22 +1508,53 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
   hs->items.clear();
   hs->groups.clear();
   hs->members.clear();
-  for (int32_t s = 0; s < S; ++s) {
-    const int32_t base = shared[s] / kSharedPartTokens;
-    for (int32_t p = 0; p < (ctx[s] - shared[s]) / pt; ++p)
-      push(hs->items, {s, base + p, shared[s] + p * pt, pt, nparts[s]});
-  }
-  std::vector<int32_t> partial;
-  for (int32_t s = 0; s < S; ++s)
-    if ((ctx[s] - shared[s]) % pt != 0) partial.push_back(s);
-  std::stable_sort(partial.begin(), partial.end(), [&](int32_t a, int32_t b) {
-    return (ctx[a] - shared[a]) % pt > (ctx[b] - shared[b]) % pt;
-  });
-  for (int32_t s : partial) {
-    const int32_t rest = ctx[s] - shared[s];
-    const int32_t full = rest / pt;
-    push(hs->items, {s, shared[s] / kSharedPartTokens + full, shared[s] + full * pt, rest % pt,
-                     nparts[s]});
+  if (balanced) {
+    // n = ceil(rest / pt) partitions of u / n or u / n + 1 units (u = units
+    // of the rest; the first u % n partitions take the extra unit), so none
+    // is longer than pt; the last one ends at the context.
+    std::vector<int32_t> single;  // items before ordering
+    for (int32_t s = 0; s < S; ++s) {
+      const int32_t rest = ctx[s] - shared[s];
+      if (rest <= 0) continue;
+      const int32_t n = (rest + pt - 1) / pt;
+      const int32_t u = (rest + q - 1) / q;
+      const int32_t base = shared[s] / kSharedPartTokens;
+      int32_t t0 = shared[s];
+      for (int32_t p = 0; p < n; ++p) {
+        const int32_t units = u / n + (p < u % n ? 1 : 0);
+        const int32_t len = std::min(units * q, ctx[s] - t0);
+        push(single, {s, base + p, t0, len, nparts[s]});
+        t0 += len;
+      }
+    }
+    // longest first (stable: ties keep sequence and partition order)
+    const size_t n_single = single.size() / kItemInts;
+    std::vector<size_t> order(n_single);
+    for (size_t i = 0; i < n_single; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+      return single[a * kItemInts + 3] > single[b * kItemInts + 3];
+    });
+    for (size_t i : order)
+      hs->items.insert(hs->items.end(), single.begin() + i * kItemInts,
+                       single.begin() + (i + 1) * kItemInts);
+  } else {
+    for (int32_t s = 0; s < S; ++s) {
+      const int32_t base = shared[s] / kSharedPartTokens;
+      for (int32_t p = 0; p < (ctx[s] - shared[s]) / pt; ++p)
+        push(hs->items, {s, base + p, shared[s] + p * pt, pt, nparts[s]});
+    }
+    std::vector<int32_t> partial;
+    for (int32_t s = 0; s < S; ++s)
+      if ((ctx[s] - shared[s]) % pt != 0) partial.push_back(s);
+    std::stable_sort(partial.begin(), partial.end(), [&](int32_t a, int32_t b) {
+      return (ctx[a] - shared[a]) % pt > (ctx[b] - shared[b]) % pt;
+    });
+    for (int32_t s : partial) {
+      const int32_t rest = ctx[s] - shared[s];
+      const int32_t full = rest / pt;
+      push(hs->items, {s, shared[s] / kSharedPartTokens + full, shared[s] + full * pt,
+                       rest % pt, nparts[s]});
+    }
   }
   for (int32_t s = 0; s < S; ++s)
     if (ctx[s] == 0) push(hs->items, {s, 0, 0, 0, 0});

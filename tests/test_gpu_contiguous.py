@@ -63,7 +63,8 @@ def test_contiguous_bit_identical_to_paged():
     step = np.array([op for op in wl.ops if op[0] == "step"][-1][1], dtype=np.int64)
     tables, ctx = eng.bm.block_tables(step, wl.max_blocks_per_seq, wl.poison_block)
     pt = eng.last_step["partition_tokens"]
-    items, pt2, mx = pk().decode_schedule(ctx, wl.H, wl.D, wl.bs, CODES[wl.dtype], pt)
+    # the engine's own (automatic) work list, rebuilt from the same contexts
+    items, pt2, mx = pk().decode_schedule(ctx, wl.H, wl.D, wl.bs, CODES[wl.dtype], 0)
     assert pt2 == pt
     k, v = contiguous_kv(wl, ctx, "SLHD")
     qd = to_dev(wl.q, wl.dtype)

@@ -34,7 +34,7 @@ def test_decode_schedule_order():
     rng = np.random.default_rng(0)
     for _ in range(20):
         ctx = rng.integers(0, 5000, size=int(rng.integers(1, 50))).astype(np.int32)
-        items, pt, mx = pk.decode_schedule(ctx, 40, 128, 16, 1, 0)
+        items, pt, mx = pk.decode_schedule(ctx, 40, 128, 16, 1, 512)
         want = sorted([(s, p) for s, c in enumerate(ctx) for p in range(-(-int(c) // pt))] +
                       [(s, 0) for s, c in enumerate(ctx) if c == 0])
         assert sorted(map(tuple, items[:, :2].tolist())) == want
@@ -43,6 +43,58 @@ def test_decode_schedule_order():
         for s, p, t0, n, npart in items.tolist():
             assert t0 == p * pt and n == min(pt, int(ctx[s]) - t0) or ctx[s] == 0
             assert npart == -(-int(ctx[s]) // pt)
+
+
+# waves the automatic partition size aims for (one round of wave slots)
+TARGET_WAVES = 2048
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32, 64, 128])
+def test_automatic_partitions_are_balanced(bs):
+    """Automatic partitions: each row is cut into ceil(ctx / pt) partitions that
+    start on whole units of max(32, bs) tokens, cover the row once, are at most pt
+    long and differ by at most one unit (the last may end early at the context);
+    pt is the smallest size from 256 up whose launch fits the wave target, else the
+    largest; the work list runs longest first."""
+    pk = _pk()
+    rng = np.random.default_rng(bs)
+    q = max(32, bs)
+    max_pt = min(64 * bs, 1024)
+    for trial in range(25):
+        H = int(rng.choice([1, 8, 40]))
+        ctx = rng.integers(0, 6000, size=int(rng.integers(1, 60))).astype(np.int32)
+        if trial % 5 == 0:
+            ctx[:] = 2048
+        items, pt, mx = pk.decode_schedule(ctx, H, 128, bs, 1, 0)
+        assert mx == int(ctx.max())
+        assert 256 <= pt <= max_pt or pt == max_pt
+        waves = lambda t: H * sum(-(-int(c) // t) for c in ctx)
+        if pt > min(256, max_pt):
+            assert waves(pt - q) > TARGET_WAVES          # a smaller size would not fit
+        assert waves(pt) <= TARGET_WAVES or pt == max_pt
+        sizes = items[:, 3].tolist()
+        assert sizes == sorted(sizes, reverse=True)
+        rows = {}
+        for s, p, t0, n, npart in items.tolist():
+            rows.setdefault(s, []).append((p, t0, n, npart))
+        assert sorted(rows) == list(range(ctx.size))
+        for s, parts in rows.items():
+            c = int(ctx[s])
+            if c == 0:
+                assert parts == [(0, 0, 0, 0)]
+                continue
+            parts.sort()
+            n_parts = -(-c // pt)
+            assert [p for p, *_ in parts] == list(range(n_parts))
+            assert all(npart == n_parts for *_, npart in parts)
+            t = 0
+            for p, t0, n, _ in parts:
+                assert t0 == t and t0 % q == 0 and 0 < n <= pt
+                t += n
+            assert t == c
+            lens = [n for _, _, n, _ in parts]
+            assert max(lens[:-1] or [0]) - min(lens[:-1] or [0]) <= q
+            assert lens[-1] <= max(lens)
 
 
 def _tables_after_step(wl):
@@ -212,14 +264,15 @@ def test_shared_schedule_errors():
 
 @pytest.mark.parametrize("bs", [8, 16, 32, 128])
 def test_automatic_partition_size(bs):
-    """The automatic partition size is the largest of 1024, 896, ..., 256 tokens
-    (at most 64 blocks) whose work list still has 2048 waves (8 per CU of the
-    256), or 256 when none has: checked as properties of the chosen size on
-    random batches, from a handful of sequences to hundreds."""
+    """The automatic partition size is the smallest of 256, 256 + q, ... tokens
+    (q = max(32, bs); at most 64 blocks and 1024 tokens) whose work list fits 2048
+    waves, or the largest when none does: checked as properties of the chosen size
+    on random batches, from a handful of sequences to hundreds."""
     pk = _pk()
     H = 40
     rng = np.random.default_rng(bs)
     cap = min(1024, 64 * bs)
+    q = max(32, bs)
     seen = set()
     for i in range(40):
         S = int(rng.integers(1, 12)) if i % 2 else int(rng.integers(12, 300))
@@ -227,9 +280,9 @@ def test_automatic_partition_size(bs):
         items, pt, _ = pk.decode_schedule(ctx, H, 128, bs, 1, 0)
         seen.add(pt)
         waves = lambda p: int((-(-ctx.astype(np.int64) // p)).sum()) * H
-        assert 256 <= pt <= cap and (cap - pt) % 128 == 0 and pt % bs == 0
+        assert min(256, cap) <= pt <= cap and (pt - min(256, cap)) % q == 0 and pt % bs == 0
         assert len(items) * H == waves(pt)
-        assert waves(pt) >= 2048 or pt == 256
-        if pt < cap:
-            assert waves(pt + 128) < 2048, "a larger partition also had enough waves"
+        assert waves(pt) <= TARGET_WAVES or pt == cap
+        if pt > min(256, cap):
+            assert waves(pt - q) > TARGET_WAVES, "a smaller partition also fitted"
     assert len(seen) > 1
