@@ -55,6 +55,8 @@ _SIGNATURES = {
     "pa_decode": (_c.c_int, _DECODE_ARGS),
     "pa_decode_partitions": (_c.c_int, _DECODE_ARGS),
     "pa_decode_reduce": (_c.c_int, _DECODE_ARGS),
+    "pa_decode_noalloc": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i64,
+                                     _f32, _i32, _i32, _vp, _i32, _vp]),
     "pa_decode_scheduled": (_c.c_int, _DECODE_ARGS + [_vp, _i32]),
     "pa_decode_scheduled_shared": (_c.c_int, _DECODE_ARGS + [_vp, _i32, _vp, _i32, _vp]),
     "pa_decode_schedule_shared": (_c.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

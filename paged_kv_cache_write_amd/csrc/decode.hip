@@ -43,6 +43,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <unordered_map>
 #include <vector>
@@ -1577,6 +1578,58 @@ int build_schedule(const int32_t* ctx, int32_t S, int32_t H, int32_t D, int32_t 
 }  // namespace pa
 
 namespace pa {
+
+// ---- the decode without a workspace argument ------------------------------
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops): the decode's scratch (row counters and partials)
+// lives in one file-scope device array, which each GPU the library runs on
+// holds until the process ends.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+// The counters keep this fixed prefix of the array (131072 rows), zeroed once
+// per device; the partials of every call come after it.
+constexpr size_t kNoAllocCounterBytes = kNoAllocScratchBytes / 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += size_t(gridDim.x) * 256)
+    p[i] = 0u;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the current device's scratch array.  The first call on a
+// device looks the address up (the array's name is only a host-side stand-in)
+// and clears the counter prefix with a kernel on `st`, so the counters start
+// at zero however the module was loaded; every completed decode leaves them
+// zero again.
+static int noalloc_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return PA_ERR_HIP;
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, st,
+                       static_cast<uint32_t*>(ptr), kNoAllocCounterBytes / 4);
+    if (launch_status() != PA_OK) return PA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace pa
+
+namespace pa {
 uint32_t debug_take_decode() { return debug_take_word(); }
 
 int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cache,
@@ -1697,6 +1750,37 @@ int pa_decode_schedule_shared(const int32_t* context_lens, const int32_t* block_
 int pa_decode(PA_DECODE_ARGS) {
   return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, PA_DECODE_PASS);
 }
+int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                      int32_t max_context_len, int32_t dtype, void* out,
+                      int32_t partition_tokens, void* stream) {
+  pa::Plan plan;
+  int rc = pa::make_plan(num_seqs, num_heads, head_dim, block_size, max_context_len, dtype,
+                         partition_tokens, &plan);
+  if (rc != PA_OK) return rc;
+  // The counters keep the array's fixed prefix whatever the call's size (a
+  // smaller call's partials never lie where a later call's counters are);
+  // the partials follow it.
+  constexpr int64_t kRows = int64_t(pa::kNoAllocCounterBytes / sizeof(int));
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0 && num_seqs > 0) {
+    if (int64_t(num_seqs) * num_heads > kRows ||
+        plan.ws_bytes - pa::counter_bytes(num_seqs, num_heads) + pa::kNoAllocCounterBytes >
+            pa::kNoAllocScratchBytes)
+      return PA_ERR_WORKSPACE;
+    rc = pa::noalloc_scratch(reinterpret_cast<hipStream_t>(stream), &ws);
+    if (rc != PA_OK) return rc;
+  }
+  pa::Schedule sc;
+  sc.counter_rows = kRows;
+  return pa::decode_impl(pa::kDoPartitions | pa::kDoReduce | pa::kFused, q, k_cache, v_cache,
+                         block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                         head_dim, block_size, num_blocks, scale, max_context_len, dtype, out,
+                         ws, ws ? pa::kNoAllocScratchBytes : 0, partition_tokens, stream, sc);
+}
+
 int pa_decode_partitions(PA_DECODE_ARGS) {
   return pa::decode_impl(pa::kDoPartitions, PA_DECODE_PASS);
 }
