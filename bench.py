@@ -384,10 +384,10 @@ def per_call_fn(torch):
 
 
 def measure_workload(wl, args, torch, pk, hev, steps, warmup, cold_steps, partition_tokens=0):
-    """One workload on the GPU: build its pool, ``warmup`` engine steps, the decode
-    alone (the last warmup step's decode, ``steps`` back-to-back launches), loop 1
+    """One workload on the GPU: build its pool, ``warmup`` engine steps, loop 1
     (``steps`` marker-free engine steps, wall clock), loop 2 (``steps`` steps with
-    the decode's own start/end events) and ``cold_steps`` steps after a cache
+    the decode's own start/end events), the decode alone (the last step's decode,
+    ``steps`` back-to-back launches) and ``cold_steps`` steps after a cache
     flush.  Returns (record, state) where state keeps what the headline's extra
     measurements reuse."""
     dev = torch.device("cuda:0")
@@ -408,15 +408,9 @@ def measure_workload(wl, args, torch, pk, hev, steps, warmup, cold_steps, partit
         eng.step(seqs, q, k_new, v_new, wl.scale, out=out)
     torch.cuda.synchronize()
 
-    # The decode kernel alone (the roofline figure): the last warmup step's
-    # decode, launched back to back between one pair of events, at the
-    # workload's contexts (the timed steps below append one token each).
-    kern_s, ctx_a, tab_a, same_out = decode_alone(eng, seqs, q, out, wl, torch, pk, hev, steps)
-    if not same_out:
-        eprint(f"warning: {wl.name}: the back-to-back decode output differs from the step's")
-
-    # Loop 1, the steps themselves: nothing but the steps is enqueued (event
-    # markers around every decode would add their own gaps to each step).
+    # Loop 1, the steps themselves, right after the warmup: nothing but the
+    # steps is enqueued (event markers around every decode would add their own
+    # gaps to each step).
     ncows, pts, ngroups = 0, set(), set()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -445,6 +439,13 @@ def measure_workload(wl, args, torch, pk, hev, steps, warmup, cold_steps, partit
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     eng.set_decode_events(None, None)
+
+    # The decode kernel alone (the roofline figure): the last step's decode,
+    # launched back to back between one pair of events, at that step's
+    # contexts (the workload's step contexts + warmup + 2 * steps - 1).
+    kern_s, ctx_a, tab_a, same_out = decode_alone(eng, seqs, q, out, wl, torch, pk, hev, steps)
+    if not same_out:
+        eprint(f"warning: {wl.name}: the back-to-back decode output differs from the step's")
 
     # each step appends one token to every sequence: the contexts of step i of
     # loop 1 are the workload's step contexts + warmup + i, loop 2 continues
@@ -651,7 +652,7 @@ def main():
         "seq_steps_per_s": rec["seq_steps_per_s"],
         "decode_seq_steps_per_s": rec["decode_seq_steps_per_s"],
         "decode_us": rec["decode_us"],
-        "decode_timing": f"the last warmup step's decode launched {args.steps} times back "
+        "decode_timing": f"the last timed step's decode launched {args.steps} times back "
                          "to back between one pair of events on its stream (same inputs, "
                          "schedule and workspace as the step; output identical to the "
                          f"step's: {rec['decode_output_same_as_step']})",

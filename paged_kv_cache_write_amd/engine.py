@@ -27,11 +27,17 @@ class PagedKVEngine:
     ``pad_block`` fills the unused tail of every exported table row (never used
     as an address).  ``max_batch`` bounds the sequences of one step and
     ``max_blocks_per_seq`` the table width (so contexts up to that many blocks).
-    ``ring`` pinned staging slots (default RING) let the host run that many
-    steps ahead; with an even count one event guards each half of them.
+    ``ring`` pinned staging slots let the host run that many steps ahead; with
+    an even count one event guards each half of them.  The default is RING
+    slots, or RING_LARGE when RING slots would take more than RING_BYTES of
+    pinned memory (batches with wide tables).
     """
 
-    RING = 16  # pinned staging slots in flight: two halves, one guard event each
+    # pinned staging slots in flight: two halves, one guard event each (a guard
+    # event costs ~4.5 us of idle GPU, so one per 32 steps instead of 8)
+    RING = 64
+    RING_LARGE = 16
+    RING_BYTES = 64 << 20
 
     def __init__(self, num_blocks, num_heads, head_dim, block_size, dtype, max_blocks_per_seq,
                  max_batch, free_order=None, pad_block=0, device="cuda", fill=None,
@@ -56,7 +62,9 @@ class PagedKVEngine:
         self.bm = BlockManager(self.NB, self.bs, free_order)
         L = self._lib = lib()  # the library that owns the handle
         slot = int(L.pa_engine_staging_bytes(self.max_batch, self.maxB, self.bs))
-        self.ring = int(ring or self.RING)
+        if ring is None:
+            ring = self.RING if slot * self.RING <= self.RING_BYTES else self.RING_LARGE
+        self.ring = int(ring)
         self._host = torch.empty(slot * self.ring, dtype=torch.uint8, pin_memory=True)
         self._dev = torch.empty(slot, dtype=torch.uint8, device=self.device)
         h = ctypes.c_void_p()
