@@ -574,61 +574,17 @@ __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h
   return cx;
 }
 
-// One wave per (sequence, head, partition): grid order from context_lens, or
-// a host-scheduled work list of single items.  A workgroup holds W waves of
-// consecutive heads.
-template <class DT, int D, int U, bool kContig = false, int W = 1>
-__device__ __forceinline__ void wave_body(DecodeParams P, uint3 block) {
+// The work of one wave on one (row, partition): stream the partition's K/V
+// chunks with the online softmax, merge the wave's token rows, then store the
+// row or the partial (and merge the row if this wave completes it).  cx holds
+// the partition's table window (make_ctx).
+template <class DT, int D, int U, bool kContig>
+__device__ __forceinline__ void stream_unit(const DecodeParams& P, ChunkCtx cx, size_t row_id,
+                                            int part, int ntok, int nparts, int lane) {
   using T = typename DT::T;
   using Sh = Shape<DT, D, U>;
   constexpr int kVec = DT::kVec;
   constexpr size_t kRowBytes = size_t(D) * sizeof(T);
-
-  const int wave = wave_uniform(threadIdx.x / kWave);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int H = P.H;
-  const int ngroups = (H + W - 1) / W;
-  int hg, part, s, t0;
-  const int32_t* it = nullptr;
-  if (P.items != nullptr) {  // scheduled launch: x = item * head_groups + head group
-    const int item = block.x / ngroups;
-    hg = block.x - item * ngroups;
-    it = P.items + kItemInts * item;
-    s = it[0];
-    part = it[1];
-    t0 = it[2];
-#ifdef PA_DEBUG
-    // an item outside the launch (sequence), the workspace (partition index
-    // and count) or the table window (first token, tokens) does nothing
-    const int nt = it[3], np = it[4];
-    if (s < 0 || s >= P.num_seqs || part < 0 || t0 < 0 || nt < 0 || nt > P.window_tokens ||
-        np < 0 || np > P.max_parts || (np > 0 && part >= np) || (nt > 0 && np == 0)) {
-      if (threadIdx.x == 0) debug_flag(PA_DEBUG_ITEM);
-      return;
-    }
-#endif
-  } else {
-    hg = block.x;
-    part = block.y;
-    s = block.z;
-    t0 = part * P.part_tokens;
-  }
-  const int h = hg * W + wave;
-  if (h >= H) return;
-  const size_t row_id = size_t(s) * H + h;
-  ChunkCtx cx = make_ctx<DT, D, U, kContig>(P, s, h, t0, lane);
-  int ntok, nparts;
-  if (it != nullptr) {
-    ntok = it[3];
-    nparts = it[4];
-  } else {
-    int ctx = P.context_lens[s];
-    // never read past the table row (the token axis) or the launched partitions
-    const int cap = kContig ? int(min(P.max_tokens, int64_t(1) << 30)) : (P.maxB << P.log2_bs);
-    ctx = min(ctx, min(cap, P.max_parts * P.part_tokens));
-    nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
-    ntok = part < nparts ? min(P.part_tokens, ctx - t0) : 0;
-  }
   const int row = lane / Sh::kLPT;
   const int col = lane % Sh::kLPT;
   if (ntok <= 0) {
@@ -697,6 +653,59 @@ __device__ __forceinline__ void wave_body(DecodeParams P, uint3 block) {
   const size_t rows[1] = {row_id};
   const int nps[1] = {nparts};
   finish<DT, D, U, 1>(P, rows, nps, 1, part, m, l, acc, lane);
+}
+
+// One wave per (sequence, head, partition): grid order from context_lens, or
+// a host-scheduled work list of single items.  A workgroup holds W waves of
+// consecutive heads.
+template <class DT, int D, int U, bool kContig = false, int W = 1>
+__device__ __forceinline__ void wave_body(DecodeParams P, uint3 block) {
+  const int wave = wave_uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int H = P.H;
+  const int ngroups = (H + W - 1) / W;
+  int hg, part, s, t0;
+  const int32_t* it = nullptr;
+  if (P.items != nullptr) {  // scheduled launch: x = item * head_groups + head group
+    const int item = block.x / ngroups;
+    hg = block.x - item * ngroups;
+    it = P.items + kItemInts * item;
+    s = it[0];
+    part = it[1];
+    t0 = it[2];
+#ifdef PA_DEBUG
+    // an item outside the launch (sequence), the workspace (partition index
+    // and count) or the table window (first token, tokens) does nothing
+    const int nt = it[3], np = it[4];
+    if (s < 0 || s >= P.num_seqs || part < 0 || t0 < 0 || nt < 0 || nt > P.window_tokens ||
+        np < 0 || np > P.max_parts || (np > 0 && part >= np) || (nt > 0 && np == 0)) {
+      if (threadIdx.x == 0) debug_flag(PA_DEBUG_ITEM);
+      return;
+    }
+#endif
+  } else {
+    hg = block.x;
+    part = block.y;
+    s = block.z;
+    t0 = part * P.part_tokens;
+  }
+  const int h = hg * W + wave;
+  if (h >= H) return;
+  const size_t row_id = size_t(s) * H + h;
+  ChunkCtx cx = make_ctx<DT, D, U, kContig>(P, s, h, t0, lane);
+  int ntok, nparts;
+  if (it != nullptr) {
+    ntok = it[3];
+    nparts = it[4];
+  } else {
+    int ctx = P.context_lens[s];
+    // never read past the table row (the token axis) or the launched partitions
+    const int cap = kContig ? int(min(P.max_tokens, int64_t(1) << 30)) : (P.maxB << P.log2_bs);
+    ctx = min(ctx, min(cap, P.max_parts * P.part_tokens));
+    nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
+    ntok = part < nparts ? min(P.part_tokens, ctx - t0) : 0;
+  }
+  stream_unit<DT, D, U, kContig>(P, cx, row_id, part, ntok, nparts, lane);
 }
 
 template <class DT, int D, int U, bool kContig = false, int W = 1>
