@@ -65,6 +65,27 @@ def test_prefill_long_prefix_and_empty_chunk():
     _run(wl, q, cu_q)
 
 
+@pytest.mark.parametrize("dtype,D", [("f16", 128), ("bf16", 64)])
+def test_prefill_prefix_past_the_table_window(dtype, D):
+    """Contexts of more than 1024 blocks (bs 8): the kernel's block-table window
+    in LDS (1024 entries) moves along the context; chunk lengths that leave
+    partial 16-query sets and one to three steps after the last full pass."""
+    synth.cache_draws(False)
+    wl, q, cu_q = synth.make_prefill(650 + D, 2, D, dtype, 8, [8500, 8200, 130],
+                                     [70, 33, 5])
+    _run(wl, q, cu_q)
+
+
+@pytest.mark.parametrize("q_len", [1, 31, 32, 33, 95, 96, 97, 129, 256, 300])
+def test_prefill_step_counts(q_len):
+    """Whole prompts whose key ranges end on and around step (32-key) and
+    tile (256-query) boundaries: every count of steps after the last pass of
+    four, and tiles with partial sets."""
+    synth.cache_draws(False)
+    wl, q, cu_q = synth.make_prefill(660 + q_len, 2, 128, "f16", 16, [0, 7], [q_len, q_len])
+    _run(wl, q, cu_q)
+
+
 def test_prefill_last_row_matches_decode():
     """A chunk's last query is the decode of that position: pa_prefill's last rows
     agree with pa_decode on the same cache within the tolerance."""
