@@ -576,7 +576,8 @@ def main():
                          "[S, L, H, D] layout (pa_decode_contiguous) next to the paged decode")
     ap.add_argument("--prefill", action="store_true",
                     help="also time the paged prefill attention (8 prompts of 1024 tokens at "
-                         "the 13B-layer shape) against the matrix cores' peak")
+                         "the 13B-layer shape) against the matrix cores' peak (the default run "
+                         "does, unless --headline-only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run 3 plain elementwise copies (neg) of this many MiB: a "
                          "known-size reference for the HBM traffic counters")
@@ -739,7 +740,7 @@ def main():
 
     if args.contiguous or not args.headline_only:
         res["contiguous"] = contiguous_compare(eng, st["seqs"], st["q"], wl, torch, pk, per_call)
-    if args.prefill:
+    if args.prefill or not args.headline_only:
         res["prefill"] = prefill_measure(torch, pk, per_call,
                                          "f16" if wl.dtype == "f32" else wl.dtype)
     del st, eng
