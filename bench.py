@@ -170,8 +170,9 @@ def cpu_baseline(wl, max_seconds=20.0, max_workers=16):
 
 
 def load_traffic(kernel_tag):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    """The committed rocprofv3 traffic record of a kernel (HBM read + write bytes
+    per launch and that launch's algorithmic bytes), if it was taken on the
+    current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -184,7 +185,7 @@ def load_traffic(kernel_tag):
             h.update(f.read())
     if h.hexdigest() != rec.get("source_sha256"):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
 
 
 def contiguous_compare(eng, seqs, q, wl, torch, pk, per_call):
@@ -627,7 +628,14 @@ def main():
                                args.cold_steps, args.partition_tokens)
     S, eng, tables = st["S"], st["eng"], st["tables"]
     value = st["total_step_bytes"] / st["elapsed"] / 1e9
-    traffic = load_traffic("decode_" + wl.name)
+    # HBM traffic per launch: the counters' ratio of (read + write) to algorithmic
+    # bytes, measured on a launch of the same workload and kernel source (the
+    # profile run's contexts are shorter), applied to this launch's bytes
+    trec = load_traffic("decode_" + wl.name)
+    traffic, traffic_ratio = None, None
+    if trec and trec.get("algorithmic_bytes_per_launch"):
+        traffic_ratio = trec["traffic_bytes_per_launch"] / trec["algorithmic_bytes_per_launch"]
+        traffic = round(traffic_ratio * int(st["uniq_a"]))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -668,6 +676,12 @@ def main():
                      "unit": "GB/s", "frac": round(st["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": rec["kernel"],
                      "algorithmic_bytes_per_launch": int(st["uniq_a"]),
+                     "traffic_over_algorithmic": (round(traffic_ratio, 4)
+                                                  if traffic_ratio else None),
+                     "traffic_source": (f"{trec['summary']}: {trec['traffic_bytes_per_launch']:.0f}"
+                                        f" B per launch of {trec['algorithmic_bytes_per_launch']}"
+                                        " algorithmic B (FETCH_SIZE and WRITE_SIZE, scaled by a"
+                                        " copy kernel of known size)") if trec else None,
                      "bytes_counted": "distinct blocks once (shared prefixes once)"},
         "decode_cold": rec["decode_cold"],
     }
