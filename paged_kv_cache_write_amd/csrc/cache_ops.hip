@@ -47,7 +47,9 @@ __global__ __launch_bounds__(kCwThreads) void copy_blocks_kernel(
     const int32_t* __restrict__ pairs, int64_t tile_vecs, int64_t src_blocks, int64_t dst_blocks) {
   const int pair = blockIdx.y;
   const int64_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
-  if (debug_bad(src, src_blocks, PA_DEBUG_PAIR) | debug_bad(dst, dst_blocks, PA_DEBUG_PAIR)) return;
+  // both ends are checked (and flagged) before either is used
+  if (int(debug_bad(src, src_blocks, PA_DEBUG_PAIR)) | int(debug_bad(dst, dst_blocks, PA_DEBUG_PAIR)))
+    return;
   const u32x4* ks = reinterpret_cast<const u32x4*>(src_k) + src * tile_vecs;
   const u32x4* vs = reinterpret_cast<const u32x4*>(src_v) + src * tile_vecs;
   u32x4* kd = reinterpret_cast<u32x4*>(dst_k) + dst * tile_vecs;

@@ -393,7 +393,7 @@ constexpr int kPfSets = 2;  // 16-query sets per wave
 constexpr int kPfWgQueries = 16 * kPfSets * kPfWaves;  // queries per workgroup
 
 template <class DT, int D>
-void launch_prefill(const PrefillParams& p, int S, int max_q_len, hipStream_t st) {
+void launch_prefill(const PrefillParams& p, int S, hipStream_t st) {
   // 8 XCDs x (sequence, head) groups per XCD x query tiles; see the kernel
   const int64_t groups_per_xcd = (int64_t(S) * p.H + 7) / 8;
   const dim3 grid(unsigned(8 * groups_per_xcd * p.num_tiles));
@@ -450,11 +450,11 @@ int pa_prefill(const void* q, const void* k_cache, const void* v_cache,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (dtype == PA_F16) {
-    if (head_dim == 64) pa::launch_prefill<pa::F16, 64>(p, num_seqs, max_q_len, st);
-    else pa::launch_prefill<pa::F16, 128>(p, num_seqs, max_q_len, st);
+    if (head_dim == 64) pa::launch_prefill<pa::F16, 64>(p, num_seqs, st);
+    else pa::launch_prefill<pa::F16, 128>(p, num_seqs, st);
   } else {
-    if (head_dim == 64) pa::launch_prefill<pa::BF16, 64>(p, num_seqs, max_q_len, st);
-    else pa::launch_prefill<pa::BF16, 128>(p, num_seqs, max_q_len, st);
+    if (head_dim == 64) pa::launch_prefill<pa::BF16, 64>(p, num_seqs, st);
+    else pa::launch_prefill<pa::BF16, 128>(p, num_seqs, st);
   }
   return pa::launch_status();
 }
