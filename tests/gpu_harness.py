@@ -115,20 +115,6 @@ def compare_outputs(gpu_out, ref, seqs=None, tol=TOL, what="", cast_dtype=None):
     return worst
 
 
-def sample_seqs(ctx, k, seed=0):
-    """Up to k sequences: the longest, the shortest and a seeded random rest."""
-    S = len(ctx)
-    if S <= k:
-        return list(range(S))
-    order = np.argsort(ctx)
-    pick = {int(order[0]), int(order[-1])}
-    rng = np.random.default_rng(seed)
-    for s in rng.permutation(S):
-        if len(pick) >= k:
-            break
-        pick.add(int(s))
-    return sorted(pick)
-
 
 def same_storage(gpu_t, ora, dtype, what):
     g = bits(gpu_t)

@@ -78,7 +78,6 @@ def test_contiguous_bit_identical_to_paged():
 
 
 def test_contiguous_rejects_bad_strides():
-    import ctypes
     L = pk().lib()
     q = torch.zeros(2, 2, 64, dtype=torch.float16, device="cuda")
     k = torch.zeros(2, 8, 2, 64, dtype=torch.float16, device="cuda")

@@ -12,8 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import (TOL, bits, compare_outputs, log, oracle_bits, run_gpu, sample_seqs,
-                         to_dev)
+from gpu_harness import TOL, bits, compare_outputs, log, oracle_bits, run_gpu, to_dev
 from gpu_harness import check_workload as _check_workload
 from gpu_harness import same_storage as _same_storage
 

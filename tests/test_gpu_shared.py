@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import TOL, bits, check_workload, compare_outputs, log, to_dev
+from gpu_harness import bits, check_workload, compare_outputs, log, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
