@@ -72,3 +72,24 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_traffic_record_only_for_the_profiled_source(tmp_path, monkeypatch):
+    """The roofline's traffic comes from a committed counter record only while
+    the kernel sources hash to the values the counters were taken on."""
+    import hashlib
+    import json
+    (tmp_path / "profiles").mkdir()
+    src = tmp_path / "k.hip"
+    src.write_bytes(b"kernel source v1")
+    rec = {"sources": ["k.hip"],
+           "source_sha256": hashlib.sha256(b"kernel source v1").hexdigest(),
+           "traffic_bytes_per_launch": 1003.0, "algorithmic_bytes_per_launch": 1000,
+           "summary": "profiles/x.md"}
+    (tmp_path / "profiles" / "decode_w_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    got = bench.load_traffic("decode_w")
+    assert got["traffic_bytes_per_launch"] / got["algorithmic_bytes_per_launch"] == 1.003
+    src.write_bytes(b"kernel source v2")          # the kernel changed since the counters
+    assert bench.load_traffic("decode_w") is None
+    assert bench.load_traffic("decode_missing") is None
