@@ -9,6 +9,8 @@
 // Both are pure 16-byte moves: each lane carries one 16-byte slice of a
 // token row (D elements), so a wave moves 1 KiB of contiguous source per
 // instruction and writes whole 16-byte slices of contiguous destination rows.
+#include <algorithm>
+
 #include "internal.hpp"
 #include "launch_common.hpp"
 #include "pa_device.hpp"
@@ -17,26 +19,33 @@ namespace pa {
 
 constexpr int kCwThreads = 256;
 
-// One lane per 16-byte slice of (token, head) row; rows_per_token = H.
+// One lane per 16-byte slice of a token's H rows: x covers the token's
+// H * vecs_per_row slices (lane r: head r >> log2_vpr, slice r mod vpr), y
+// strides over the tokens.  No division: vecs_per_row is a power of two.
 __global__ __launch_bounds__(kCwThreads) void cache_write_kernel(
     const char* __restrict__ k, const char* __restrict__ v, const int64_t* __restrict__ slots,
-    char* __restrict__ k_cache, char* __restrict__ v_cache, int64_t total_vecs, int H,
-    int vecs_per_row, int row_bytes, int log2_bs, int64_t num_slots) {
-  const int64_t g = int64_t(blockIdx.x) * kCwThreads + threadIdx.x;
-  if (g >= total_vecs) return;
-  const int64_t row = g / vecs_per_row;  // n * H + h
-  const int col = int(g - row * vecs_per_row);
-  const int64_t n = row / H;
-  const int h = int(row - n * H);
-  const int64_t slot = slots[n];
-  if (slot < 0) return;
-  if (debug_bad(slot, num_slots, PA_DEBUG_SLOT)) return;
-  const int64_t blk = slot >> log2_bs;
-  const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
-  const int64_t dst = ((((blk * H + h) << log2_bs) + off) * row_bytes) + int64_t(col) * 16;
-  const int64_t src = g * 16;
-  *reinterpret_cast<u32x4*>(k_cache + dst) = *reinterpret_cast<const u32x4*>(k + src);
-  *reinterpret_cast<u32x4*>(v_cache + dst) = *reinterpret_cast<const u32x4*>(v + src);
+    char* __restrict__ k_cache, char* __restrict__ v_cache, int64_t num_tokens, int H,
+    int log2_vpr, int row_bytes, int log2_bs, int64_t num_slots) {
+  const int per_token = H << log2_vpr;
+  const int r = int(blockIdx.x) * kCwThreads + int(threadIdx.x);
+  if (r >= per_token) return;
+  const int h = r >> log2_vpr;
+  const int col = r & ((1 << log2_vpr) - 1);
+  for (int64_t n = blockIdx.y; n < num_tokens; n += gridDim.y) {
+    // the slices are loaded while the slot is (both are in bounds whatever
+    // the slot holds): one memory round trip, not two
+    const int64_t src = (n * per_token + r) * 16;
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(k + src);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(v + src);
+    const int64_t slot = slots[n];
+    if (slot < 0) continue;
+    if (debug_bad(slot, num_slots, PA_DEBUG_SLOT)) continue;
+    const int64_t blk = slot >> log2_bs;
+    const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
+    const int64_t dst = ((((blk * H + h) << log2_bs) + off) * row_bytes) + int64_t(col) * 16;
+    *reinterpret_cast<u32x4*>(k_cache + dst) = kx;
+    *reinterpret_cast<u32x4*>(v_cache + dst) = vx;
+  }
 }
 
 // blockIdx.y = pair; blocks of blockIdx.x stride over the block's 16-byte
@@ -165,15 +174,16 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, in
   if (!pa::aligned16(k) || !pa::aligned16(v) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache))
     return PA_ERR_INVALID;
   const int row_bytes = head_dim * pa::elem_bytes(dtype);
-  const int vecs_per_row = row_bytes / 16;
-  const int64_t total = num_tokens * num_heads * vecs_per_row;
-  const int64_t nblocks = (total + pa::kCwThreads - 1) / pa::kCwThreads;
-  if (nblocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int log2_vpr = pa::log2_exact(row_bytes / 16);  // 8, 16 or 32 slices per row
+  const int64_t per_token = int64_t(num_heads) << log2_vpr;
+  if (per_token > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const unsigned gx = unsigned((per_token + pa::kCwThreads - 1) / pa::kCwThreads);
+  const unsigned gy = unsigned(std::min<int64_t>(num_tokens, 65535));
   (void)hipGetLastError();
-  hipLaunchKernelGGL(pa::cache_write_kernel, dim3(unsigned(nblocks)), dim3(pa::kCwThreads), 0,
+  hipLaunchKernelGGL(pa::cache_write_kernel, dim3(gx, gy), dim3(pa::kCwThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<const char*>(k),
                      static_cast<const char*>(v), slot_mapping, static_cast<char*>(k_cache),
-                     static_cast<char*>(v_cache), total, num_heads, vecs_per_row, row_bytes,
+                     static_cast<char*>(v_cache), num_tokens, num_heads, log2_vpr, row_bytes,
                      pa::log2_exact(block_size), num_blocks * block_size);
   return pa::launch_status();
 }
