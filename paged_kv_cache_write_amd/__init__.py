@@ -106,6 +106,8 @@ _SIGNATURES = {
     "pa_engine_last_step": (_c.c_int, [_vp, _i32, _vp, _vp, _vp, _i32]),
     "pa_engine_set_decode_events": (_c.c_int, [_vp, _vp, _vp]),
     "pa_engine_set_sharing": (_c.c_int, [_vp, _i32]),
+    "pa_engine_set_mapped_staging": (_c.c_int, [_vp, _i32]),
+    "pa_engine_has_mapped_staging": (_i32, [_vp]),
     "pa_stream_read": (_c.c_int, [_vp, _i64, _vp, _i32, _vp]),
     "pa_decode_contiguous": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64,
                                         _i64, _f32, _i32, _i32, _vp, _vp, _sz, _i32, _vp, _vp,

@@ -107,6 +107,15 @@ struct DecodeParams {
   int num_seqs;        // sequences of the launch (checked against work items in debug builds)
   int64_t ws_o_bytes;  // bytes of the ws_o region
   int num_group_wgs;   // decode_shared_kernel: workgroups of the group items
+  // Engine step (single items only): each row's new token, K and V as
+  // [S, H, D] like q, which is the last token of the row's context, and its
+  // slot (int64 [S]; negative: none).  The wave of the row's last partition
+  // reads the token from here; workgroups after the launch's item
+  // workgroups write it into the slot.  NULL: no new tokens.
+  const void* new_k;
+  const void* new_v;
+  const int64_t* new_slots;
+  int num_item_wgs;  // workgroups of the items (the token writers follow them)
 };
 
 template <class DT, int D, int U>
@@ -167,6 +176,10 @@ struct ChunkCtx {
   const char* vbase;
   uint64_t row_stride;
   uint64_t lane_off_c;
+  // the row's new token (the partition's last token), K and V rows, read
+  // from here instead of the pool (NULL: none)
+  const char* nk;
+  const char* nv;
 };
 
 // Issue the 2U 16-byte loads (K and V) of one chunk.  kMasked is the
@@ -203,8 +216,19 @@ __device__ __forceinline__ void chunk_load(const ChunkCtx& cx, int t0, u32x4 (&k
     // (block, head) tile index fits 32 bits; tiles are a power of two in size
     const uint32_t tile_idx = uint32_t(pb) * uint32_t(cx.H) + uint32_t(cx.h);
     const size_t tile = (size_t(tile_idx) << cx.log2_tile) + uint32_t(tt & cx.bs_mask) * kRowBytes;
-    kr[i] = load_stream(cx.kc + tile + off);
-    vr[i] = load_stream(cx.vc + tile + off);
+    const char* kp = cx.kc + tile + off;
+    const char* vp = cx.vc + tile + off;
+    if constexpr (kMasked) {
+      // the lanes of the new token's row read it from the new K/V (token
+      // writer workgroups of the launch put it into its slot)
+      if (cx.nk != nullptr && t0 + i * Sh::kTPI + cx.row == cx.ntok - 1) {
+        const uint32_t in_row = cx.lane_off - uint32_t(cx.row) * kRowBytes;
+        kp = cx.nk + in_row;
+        vp = cx.nv + in_row;
+      }
+    }
+    kr[i] = load_stream(kp);
+    vr[i] = load_stream(vp);
   }
   // Keep all 2U loads in flight before any of them is consumed: without this
   // fence the scheduler interleaves the dot products with the loads to save
@@ -224,14 +248,16 @@ __device__ __forceinline__ void chunk_apply(const ChunkCtx& cx, const u32x4 (&kr
   for (int i = 0; i < U; ++i) vr[i] = (!kMasked || ok[i]) ? vr_in[i] : u32x4{0, 0, 0, 0};
   using Sh = Shape<DT, D, U>;
   constexpr int kVec = DT::kVec;
+  // A valid row's score and weight are computed by the same operations
+  // whether the chunk is masked or not (the mask selects only around them),
+  // so a full chunk gives the same bits on either path.
   float sc[U];
   float mx = kNegBig;
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     const float d = group_sum<Sh::kLPT>(dot16(DT{}, kr[i], qv, 0.f));
     sc[i] = d * cx.qk_scale;
-    if constexpr (kMasked) sc[i] = ok[i] ? sc[i] : -__builtin_inff();
-    mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, (!kMasked || ok[i]) ? sc[i] : -__builtin_inff());
   }
   const float mn = fmaxf(m, mx);
   const float alpha = fast_exp2(m - mn);
@@ -240,11 +266,44 @@ __device__ __forceinline__ void chunk_apply(const ChunkCtx& cx, const u32x4 (&kr
   for (int e = 0; e < kVec; ++e) acc[e] *= alpha;
 #pragma unroll
   for (int i = 0; i < U; ++i) {
-    const float p = fast_exp2(sc[i] - mn);
+    float p = fast_exp2(sc[i] - mn);
+    if constexpr (kMasked) p = ok[i] ? p : 0.f;
     l += p;
     axpy16(DT{}, acc, vr[i], p);
   }
   m = mn;
+}
+
+// A token writer workgroup of a launch with new tokens: row s's new token,
+// its H rows of K and V, into its slot, 16 bytes per lane (the slices of a
+// row are a power of two).  No wave of the launch reads the slot (the wave
+// of the row's last partition takes the token from the new K/V, chunk_load),
+// so the writers need no ordering with the decode waves; later launches see
+// the token through the kernel boundary, as after a separate cache-write
+// kernel.
+template <class DT, int D>
+__device__ __forceinline__ void write_new_token(const DecodeParams& P, int s) {
+  constexpr int kRowBytes = D * int(sizeof(typename DT::T));
+  constexpr int kLog2Vecs = __builtin_ctz(kRowBytes / 16);
+  const int64_t slot = P.new_slots[s];
+  if (slot < 0) return;
+  if (debug_bad(slot, P.num_blocks << P.log2_bs, PA_DEBUG_SLOT)) return;
+  const int64_t blk = slot >> P.log2_bs;
+  const int64_t off = slot & ((int64_t(1) << P.log2_bs) - 1);
+  const int per_token = P.H << kLog2Vecs;
+  const char* ks = static_cast<const char*>(P.new_k) + int64_t(s) * per_token * 16;
+  const char* vs = static_cast<const char*>(P.new_v) + int64_t(s) * per_token * 16;
+  char* kd = static_cast<char*>(const_cast<void*>(P.k_cache));
+  char* vd = static_cast<char*>(const_cast<void*>(P.v_cache));
+  for (int r = int(threadIdx.x); r < per_token; r += int(blockDim.x)) {
+    const int h = r >> kLog2Vecs;
+    const int col = r & ((1 << kLog2Vecs) - 1);
+    const u32x4 kx = load16(ks + int64_t(r) * 16);
+    const u32x4 vx = load16(vs + int64_t(r) * 16);
+    const int64_t dst = ((((blk * P.H + h) << P.log2_bs) + off) * kRowBytes) + int64_t(col) * 16;
+    *reinterpret_cast<u32x4*>(kd + dst) = kx;
+    *reinterpret_cast<u32x4*>(vd + dst) = vx;
+  }
 }
 
 // Merge the token rows of a wave (lanes with equal col): afterwards every
@@ -540,6 +599,7 @@ __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h
     cx.ntok = 0;
     cx.last_group = 0;
     cx.qk_scale = P.qk_scale;
+    cx.nk = cx.nv = nullptr;
     return cx;
   }
   const int blk0 = t0 >> P.log2_bs;
@@ -571,6 +631,7 @@ __device__ __forceinline__ ChunkCtx make_ctx(const DecodeParams& P, int s, int h
   cx.qk_scale = P.qk_scale;
   cx.kbase = cx.vbase = nullptr;
   cx.row_stride = cx.lane_off_c = 0;
+  cx.nk = cx.nv = nullptr;
   return cx;
 }
 
@@ -607,7 +668,10 @@ __device__ __forceinline__ void stream_unit(const DecodeParams& P, ChunkCtx cx, 
   // is computed.  Loads inside the loop are unconditional, so the compiler's
   // wait counts stay exact (a load issued on one path only makes it wait for
   // everything where the paths join); the last chunks are peeled.
-  const int nfull = ntok / Sh::kChunk;
+  // With a new token (the last one) the last chunk is always the masked
+  // one, full or not: its loads take the new token from the new K/V.  A
+  // masked full chunk computes the same bits as an unmasked one.
+  const int nfull = (cx.nk != nullptr ? ntok - 1 : ntok) / Sh::kChunk;
   const bool tail = nfull * Sh::kChunk < ntok;
   const int t_tail = nfull * Sh::kChunk;
   u32x4 ka[U], va[U], kb[U], vb[U];
@@ -705,11 +769,24 @@ __device__ __forceinline__ void wave_body(DecodeParams P, uint3 block) {
     nparts = (ctx + P.part_tokens - 1) / P.part_tokens;
     ntok = part < nparts ? min(P.part_tokens, ctx - t0) : 0;
   }
+  if constexpr (!kContig) {
+    if (P.new_k != nullptr && it != nullptr && ntok > 0 && part == nparts - 1) {
+      constexpr size_t kRowBytes = size_t(D) * sizeof(typename DT::T);
+      cx.nk = static_cast<const char*>(P.new_k) + row_id * kRowBytes;
+      cx.nv = static_cast<const char*>(P.new_v) + row_id * kRowBytes;
+    }
+  }
   stream_unit<DT, D, U, kContig>(P, cx, row_id, part, ntok, nparts, lane);
 }
 
 template <class DT, int D, int U, bool kContig = false, int W = 1>
 __global__ __launch_bounds__(W * kWave) void decode_wave_kernel(DecodeParams P) {
+  if constexpr (!kContig) {
+    if (P.new_k != nullptr && int(blockIdx.x) >= P.num_item_wgs) {
+      write_new_token<DT, D>(P, int(blockIdx.x) - P.num_item_wgs);
+      return;
+    }
+  }
   wave_body<DT, D, U, kContig, W>(P, uint3{blockIdx.x, blockIdx.y, blockIdx.z});
 }
 
@@ -1232,18 +1309,23 @@ static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t
                       dim3(kWave), st, t, p);
       break;
     case Launch::kSingles: {
+      // with new tokens, S token writer workgroups follow the item workgroups
+      DecodeParams pw = p;
+      const unsigned writers = p.new_k ? unsigned(S) : 0u;
       if (p.items && !p.contig && int64_t(n) * p.H >= kWideLaunchWaves) {
         const unsigned wgs = unsigned(n) * unsigned((p.H + kWideWaves - 1) / kWideWaves);
-        launch_kernel(decode_wave_kernel<DT, D, kUnroll, false, kWideWaves>, dim3(wgs),
-                      dim3(kWideWaves * kWave), st, t, p);
+        pw.num_item_wgs = int(wgs);
+        launch_kernel(decode_wave_kernel<DT, D, kUnroll, false, kWideWaves>,
+                      dim3(wgs + writers), dim3(kWideWaves * kWave), st, t, pw);
         break;
       }
-      const dim3 grid = p.items ? dim3(unsigned(n) * unsigned(ngroups), 1, 1)
+      const dim3 grid = p.items ? dim3(unsigned(n) * unsigned(ngroups) + writers, 1, 1)
                                 : dim3(ngroups, p.max_parts, S);
+      pw.num_item_wgs = p.items ? int(unsigned(n) * unsigned(ngroups)) : 0;
       if (p.contig)
-        launch_kernel(decode_wave_kernel<DT, D, kUnroll, true>, grid, dim3(kThreads), st, t, p);
+        launch_kernel(decode_wave_kernel<DT, D, kUnroll, true>, grid, dim3(kThreads), st, t, pw);
       else
-        launch_kernel(decode_wave_kernel<DT, D, kUnroll>, grid, dim3(kThreads), st, t, p);
+        launch_kernel(decode_wave_kernel<DT, D, kUnroll>, grid, dim3(kThreads), st, t, pw);
       break;
     }
     case Launch::kShared:  // group and single items in one launch (16-bit storage only)
@@ -1287,6 +1369,7 @@ struct Schedule {
   const int32_t* group_members = nullptr;
   Timing timing;  // optional: recorded at the start of the first and the end of the last launch
   int64_t counter_rows = 0;  // counters reserved at the workspace start (0: S*H of the call)
+  NewTokens new_tokens;      // optional: new tokens written by the last partitions
 };
 
 static int decode_impl(int what, const void* q, const void* k_cache, const void* v_cache,
@@ -1362,6 +1445,17 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.num_seqs = S;
   p.ws_o_bytes = split ? int64_t(S) * H * plan.max_parts * D * int64_t(sizeof(float)) : 0;
   p.num_group_wgs = 0;
+  const NewTokens& nt = sched.new_tokens;
+  p.new_k = nt.k;
+  p.new_v = nt.v;
+  p.new_slots = nt.slots;
+  p.num_item_wgs = 0;
+  if (nt.k || nt.v || nt.slots) {
+    // single items only: their last partitions hold the new tokens
+    if (!nt.k || !nt.v || !nt.slots || !aligned16(nt.k) || !aligned16(nt.v) ||
+        !sched.scheduled || !sched.items || sched.num_items <= 0 || shared || cg.on)
+      return PA_ERR_INVALID;
+  }
   if (shared && !p.counters) return PA_ERR_INVALID;  // groups need the one-launch merge
   if (shared && cg.on) return PA_ERR_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -1649,7 +1743,7 @@ int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cac
                            size_t workspace_bytes, int32_t partition_tokens, void* stream,
                            const int32_t* items, int32_t num_items, const int32_t* group_items,
                            int32_t num_group_items, const int32_t* members, hipEvent_t start,
-                           hipEvent_t stop, int64_t counter_rows) {
+                           hipEvent_t stop, int64_t counter_rows, const NewTokens& new_tokens) {
   if (num_seqs > 0 && ((num_items > 0 && !items) || num_items < 0 || num_group_items < 0 ||
                        (num_group_items > 0 && (!group_items || !members)) ||
                        num_items + num_group_items <= 0))
@@ -1664,6 +1758,7 @@ int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cac
   sc.timing.start = start;
   sc.timing.stop = stop;
   sc.counter_rows = counter_rows;
+  sc.new_tokens = new_tokens;
   return decode_impl(kDoPartitions | kDoReduce | kFused, q, k_cache, v_cache, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, num_heads, head_dim,
                      block_size, num_blocks, scale, max_context_len, dtype, out, workspace,

@@ -18,11 +18,21 @@
 // packet sits between only every ring/2-th pair of steps; a host slot is
 // rewritten only after the event of its group.  The device slot is reused in
 // stream order.
+//
+// Where the device's memory is mapped for the host (a large PCIe BAR), the
+// engine also keeps `ring` slots of uncached device memory: the host copies
+// the used bytes of its slot straight into the matching device slot, so no
+// kernel reads host memory, and a step without shared-prefix groups is one
+// launch: the decode, whose last partition of each row also writes that
+// row's new token (with groups, a cache-write kernel comes first).  The
+// device slots follow the host slots' guard events.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -40,6 +50,8 @@ struct pa_engine {
   char* host = nullptr;
   char* host_dev = nullptr;  // device-visible address of `host` (NULL: use hipMemcpyAsync)
   char* dev = nullptr;
+  char* mapped = nullptr;     // ring slots of host-written device memory (NULL: none)
+  bool use_mapped = true;     // steps use `mapped` when present
   size_t slot_bytes = 0;
   int32_t ring = 0, next = 0;
   int32_t group = 1;       // host slots per guarding event (the event sits on the group's last)
@@ -64,6 +76,63 @@ int64_t item_ints(int32_t max_batch, int32_t max_blocks, int32_t bs) {
 }
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+// Uncached device memory that the host writes through the BAR mapping.  The
+// device reads it from memory every time (no cache holds a line of it), so a
+// slot the host rewrites is never read stale.  Once a kernel has read such
+// memory it is not returned to the runtime: chunks are kept for the life of
+// the process and reused, smallest fit first, by later engines of the same
+// device.
+struct MappedChunk {
+  int device;
+  char* ptr;
+  size_t bytes;
+  bool used;
+};
+std::mutex g_mapped_mu;
+std::vector<MappedChunk> g_mapped;
+
+char* mapped_take(int device, size_t bytes) {
+  std::lock_guard<std::mutex> lock(g_mapped_mu);
+  MappedChunk* best = nullptr;
+  for (auto& c : g_mapped)
+    if (!c.used && c.device == device && c.bytes >= bytes && (!best || c.bytes < best->bytes))
+      best = &c;
+  if (best) {
+    best->used = true;
+    return best->ptr;
+  }
+  int large_bar = 0;
+  if (hipDeviceGetAttribute(&large_bar, hipDeviceAttributeIsLargeBar, device) != hipSuccess ||
+      !large_bar) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = nullptr;
+  if (hipExtMallocWithFlags(&p, bytes, hipDeviceMallocUncached) != hipSuccess || !p ||
+      size_t(p) % 16) {
+    (void)hipGetLastError();
+    return nullptr;  // (an unaligned chunk is never handed out; none is expected)
+  }
+  g_mapped.push_back({device, static_cast<char*>(p), bytes, true});
+  return static_cast<char*>(p);
+}
+
+void mapped_give(char* p) {
+  std::lock_guard<std::mutex> lock(g_mapped_mu);
+  for (auto& c : g_mapped)
+    if (c.ptr == p) c.used = false;
+}
+
+// Copy the used staging bytes into a mapped device slot so that the next
+// launch sees them: the fence drains the CPU's write-combining buffers, and
+// the read of the last word, which travels behind the writes over the link,
+// returns only once they have reached the device.
+void mapped_publish(char* dst, const char* src, size_t used) {
+  std::memcpy(dst, src, used);
+  std::atomic_thread_fence(std::memory_order_seq_cst);
+  (void)*reinterpret_cast<volatile const uint32_t*>(dst + used - 4);
+}
 
 }  // namespace
 
@@ -120,6 +189,13 @@ int pa_engine_create(pa_bm* bm, void* k_cache, void* v_cache, int64_t num_blocks
     else
       (void)hipGetLastError();
   }
+  {
+    int device = 0;
+    if (hipGetDevice(&device) == hipSuccess)
+      e->mapped = mapped_take(device, e->slot_bytes * size_t(ring));
+    else
+      (void)hipGetLastError();
+  }
   e->events.assign(size_t(ring), nullptr);
   e->pending.assign(size_t(ring), 0);
   // The ring events only order work (the host waits on one before it reuses a
@@ -147,6 +223,7 @@ void pa_engine_destroy(pa_engine* e) {
       (void)hipEventDestroy(e->events[i]);
     }
   }
+  if (e->mapped) mapped_give(e->mapped);  // no step that reads it is pending
   delete e;
 }
 
@@ -252,12 +329,32 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
   const int32_t pt = hs.part_tokens, max_ctx = hs.max_ctx;
 
   // 4. Ship the used bytes, copy shared last blocks, write the new tokens.
-  //    Copies must land before the writes into the copied blocks; without
+  //    Copies must land before the writes into the copied blocks.  Mapped
+  //    device staging: the host writes the device slot, and the decode writes
+  //    the new tokens unless the launch has groups.  Otherwise, without
   //    copies, one prologue launch ships the staging and writes the tokens.
   const size_t used = (off_members + 4 * hs.members.size() + 15) & ~size_t(15);
   char* d = e->dev;
-  const bool fused = e->host_dev != nullptr && ncow == 0;
-  if (fused) {
+  const bool mapped = e->mapped != nullptr && e->use_mapped;
+  const bool fused = !mapped && e->host_dev != nullptr && ncow == 0;
+  // mapped staging without groups: the decode writes the new tokens itself
+  const bool write_in_decode = mapped && n_groups == 0 && n_items > 0;
+  if (mapped) {
+    d = e->mapped + size_t(slot) * e->slot_bytes;
+    mapped_publish(d, h, used);
+    enqueued = true;
+    if (ncow > 0) {
+      rc = pa_copy_blocks(e->k_cache, e->v_cache, reinterpret_cast<const int32_t*>(d + off_cow),
+                          ncow, e->num_blocks, e->H, e->D, e->bs, e->dtype, stream);
+      if (rc != PA_OK) return fail(rc);
+    }
+    if (!write_in_decode) {
+      rc = pa_cache_write(k_new, v_new, reinterpret_cast<const int64_t*>(d + off_slots), n,
+                          e->k_cache, e->v_cache, e->num_blocks, e->H, e->D, e->bs, e->dtype,
+                          stream);
+      if (rc != PA_OK) return fail(rc);
+    }
+  } else if (fused) {
     char* hd = e->host_dev + size_t(slot) * e->slot_bytes;
     rc = pa::launch_step_prologue(hd, d, used, reinterpret_cast<const int64_t*>(hd + off_slots),
                                   k_new, v_new, n, e->k_cache, e->v_cache, e->num_blocks, e->H,
@@ -293,7 +390,12 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
                                   n_groups,
                                   n_groups ? reinterpret_cast<const int32_t*>(d + off_members)
                                            : nullptr,
-                                  e->ev_start, e->ev_end, int64_t(e->max_batch) * e->H);
+                                  e->ev_start, e->ev_end, int64_t(e->max_batch) * e->H,
+                                  write_in_decode
+                                      ? pa::NewTokens{k_new, v_new,
+                                                      reinterpret_cast<const int64_t*>(
+                                                          d + off_slots)}
+                                      : pa::NewTokens());
   if (rc != PA_OK) return fail(rc);
   e->undo.clear();
   // The host slots of this group may be rewritten once this step has run
@@ -320,6 +422,15 @@ int pa_engine_set_sharing(pa_engine* e, int32_t enable) {
   e->sharing = enable != 0;
   return PA_OK;
 }
+
+int pa_engine_set_mapped_staging(pa_engine* e, int32_t enable) {
+  if (!e) return PA_ERR_INVALID;
+  if (enable && !e->mapped) return PA_ERR_UNSUPPORTED;
+  e->use_mapped = enable != 0;
+  return PA_OK;
+}
+
+int32_t pa_engine_has_mapped_staging(const pa_engine* e) { return e && e->mapped ? 1 : 0; }
 
 int pa_engine_set_decode_events(pa_engine* e, void* start_event, void* end_event) {
   if (!e) return PA_ERR_INVALID;

@@ -44,6 +44,15 @@ int launch_step_prologue(const void* host_src, void* dev_dst, size_t copy_bytes,
 // counter_rows row counters reserved at the start of the workspace (0: one
 // per row of this call; the engine reserves its largest batch's rows, so the
 // counters stay in place when the batch grows).
+// New tokens that a scheduled decode of single items reads and writes into
+// the pool (see DecodeParams): K and V [S, H, D], each row's token being the
+// last of its context, and their slots (int64 [S]).
+struct NewTokens {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int64_t* slots = nullptr;
+};
+
 int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
@@ -52,7 +61,8 @@ int decode_scheduled_timed(const void* q, const void* k_cache, const void* v_cac
                            size_t workspace_bytes, int32_t partition_tokens, void* stream,
                            const int32_t* items, int32_t num_items, const int32_t* group_items,
                            int32_t num_group_items, const int32_t* members, hipEvent_t start,
-                           hipEvent_t stop, int64_t counter_rows);
+                           hipEvent_t stop, int64_t counter_rows,
+                           const NewTokens& new_tokens = NewTokens());
 
 // Device error words of the translation units with kernels (debug builds:
 // table entries, slots and copy pairs out of range; release builds: 0), each

@@ -183,6 +183,17 @@ class PagedKVEngine:
         _check(self._lib.pa_engine_set_sharing(self._e, 1 if enable else 0),
                "pa_engine_set_sharing")
 
+    @property
+    def has_mapped_staging(self) -> bool:
+        """True when the engine got host-written (mapped) device staging."""
+        return bool(self._lib.pa_engine_has_mapped_staging(self._e))
+
+    def set_mapped_staging(self, enable: bool):
+        """Mapped device staging in later steps (on by default where available);
+        off: the prologue kernel reads the pinned host slot."""
+        _check(self._lib.pa_engine_set_mapped_staging(self._e, 1 if enable else 0),
+               "pa_engine_set_mapped_staging")
+
     def set_decode_events(self, start=None, end=None):
         """Record ``start``/``end`` around the decode launch of the following steps
         (None = stop): torch.cuda.Event objects, or raw hipEvent_t handles (int)."""

@@ -50,8 +50,10 @@ def oracle_bits(a, dtype_name):
     return np.ascontiguousarray(a).view(np.int32)
 
 
-def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True, ring=None):
-    """Execute wl.ops with PagedKVEngine; returns dict with the engine and the step output."""
+def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True, ring=None, mapped=None):
+    """Execute wl.ops with PagedKVEngine; returns dict with the engine and the step output.
+    mapped: None = the engine's default staging, else force mapped device staging on
+    (True; it must be available) or off (False)."""
     import torch
     from paged_kv_cache_write_amd.engine import PagedKVEngine
     tdt = torch_dtype(wl.dtype)
@@ -60,6 +62,8 @@ def run_gpu(wl, partition_tokens=0, fill_nan=True, sharing=True, ring=None):
                         fill=float("nan") if fill_nan else 0.0,
                         partition_tokens=partition_tokens, ring=ring)
     eng.set_sharing(sharing)
+    if mapped is not None:
+        eng.set_mapped_staging(mapped)
     out = None
     for op in wl.ops:
         if op[0] == "add":
@@ -133,12 +137,12 @@ def same_storage(gpu_t, ora, dtype, what):
 
 
 def check_workload(wl, seqs=None, partition_tokens=0, tol=TOL, compare_pools=True,
-                   cast_bound=False, sharing=True):
+                   cast_bound=False, sharing=True, mapped=None):
     """Run wl through the engine and the oracle: step bookkeeping and pools bit-exact,
     outputs within tol.  Returns (gpu dict, oracle dict, max error)."""
     log(f"case {wl.name}: S={wl.S} H={wl.H} D={wl.D} {wl.dtype} bs={wl.bs} NB={wl.NB} "
-        f"sum(ctx)={int(wl.ctx.sum())} partition_tokens={partition_tokens}")
-    g = run_gpu(wl, partition_tokens=partition_tokens, sharing=sharing)
+        f"sum(ctx)={int(wl.ctx.sum())} partition_tokens={partition_tokens} mapped={mapped}")
+    g = run_gpu(wl, partition_tokens=partition_tokens, sharing=sharing, mapped=mapped)
     log("  gpu done; running oracle")
     r = oracle.run_workload(wl, decode_seqs=seqs)
     eng = g["engine"]

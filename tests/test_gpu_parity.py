@@ -38,23 +38,72 @@ def test_config2_llama13b_layer():
     _check_workload(synth.make_workload(2))
 
 
+def test_mapped_staging_available():
+    """The engine's host-written device staging (large PCIe BAR) is there on this
+    GPU, so the steps above ran the decode that writes the new tokens itself."""
+    from paged_kv_cache_write_amd.engine import PagedKVEngine
+    eng = PagedKVEngine(8, 2, 64, 16, torch.float16, 4, 2)
+    if not eng.has_mapped_staging:
+        pytest.skip("device memory is not mapped for the host here: the engine uses the "
+                    "prologue kernel")
+    eng.set_mapped_staging(False)
+    eng.set_mapped_staging(True)
+
+
+@pytest.mark.parametrize("dtype,D,bs", [("f16", 128, 16), ("bf16", 64, 8), ("f32", 128, 128),
+                                        ("f16", 64, 32)])
+def test_new_tokens_written_by_the_decode(dtype, D, bs):
+    """The decode launch that writes the step's new tokens itself (mapped
+    staging) against the prologue kernel's write followed by the decode: the
+    same pools and the same output bits.  The contexts put the new token at
+    every place in a partition's last chunk, on a full last chunk, and alone
+    in a partition; the oracle checks the mapped run."""
+    synth.cache_draws(False)
+    ctx = [1, 2, 31, 32, 33, 63, 64, 65, 96, 97, 256, 257, 1024, 1025, 2 * 64 * bs + 32,
+           2 * 64 * bs + 33]
+    wl = synth.make_custom(900 + D + bs, 5, D, dtype, bs, ctx)
+    g, r, _ = _check_workload(wl, cast_bound=True)
+    if not g["engine"].has_mapped_staging:
+        pytest.skip("no mapped staging on this device")
+    g2 = run_gpu(wl, mapped=False)
+    assert np.array_equal(bits(g["out"]), bits(g2["out"])), "output bits differ between the paths"
+    assert torch.equal(g["engine"].k_cache.view(torch.uint8), g2["engine"].k_cache.view(torch.uint8))
+    assert torch.equal(g["engine"].v_cache.view(torch.uint8), g2["engine"].v_cache.view(torch.uint8))
+    pt = max(32, bs)  # short partitions: many rows end in a partition of their own
+    g3 = run_gpu(wl, partition_tokens=pt)
+    g4 = run_gpu(wl, partition_tokens=pt, mapped=False)
+    assert np.array_equal(bits(g3["out"]), bits(g4["out"])), "split: output bits differ"
+    compare_outputs(g3["out"], r["out"], what=f"{wl.name} split pt={pt}", cast_dtype=dtype)
+
+
+def test_config2_prologue_staging():
+    """Config 2 with mapped staging off: the prologue kernel reads the pinned host
+    slot and writes the new tokens, then the decode."""
+    _check_workload(synth.make_workload(2), mapped=False)
+
+
 def test_config3_long_context_split():
     wl = synth.make_workload(3)
     _check_workload(wl, partition_tokens=wl.partition_tokens)
 
 
+@pytest.mark.parametrize("mapped", [None, False])
 @pytest.mark.parametrize("cow", [False, True])
-def test_config4_shared_prefix(cow):
+def test_config4_shared_prefix(cow, mapped):
     """With shared-prefix group items (32: 8 groups x 4 partitions of 256 tokens)
-    and without: both within tolerance of the oracle."""
+    and without: both within tolerance of the oracle, pools bit-exact.  Without
+    groups (and with mapped staging) the decode writes the new tokens itself,
+    after the step's copies on write."""
     wl = synth.make_workload(4, cow=cow)
-    g, r, _ = _check_workload(wl)
+    g, r, _ = _check_workload(wl, mapped=mapped)
     if cow:
         assert r["all_cows"].shape[0] == 7 * 8
     assert g["engine"].last_step["num_group_items"] == 32
-    g_off = run_gpu(wl, sharing=False)
+    g_off = run_gpu(wl, sharing=False, mapped=mapped)
     assert g_off["engine"].last_step["num_group_items"] == 0
     compare_outputs(g_off["out"], r["out"], what=wl.name + " no sharing")
+    _same_storage(g_off["engine"].k_cache, r["k_cache"], wl.dtype, "k_cache, no sharing")
+    _same_storage(g_off["engine"].v_cache, r["v_cache"], wl.dtype, "v_cache, no sharing")
 
 
 @pytest.mark.parametrize("bs", synth.SWEEP_BLOCK_SIZES)
@@ -291,13 +340,19 @@ def test_fused_merge_repeatable():
         log(f"fused merge pt={pt}: 50 calls bit-identical to the two-launch merge")
 
 
-@pytest.mark.parametrize("ring", [16, 4, 3])
-def test_engine_steps_in_flight(ring):
+@pytest.mark.parametrize("ring,mapped,sharing", [(16, None, True), (4, None, True),
+                                                 (3, None, True), (16, None, False),
+                                                 (4, False, True)])
+def test_engine_steps_in_flight(ring, mapped, sharing):
     """Forty engine steps enqueued behind a long GPU wait, so that the host wraps
-    the pinned staging ring several times (16 or 4 slots: one guard event per
+    the staging ring several times (16 or 4 slots: one guard event per
     half; 3 slots: one event per step) while earlier steps have not run:
     every step's output, pool write and
     copy-on-write must match the oracle replaying the same steps in order.
+    The staging is the engine's default (mapped device slots where the host
+    can write them: the host rewrites a device slot only after its guard
+    event), or the pinned host slots (mapped off); without sharing the decode
+    writes the new tokens itself.
     Twice a beam-style selection (one fork, one retired sequence) happens on
     the host between in-flight steps, so later steps copy on write and reuse
     freed blocks; each step has its own q and new-token K/V."""
@@ -315,7 +370,7 @@ def test_engine_steps_in_flight(ring):
     r = oracle.run_workload(wl2, decode=False)     # through the workload's own step
     bm, kc, vc = r["model"], r["k_cache"], r["v_cache"]
     seqs = [int(s) for s in wl.ops[-1][1]]
-    g = run_gpu(wl2, ring=ring)
+    g = run_gpu(wl2, ring=ring, mapped=mapped, sharing=sharing)
     eng = g["engine"]
     assert eng.ring == ring
     rng = np.random.default_rng(np.random.SeedSequence([733, 77]))
