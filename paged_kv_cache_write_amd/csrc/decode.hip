@@ -1195,10 +1195,16 @@ __global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParam
 // any order; the group waves' streaming overlaps the short single waves.
 template <class DT, int D>
 __global__ __launch_bounds__(kWave, 2) void decode_shared_kernel(DecodeParams P) {
-  if (blockIdx.x < unsigned(P.num_group_wgs))
+  if (blockIdx.x < unsigned(P.num_group_wgs)) {
     group_mfma_body<DT, D>(P, blockIdx.x);
-  else
-    wave_body<DT, D, kUnroll>(P, uint3{blockIdx.x - unsigned(P.num_group_wgs), 0u, 0u});
+    return;
+  }
+  const unsigned x = blockIdx.x - unsigned(P.num_group_wgs);
+  if (P.new_k != nullptr && x >= unsigned(P.num_item_wgs)) {
+    write_new_token<DT, D>(P, int(x) - P.num_item_wgs);
+    return;
+  }
+  wave_body<DT, D, kUnroll>(P, uint3{x, 0u, 0u});
 }
 
 // Second launch of the two-launch form: one wave per (sequence, head) row.
@@ -1329,10 +1335,15 @@ static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t
       break;
     }
     case Launch::kShared:  // group and single items in one launch (16-bit storage only)
-      if constexpr (!std::is_same<DT, F32>::value)
+      if constexpr (!std::is_same<DT, F32>::value) {
+        // with new tokens, S token writer workgroups follow the single items
+        DecodeParams pw = p;
+        pw.num_item_wgs = int(unsigned(n) * unsigned(ngroups));
+        const unsigned writers = p.new_k ? unsigned(S) : 0u;
         launch_kernel(decode_shared_kernel<DT, D>,
-                      dim3(unsigned(p.num_group_wgs) + unsigned(n) * unsigned(ngroups)),
-                      dim3(kWave), st, t, p);
+                      dim3(unsigned(p.num_group_wgs) + unsigned(pw.num_item_wgs) + writers),
+                      dim3(kWave), st, t, pw);
+      }
       break;
     case Launch::kReduce:
       launch_kernel(decode_reduce_kernel<DT, D, kUnroll>, dim3(p.H, S), dim3(kWave), st, t, p);
@@ -1451,9 +1462,10 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.new_slots = nt.slots;
   p.num_item_wgs = 0;
   if (nt.k || nt.v || nt.slots) {
-    // single items only: their last partitions hold the new tokens
+    // the single items' last partitions hold the new tokens (the caller
+    // guarantees that every row has one: no new token lies in a shared range)
     if (!nt.k || !nt.v || !nt.slots || !aligned16(nt.k) || !aligned16(nt.v) ||
-        !sched.scheduled || !sched.items || sched.num_items <= 0 || shared || cg.on)
+        !sched.scheduled || !sched.items || sched.num_items <= 0 || cg.on)
       return PA_ERR_INVALID;
   }
   if (shared && !p.counters) return PA_ERR_INVALID;  // groups need the one-launch merge

@@ -22,10 +22,11 @@
 // Where the device's memory is mapped for the host (a large PCIe BAR), the
 // engine also keeps `ring` slots of uncached device memory: the host copies
 // the used bytes of its slot straight into the matching device slot, so no
-// kernel reads host memory, and a step without shared-prefix groups is one
-// launch: the decode, whose last partition of each row also writes that
-// row's new token (with groups, a cache-write kernel comes first).  The
-// device slots follow the host slots' guard events.
+// kernel reads host memory, and a step without copies on write is one
+// launch: the decode, whose wave of each row's last partition reads the new
+// token from k_new / v_new while extra workgroups of the launch write the
+// tokens into their slots.  The device slots follow the host slots' guard
+// events.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -63,6 +64,7 @@ struct pa_engine {
   bool sharing = true;  // detect shared prefixes in the tables each step
   pa::HostSchedule hs;
   std::vector<pa::AppendUndo> undo;  // the block manager's appends of the current step
+  std::vector<char> covered;         // rows whose last token lies in a single item
 };
 
 namespace {
@@ -330,15 +332,25 @@ int pa_engine_step(pa_engine* e, const int64_t* seqs, int32_t n, const void* q,
 
   // 4. Ship the used bytes, copy shared last blocks, write the new tokens.
   //    Copies must land before the writes into the copied blocks.  Mapped
-  //    device staging: the host writes the device slot, and the decode writes
-  //    the new tokens unless the launch has groups.  Otherwise, without
-  //    copies, one prologue launch ships the staging and writes the tokens.
+  //    device staging: the host writes the device slot, and the decode launch
+  //    writes the new tokens.  Otherwise, without copies, one prologue launch
+  //    ships the staging and writes the tokens.
   const size_t used = (off_members + 4 * hs.members.size() + 15) & ~size_t(15);
   char* d = e->dev;
   const bool mapped = e->mapped != nullptr && e->use_mapped;
   const bool fused = !mapped && e->host_dev != nullptr && ncow == 0;
-  // mapped staging without groups: the decode writes the new tokens itself
-  const bool write_in_decode = mapped && n_groups == 0 && n_items > 0;
+  // mapped staging: the decode launch writes the new tokens itself when
+  // every row's last token lies in a single item (its last partition; never
+  // in a shared range, whose last block is private after copy on write)
+  bool write_in_decode = mapped && n_items > 0;
+  if (write_in_decode && n_groups > 0) {
+    e->covered.assign(size_t(n), 0);
+    for (size_t i = 0; i + 4 < hs.items.size(); i += 5) {
+      const int32_t s = hs.items[i], part = hs.items[i + 1], ntok = hs.items[i + 3];
+      if (s >= 0 && s < n && ntok > 0 && part == hs.items[i + 4] - 1) e->covered[size_t(s)] = 1;
+    }
+    write_in_decode = std::all_of(e->covered.begin(), e->covered.end(), [](char c) { return c; });
+  }
   if (mapped) {
     d = e->mapped + size_t(slot) * e->slot_bytes;
     mapped_publish(d, h, used);

@@ -87,23 +87,28 @@ def test_config3_long_context_split():
     _check_workload(wl, partition_tokens=wl.partition_tokens)
 
 
-@pytest.mark.parametrize("mapped", [None, False])
 @pytest.mark.parametrize("cow", [False, True])
-def test_config4_shared_prefix(cow, mapped):
+def test_config4_shared_prefix(cow):
     """With shared-prefix group items (32: 8 groups x 4 partitions of 256 tokens)
-    and without: both within tolerance of the oracle, pools bit-exact.  Without
-    groups (and with mapped staging) the decode writes the new tokens itself,
-    after the step's copies on write."""
+    and without: within tolerance of the oracle, pools bit-exact.  With mapped
+    staging the shared-prefix decode launch writes the new tokens itself
+    (after the step's copies on write); the prologue path gives the same bits."""
     wl = synth.make_workload(4, cow=cow)
-    g, r, _ = _check_workload(wl, mapped=mapped)
+    g, r, _ = _check_workload(wl)
     if cow:
         assert r["all_cows"].shape[0] == 7 * 8
     assert g["engine"].last_step["num_group_items"] == 32
-    g_off = run_gpu(wl, sharing=False, mapped=mapped)
+    g_off = run_gpu(wl, sharing=False)
     assert g_off["engine"].last_step["num_group_items"] == 0
     compare_outputs(g_off["out"], r["out"], what=wl.name + " no sharing")
     _same_storage(g_off["engine"].k_cache, r["k_cache"], wl.dtype, "k_cache, no sharing")
     _same_storage(g_off["engine"].v_cache, r["v_cache"], wl.dtype, "v_cache, no sharing")
+    if g["engine"].has_mapped_staging:
+        for sharing, ref in ((True, g), (False, g_off)):
+            gp = run_gpu(wl, sharing=sharing, mapped=False)
+            assert np.array_equal(bits(gp["out"]), bits(ref["out"])), f"sharing={sharing}: bits"
+            _same_storage(gp["engine"].k_cache, r["k_cache"], wl.dtype, "k_cache, prologue path")
+            _same_storage(gp["engine"].v_cache, r["v_cache"], wl.dtype, "v_cache, prologue path")
 
 
 @pytest.mark.parametrize("bs", synth.SWEEP_BLOCK_SIZES)
