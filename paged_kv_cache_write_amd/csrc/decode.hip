@@ -79,6 +79,62 @@ constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so max - max 
 constexpr int kItemInts = 5;
 constexpr int kMemberInts = 2;
 
+// XCD-aware order of a scheduled launch's single items.  The chip deals a
+// launch's workgroups out to its 8 XCDs in turn (workgroup b runs on XCD
+// b mod 8), and under a full-chip stream its odd XCDs read ~9% slower than
+// its even ones (per-wave timestamps of the decode on several workloads and
+// boxes), so with one unit (item, head group) per workgroup in item order the
+// even XCDs finish first and the odd ones end the launch alone.  Here the
+// units, longest first as the schedule lists them, go out in cycles of 84:
+// ten rounds of one unit per XCD, then one more round for the even XCDs
+// only, so the odd XCDs get 10 units for every 11 of the even ones, spread
+// evenly over the launch; each XCD still takes its units longest first.
+// Position p of the items' region (global workgroup offset + p) runs unit
+// xcd_order_unit(p, offset); positions whose unit is past the last are empty.
+constexpr int kXcds = 8;
+constexpr int kOddRounds = 10;   // rounds per cycle of an odd XCD
+constexpr int kEvenRounds = 11;  // rounds per cycle of an even XCD
+constexpr int kCycleUnits = kXcds * kOddRounds + (kXcds / 2) * (kEvenRounds - kOddRounds);
+
+__host__ __device__ inline int xcd_order_unit(int p, int offset) {
+  const int x = (offset + p) & (kXcds - 1);
+  const int first = (x - offset) & (kXcds - 1);  // XCD x's first position
+  const int k = (p - first) / kXcds;             // its k-th unit
+  if (x & 1) {
+    const int c = k / kOddRounds, r = k - c * kOddRounds;
+    return c * kCycleUnits + r * kXcds + x;
+  }
+  const int c = k / kEvenRounds, r = k - c * kEvenRounds;
+  return r < kOddRounds ? c * kCycleUnits + r * kXcds + x
+                        : c * kCycleUnits + kXcds * kOddRounds + x / 2;
+}
+
+// The inverse: the position of unit u.
+inline int64_t xcd_order_position(int64_t u, int64_t offset) {
+  const int64_t c = u / kCycleUnits, j = u - c * kCycleUnits;
+  int x;
+  int64_t k;
+  if (j < kXcds * kOddRounds) {
+    x = int(j % kXcds);
+    k = c * ((x & 1) ? kOddRounds : kEvenRounds) + j / kXcds;
+  } else {
+    x = int(2 * (j - kXcds * kOddRounds));
+    k = c * kEvenRounds + kOddRounds;
+  }
+  const int first = int((int64_t(x) - offset) & (kXcds - 1));
+  return first + kXcds * k;
+}
+
+// Positions (workgroups) of a launch of `units` units: one past the last
+// unit's position over all XCDs.  An XCD's units are at most 12 apart in the
+// unit order, so its last unit is among the last kCycleUnits.
+inline int64_t xcd_order_positions(int64_t units, int64_t offset) {
+  int64_t end = 0;
+  for (int64_t u = std::max<int64_t>(0, units - kCycleUnits); u < units; ++u)
+    end = std::max(end, xcd_order_position(u, offset) + 1);
+  return end;
+}
+
 struct DecodeParams {
   const void* q;
   const void* k_cache;
@@ -116,6 +172,8 @@ struct DecodeParams {
   const void* new_v;
   const int64_t* new_slots;
   int num_item_wgs;  // workgroups of the items (the token writers follow them)
+  int num_units;     // scheduled launches: item workgroup units (items x head groups)
+  int order_offset;  // global index of the first position of the items' region
 };
 
 template <class DT, int D, int U>
@@ -730,9 +788,11 @@ __device__ __forceinline__ void wave_body(DecodeParams P, uint3 block) {
   const int ngroups = (H + W - 1) / W;
   int hg, part, s, t0;
   const int32_t* it = nullptr;
-  if (P.items != nullptr) {  // scheduled launch: x = item * head_groups + head group
-    const int item = block.x / ngroups;
-    hg = block.x - item * ngroups;
+  if (P.items != nullptr) {  // scheduled launch: unit = item * head_groups + head group
+    const int unit = xcd_order_unit(int(block.x), P.order_offset);
+    if (unit >= P.num_units) return;  // an empty position of the order
+    const int item = unit / ngroups;
+    hg = unit - item * ngroups;
     it = P.items + kItemInts * item;
     s = it[0];
     part = it[1];
@@ -1318,16 +1378,19 @@ static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t
       // with new tokens, S token writer workgroups follow the item workgroups
       DecodeParams pw = p;
       const unsigned writers = p.new_k ? unsigned(S) : 0u;
+      pw.order_offset = 0;
       if (p.items && !p.contig && int64_t(n) * p.H >= kWideLaunchWaves) {
-        const unsigned wgs = unsigned(n) * unsigned((p.H + kWideWaves - 1) / kWideWaves);
+        pw.num_units = n * ((p.H + kWideWaves - 1) / kWideWaves);
+        const unsigned wgs = unsigned(xcd_order_positions(pw.num_units, 0));
         pw.num_item_wgs = int(wgs);
         launch_kernel(decode_wave_kernel<DT, D, kUnroll, false, kWideWaves>,
                       dim3(wgs + writers), dim3(kWideWaves * kWave), st, t, pw);
         break;
       }
-      const dim3 grid = p.items ? dim3(unsigned(n) * unsigned(ngroups) + writers, 1, 1)
-                                : dim3(ngroups, p.max_parts, S);
-      pw.num_item_wgs = p.items ? int(unsigned(n) * unsigned(ngroups)) : 0;
+      pw.num_units = p.items ? n * ngroups : 0;
+      const unsigned item_wgs = p.items ? unsigned(xcd_order_positions(pw.num_units, 0)) : 0u;
+      const dim3 grid = p.items ? dim3(item_wgs + writers, 1, 1) : dim3(ngroups, p.max_parts, S);
+      pw.num_item_wgs = int(item_wgs);
       if (p.contig)
         launch_kernel(decode_wave_kernel<DT, D, kUnroll, true>, grid, dim3(kThreads), st, t, pw);
       else
@@ -1338,7 +1401,9 @@ static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t
       if constexpr (!std::is_same<DT, F32>::value) {
         // with new tokens, S token writer workgroups follow the single items
         DecodeParams pw = p;
-        pw.num_item_wgs = int(unsigned(n) * unsigned(ngroups));
+        pw.num_units = n * ngroups;
+        pw.order_offset = p.num_group_wgs;
+        pw.num_item_wgs = int(xcd_order_positions(pw.num_units, p.num_group_wgs));
         const unsigned writers = p.new_k ? unsigned(S) : 0u;
         launch_kernel(decode_shared_kernel<DT, D>,
                       dim3(unsigned(p.num_group_wgs) + unsigned(pw.num_item_wgs) + writers),
@@ -1461,6 +1526,8 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.new_v = nt.v;
   p.new_slots = nt.slots;
   p.num_item_wgs = 0;
+  p.num_units = 0;
+  p.order_offset = 0;
   if (nt.k || nt.v || nt.slots) {
     // the single items' last partitions hold the new tokens (the caller
     // guarantees that every row has one: no new token lies in a shared range)
