@@ -251,7 +251,10 @@ def prefill_measure(torch, pk, per_call, dtype, seqs=8, prompt=1024, H=40, D=128
     cu = torch.from_numpy(cu_q).cuda()
     out = torch.empty_like(q)
     run = lambda: pk.prefill(q, eng.k_cache, eng.v_cache, dt_, cu, dc, wl.scale, prompt, out=out)
-    run()
+    # warm-up: ~60 calls (~10 ms): the first few dozen calls after an idle
+    # spell run up to ~15% slower (the clocks ramp up under the load)
+    for _ in range(60):
+        run()
     t = per_call(run)
     pairs = seqs * prompt * (prompt + 1) // 2
     flops = 4.0 * D * H * pairs
@@ -260,7 +263,7 @@ def prefill_measure(torch, pk, per_call, dtype, seqs=8, prompt=1024, H=40, D=128
             "tflops": round(flops / t / 1e12, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
             "frac": round(flops / t / 1e12 / MFMA_PEAK_TFLOPS, 4),
             "flops_counted": "4*D*H per causal (query, key) pair",
-            "timing": "20 back-to-back calls between one pair of events"}
+            "timing": "20 back-to-back calls between one pair of events, after 60 untimed calls"}
 
 
 class FenceFreeEvents:
