@@ -89,6 +89,8 @@ constexpr int kMemberInts = 2;
 // ten rounds of one unit per XCD, then one more round for the even XCDs
 // only, so the odd XCDs get 10 units for every 11 of the even ones, spread
 // evenly over the launch; each XCD still takes its units longest first.
+// The shared-prefix launch orders its group workgroups (first) the same way,
+// then its single items after them.
 // Position p of the items' region (global workgroup offset + p) runs unit
 // xcd_order_unit(p, offset); positions whose unit is past the last are empty.
 constexpr int kXcds = 8;
@@ -174,6 +176,7 @@ struct DecodeParams {
   int num_item_wgs;  // workgroups of the items (the token writers follow them)
   int num_units;     // scheduled launches: item workgroup units (items x head groups)
   int order_offset;  // global index of the first position of the items' region
+  int num_group_pos; // shared-prefix launch: positions of the group workgroups' region
 };
 
 template <class DT, int D, int U>
@@ -1255,11 +1258,13 @@ __global__ __launch_bounds__(kWave, 2) void decode_group_mfma_kernel(DecodeParam
 // any order; the group waves' streaming overlaps the short single waves.
 template <class DT, int D>
 __global__ __launch_bounds__(kWave, 2) void decode_shared_kernel(DecodeParams P) {
-  if (blockIdx.x < unsigned(P.num_group_wgs)) {
-    group_mfma_body<DT, D>(P, blockIdx.x);
+  if (blockIdx.x < unsigned(P.num_group_pos)) {
+    const int u = xcd_order_unit(int(blockIdx.x), 0);
+    if (u >= P.num_group_wgs) return;
+    group_mfma_body<DT, D>(P, unsigned(u));
     return;
   }
-  const unsigned x = blockIdx.x - unsigned(P.num_group_wgs);
+  const unsigned x = blockIdx.x - unsigned(P.num_group_pos);
   if (P.new_k != nullptr && x >= unsigned(P.num_item_wgs)) {
     write_new_token<DT, D>(P, int(x) - P.num_item_wgs);
     return;
@@ -1402,11 +1407,12 @@ static void launch(Launch what, const DecodeParams& p, int S, int n, hipStream_t
         // with new tokens, S token writer workgroups follow the single items
         DecodeParams pw = p;
         pw.num_units = n * ngroups;
-        pw.order_offset = p.num_group_wgs;
-        pw.num_item_wgs = int(xcd_order_positions(pw.num_units, p.num_group_wgs));
+        pw.num_group_pos = int(xcd_order_positions(p.num_group_wgs, 0));
+        pw.order_offset = pw.num_group_pos;
+        pw.num_item_wgs = int(xcd_order_positions(pw.num_units, pw.num_group_pos));
         const unsigned writers = p.new_k ? unsigned(S) : 0u;
         launch_kernel(decode_shared_kernel<DT, D>,
-                      dim3(unsigned(p.num_group_wgs) + unsigned(pw.num_item_wgs) + writers),
+                      dim3(unsigned(pw.num_group_pos) + unsigned(pw.num_item_wgs) + writers),
                       dim3(kWave), st, t, pw);
       }
       break;
@@ -1528,6 +1534,7 @@ static int decode_impl(int what, const void* q, const void* k_cache, const void*
   p.num_item_wgs = 0;
   p.num_units = 0;
   p.order_offset = 0;
+  p.num_group_pos = 0;
   if (nt.k || nt.v || nt.slots) {
     // the single items' last partitions hold the new tokens (the caller
     // guarantees that every row has one: no new token lies in a shared range)
