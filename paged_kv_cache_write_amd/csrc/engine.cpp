@@ -32,6 +32,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -94,6 +95,25 @@ struct MappedChunk {
 std::mutex g_mapped_mu;
 std::vector<MappedChunk> g_mapped;
 
+// Whether [p, p + bytes) is covered by readable and writable mappings of
+// this process without a gap (/proc/self/maps lists them in address order).
+bool host_mapped_rw(const void* p, size_t bytes) {
+  std::FILE* f = std::fopen("/proc/self/maps", "r");
+  if (!f) return false;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p), hi = lo + bytes;
+  uintptr_t covered = lo;  // [lo, covered) is known to be mapped rw
+  char line[512];
+  while (covered < hi && std::fgets(line, sizeof(line), f)) {
+    unsigned long a = 0, b = 0;
+    char perm[8] = {0};
+    if (std::sscanf(line, "%lx-%lx %7s", &a, &b, perm) != 3 || b <= covered) continue;
+    if (a > covered || perm[0] != 'r' || perm[1] != 'w') break;  // a gap, or not rw
+    covered = b;
+  }
+  std::fclose(f);
+  return covered >= hi;
+}
+
 char* mapped_take(int device, size_t bytes) {
   std::lock_guard<std::mutex> lock(g_mapped_mu);
   MappedChunk* best = nullptr;
@@ -111,10 +131,17 @@ char* mapped_take(int device, size_t bytes) {
     return nullptr;
   }
   void* p = nullptr;
-  if (hipExtMallocWithFlags(&p, bytes, hipDeviceMallocUncached) != hipSuccess || !p ||
-      size_t(p) % 16) {
+  if (hipExtMallocWithFlags(&p, bytes, hipDeviceMallocUncached) != hipSuccess || !p) {
     (void)hipGetLastError();
-    return nullptr;  // (an unaligned chunk is never handed out; none is expected)
+    return nullptr;
+  }
+  // The host writes the chunk at the device address: that range must be a
+  // readable and writable mapping of this process.  Otherwise the chunk is
+  // returned (no kernel has read it yet) and the engine keeps its prologue.
+  if (size_t(p) % 16 || !host_mapped_rw(p, bytes)) {
+    (void)hipFree(p);
+    (void)hipGetLastError();
+    return nullptr;
   }
   g_mapped.push_back({device, static_cast<char*>(p), bytes, true});
   return static_cast<char*>(p);
