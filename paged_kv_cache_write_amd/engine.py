@@ -81,7 +81,12 @@ class PagedKVEngine:
         # every completed decode leaves them at zero
         self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=self.device)
         self._info = StepInfo()
-        self._seqs_cache = (None, None)
+        self._seqs_cache = (None, None, None)  # (seqs object, int64 array, its address)
+        self._last_n = 0                       # sequences of the last step
+        # the current stream's raw handle without a Stream object (~2 us less per step)
+        self._raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        self._dev_index = self.device.index if self.device.index is not None \
+            else torch.cuda.current_device()
         self.last_info = None
 
     def __del__(self):
@@ -158,23 +163,34 @@ class PagedKVEngine:
         tables, copy shared last blocks, write k_new/v_new [S, H, D], decode q [S, H, D].
         Returns out [S, H, D]."""
         torch = self.torch
-        cached, arr = self._seqs_cache
+        cached, arr, aptr = self._seqs_cache
         if cached is not seqs:
             arr = np.ascontiguousarray(seqs, dtype=np.int64)
-            self._seqs_cache = (seqs, arr)
+            aptr = arr.__array_interface__["data"][0] if arr.size else None
+            # An int64 contiguous array is used in place (arr is seqs), so a
+            # later change of its contents is seen through the cached address;
+            # anything else (a list, another dtype) is converted on every call.
+            self._seqs_cache = (seqs, arr, aptr) if arr is seqs else (None, None, None)
         S = arr.size
+        shape = (S, self.H, self.D)
         for t in (q, k_new, v_new):
-            if tuple(t.shape) != (S, self.H, self.D) or t.dtype != self.dtype or \
-                    not t.is_contiguous() or not t.is_cuda:
+            if t.shape != shape or t.dtype != self.dtype or not t.is_contiguous() or \
+                    not t.is_cuda:
                 raise ValueError("q, k_new, v_new must be contiguous [S, H, D] device tensors")
         if out is None:
             out = torch.empty_like(q)
-        st = (torch.cuda.current_stream(self.device) if stream is None else stream).cuda_stream
-        rc = self._lib.pa_engine_step(self._e, _ptr(arr), S, q.data_ptr(), k_new.data_ptr(),
-                                  v_new.data_ptr(), float(scale), out.data_ptr(),
-                                  self.workspace.data_ptr(), self.workspace.numel(),
-                                  self.partition_tokens, st, ctypes.byref(self._info))
+        if stream is not None:
+            st = stream.cuda_stream
+        elif self._raw_stream is not None:
+            st = self._raw_stream(self._dev_index)
+        else:
+            st = torch.cuda.current_stream(self.device).cuda_stream
+        rc = self._lib.pa_engine_step(self._e, aptr, S, q.data_ptr(), k_new.data_ptr(),
+                                      v_new.data_ptr(), float(scale), out.data_ptr(),
+                                      self.workspace.data_ptr(), self.workspace.numel(),
+                                      self.partition_tokens, st, ctypes.byref(self._info))
         _check(rc, "pa_engine_step")
+        self._last_n = S
         self.last_info = self._info
         return out
 
@@ -216,7 +232,7 @@ class PagedKVEngine:
     def last_step(self):
         """Host copies of the last step: dict(ctx, slots, cows, num_cow, ...)."""
         info = self.last_info
-        S = self._seqs_cache[1].size
+        S = self._last_n
         slots = np.empty(S, dtype=np.int64)
         ctx = np.empty(S, dtype=np.int32)
         cows = np.empty((max(info.num_cow, 1), 2), dtype=np.int32)
