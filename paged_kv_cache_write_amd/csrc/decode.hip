@@ -108,11 +108,11 @@ struct DecodeParams {
   int num_seqs;        // sequences of the launch (checked against work items in debug builds)
   int64_t ws_o_bytes;  // bytes of the ws_o region
   int num_group_wgs;   // decode_shared_kernel: workgroups of the group items
-  // Engine step (single items only): each row's new token, K and V as
-  // [S, H, D] like q, which is the last token of the row's context, and its
-  // slot (int64 [S]; negative: none).  The wave of the row's last partition
-  // reads the token from here; workgroups after the launch's item
-  // workgroups write it into the slot.  NULL: no new tokens.
+  // Engine step: each row's new token, K and V as [S, H, D] like q, which is
+  // the last token of the row's context and lies in the row's last single
+  // item, and its slot (int64 [S]; negative: none).  The wave of the row's
+  // last partition reads the token from here; workgroups after the launch's
+  // single-item workgroups write it into the slot.  NULL: no new tokens.
   const void* new_k;
   const void* new_v;
   const int64_t* new_slots;
