@@ -212,27 +212,47 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void prefill_mfma_kernel(
       if (debug_bad(ids.b[c], P.num_blocks, PA_DEBUG_TABLE)) ids.b[c] = 0;  // t is in the context
     }
   };
+  // Row base + r of a step lies at (base & bs_mask) + (r & bs_mask) in its
+  // block (base is a multiple of 64 and bs a power of two: for bs <= 64 the
+  // first term is 0, for bs >= 64 the second is r), so a load's address is a
+  // wave-uniform block address plus a per-thread offset fixed for the kernel.
+  uint32_t lane_off[kPerThread];
+#pragma unroll
+  for (int c = 0; c < kPerThread; ++c) {
+    const int chunk = tid + c * kPfWaves * kWave;
+    const int r = chunk / (D / 8), col = chunk % (D / 8);
+    lane_off[c] = uint32_t(r & bs_mask) * kRowBytes + uint32_t(col) * 16;
+  }
   struct Regs { u32x4 k[kPerThread], v[kPerThread]; };
   auto load_step = [&](int base, const Ids& ids, Regs& g_) {
+    const size_t in_block = size_t(base & bs_mask) * kRowBytes;
 #pragma unroll
     for (int c = 0; c < kPerThread; ++c) {
-      const int chunk = tid + c * kPfWaves * kWave;
-      const int r = chunk / (D / 8), col = chunk % (D / 8);
-      const size_t off = (size_t(uint32_t(ids.b[c]) * uint32_t(H) + uint32_t(h)) << log2_tile) +
-                         size_t((base + r) & bs_mask) * kRowBytes + size_t(col) * 16;
-      g_.k[c] = *reinterpret_cast<const u32x4*>(kc + off);
-      g_.v[c] = *reinterpret_cast<const u32x4*>(vc + off);
+      const size_t blk = (size_t(uint32_t(ids.b[c]) * uint32_t(H) + uint32_t(h)) << log2_tile) +
+                         in_block;
+      g_.k[c] = *reinterpret_cast<const u32x4*>(kc + blk + lane_off[c]);
+      g_.v[c] = *reinterpret_cast<const u32x4*>(vc + blk + lane_off[c]);
     }
   };
   auto store_step = [&](int buf, int base, const Regs& g_) {
+    // V rows past the last key become zeros (their weights are 0, their
+    // memory may hold anything); only a step that reaches past it has any
+    const bool tail = base + kPfKeys - 1 > last;  // workgroup-uniform
 #pragma unroll
     for (int c = 0; c < kPerThread; ++c) {
       const int chunk = tid + c * kPfWaves * kWave;
       const int r = chunk / (D / 8), col = chunk % (D / 8);
-      const bool live = base + r <= last;
       *reinterpret_cast<u32x4*>(&lds_k[buf][L::at(r, col)]) = g_.k[c];
-      *reinterpret_cast<u32x4*>(&lds_v[buf][r * L::kVRow + col * 16]) =
-          live ? g_.v[c] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(&lds_v[buf][r * L::kVRow + col * 16]) = g_.v[c];
+    }
+    if (tail) {  // overwrite those rows (same thread, program order)
+#pragma unroll
+      for (int c = 0; c < kPerThread; ++c) {
+        const int chunk = tid + c * kPfWaves * kWave;
+        const int r = chunk / (D / 8), col = chunk % (D / 8);
+        if (base + r > last)
+          *reinterpret_cast<u32x4*>(&lds_v[buf][r * L::kVRow + col * 16]) = u32x4{0, 0, 0, 0};
+      }
     }
   };
 
