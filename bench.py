@@ -266,6 +266,50 @@ def prefill_measure(torch, pk, per_call, dtype, seqs=8, prompt=1024, H=40, D=128
             "timing": "20 back-to-back calls between one pair of events, after 60 untimed calls"}
 
 
+def pattern_read(eng, seqs, wl, torch, pk, n=20, reps=5):
+    """pa_tile_read over the K and V tiles that the last step's decode reads:
+    one unit per (work item, head) in the decode's order (group items first,
+    through their first member's table), no arithmetic.  ``n`` back-to-back
+    launches between one pair of events, median of ``reps``.  Returns
+    (GB/s, bytes per launch, units)."""
+    tables, ctx = eng.bm.block_tables(seqs, eng.maxB, wl.poison_block)
+    code = pk.DTYPE_CODES()[eng.k_cache.dtype]
+    sch = pk.decode_schedule_shared(ctx, tables, wl.H, wl.D, wl.bs, code, eng.partition_tokens)
+    H, bs = wl.H, wl.bs
+    lists = []
+
+    def add(s, t0, ntok):
+        blocks = tables[s, t0 // bs:(t0 + ntok - 1) // bs + 1].astype(np.int64)
+        for h in range(H):
+            lists.append(blocks * H + h)
+    for moff, _cnt, _part, t0, ntok in sch["groups"]:
+        if ntok > 0:
+            add(int(sch["members"][moff][0]), int(t0), int(ntok))
+    for s, _part, t0, ntok, _np in sch["items"]:
+        if ntok > 0:
+            add(int(s), int(t0), int(ntok))
+    offsets = np.zeros(len(lists) + 1, np.int32)
+    offsets[1:] = np.cumsum([len(x) for x in lists])
+    ids = np.concatenate(lists).astype(np.int32)
+    dev = eng.k_cache.device
+    od, idd = torch.from_numpy(offsets).to(dev), torch.from_numpy(ids).to(dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    tile = bs * wl.D * eng.k_cache.element_size()
+    run = lambda: pk.tile_read(eng.k_cache, eng.v_cache, tile, od, idd, sink)
+    run()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3 / n)
+    nbytes = 2 * int(ids.size) * tile
+    return nbytes / float(np.median(ts)) / 1e9, nbytes, len(lists)
+
+
 class FenceFreeEvents:
     """HIP timing events created with hipEventDisableSystemFence: recording one
     does not write back and invalidate the caches (a default event's system-scope
@@ -732,6 +776,16 @@ def main():
                                   "kernel": "stream_read_kernel (pa_stream_read), best of 5"}
         res["roofline"]["frac_of_achievable_read"] = round(st["achieved"] / rgbps, 4)
         del buf
+
+    # the decode's own access pattern read without arithmetic: the K and V
+    # tiles of the last step's work list, gathered through the tables
+    pgbps, pbytes, punits = pattern_read(eng, st["seqs"], wl, torch, pk)
+    res["pattern_read"] = {"gbps": round(pgbps, 1), "bytes": pbytes, "units": punits,
+                           "kernel": "tile_read_kernel (pa_tile_read): the K and V tiles of the "
+                                     "last step's decode work list, one wave per (item, head) "
+                                     "in the decode's order, no arithmetic; 20 back-to-back "
+                                     "launches, median of 5"}
+    res["roofline"]["frac_of_pattern_read"] = round(st["achieved"] / pgbps, 4)
 
     # secondary: the cache write and the copy-on-write copy on their own, both
     # shorter than their host issue: timed queued behind a lead read

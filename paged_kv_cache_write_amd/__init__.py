@@ -109,6 +109,7 @@ _SIGNATURES = {
     "pa_engine_set_mapped_staging": (_c.c_int, [_vp, _i32]),
     "pa_engine_has_mapped_staging": (_i32, [_vp]),
     "pa_stream_read": (_c.c_int, [_vp, _i64, _vp, _i32, _vp]),
+    "pa_tile_read": (_c.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp]),
     "pa_decode_contiguous": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64,
                                         _i64, _f32, _i32, _i32, _vp, _vp, _sz, _i32, _vp, _vp,
                                         _i32]),
@@ -422,6 +423,25 @@ def stream_read(buf, sink, waves=0, stream=None):
     nbytes = buf.numel() * buf.element_size()
     _check(lib().pa_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink", torch.int32), waves,
                                 _stream(stream, buf.device)), "pa_stream_read")
+
+
+def tile_read(a, b, tile_bytes, offsets, ids, sink, stream=None):
+    """pa_tile_read: unit u reads tiles ``ids[offsets[u]:offsets[u + 1]]`` of device
+    tensors ``a`` and ``b`` (same size, ``tile_bytes`` per tile; the decode's
+    gathered-read reference).  ``offsets``, ``ids``: device int32; ``sink``:
+    device int32 tensor of >= 1."""
+    torch = _torch()
+    nbytes = a.numel() * a.element_size()
+    if b.numel() * b.element_size() != nbytes:
+        raise ValueError("tile_read: a and b differ in size")
+    units = offsets.numel() - 1
+    if units < 0:
+        raise ValueError("tile_read: offsets needs units + 1 entries")
+    _check(lib().pa_tile_read(_dev(a, "a"), _dev(b, "b"), int(tile_bytes),
+                              nbytes // int(tile_bytes), _dev(offsets, "offsets", torch.int32),
+                              _dev(ids, "ids", torch.int32), units,
+                              _dev(sink, "sink", torch.int32), _stream(stream, a.device)),
+           "pa_tile_read")
 
 
 def decode_schedule_shared(context_lens_host, block_tables_host, num_heads, head_dim,

@@ -85,6 +85,15 @@ def test_host_side_argument_checks_enqueue_nothing():
     assert lib.pa_stream_read(256, 8192 + 16, 512, 0, None) == -1
     assert lib.pa_stream_read(None, 8192, 512, 0, None) == -1
     assert lib.pa_stream_read(264, 8192, 512, 0, None) == -1     # src not 16-byte aligned
+    # gathered tile read: no units is a no-op; tiles are powers of two from 1 KiB to 1 MiB
+    assert lib.pa_tile_read(None, None, 4096, 0, None, None, 0, None, None) == 0
+    assert lib.pa_tile_read(256, 512, 3072, 8, 768, 1024, 1, 1280, None) == -1   # not a power of 2
+    assert lib.pa_tile_read(256, 512, 512, 8, 768, 1024, 1, 1280, None) == -1    # below 1 KiB
+    assert lib.pa_tile_read(256, 512, 2 << 20, 8, 768, 1024, 1, 1280, None) == -1  # above 1 MiB
+    assert lib.pa_tile_read(264, 512, 4096, 8, 768, 1024, 1, 1280, None) == -1   # a not aligned
+    assert lib.pa_tile_read(256, 512, 4096, 8, None, 1024, 1, 1280, None) == -1  # no offsets
+    assert lib.pa_tile_read(256, 512, 4096, -1, 768, 1024, 1, 1280, None) == -1  # negative extent
+    assert lib.pa_tile_read(256, 512, 4096, 8, 768, 1024, -1, 1280, None) == -1  # negative units
 
 
 @pytest.mark.parametrize("S,H,D,bs,L,req", [(30, 40, 128, 16, 2048, 0), (8, 40, 128, 16, 4096, 512),
